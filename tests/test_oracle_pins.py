@@ -1,0 +1,513 @@
+"""Pins for the CPU oracle: each test ties an oracle function to something other
+than itself — a hand-worked example, a library routine that computes the same
+thing by another route, a closed form, an invariant, or a brute force on tiny
+inputs. A dropped term, a wrong index or sign, or a transposed operand in the
+oracle fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+
+
+# ------------------------------------------------------------------ helpers
+
+def bf16_bits_of(vals):
+    t = torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_float(bits):
+    b = np.asarray(bits, dtype=np.uint16)
+    return torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+
+
+def rne_f32(q: Fraction) -> float:
+    """Exact value -> nearest binary32, ties to even (subnormals included)."""
+    if q == 0:
+        return 0.0
+    neg = q < 0
+    a = -q if neg else q
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    quantum = Fraction(2) ** (e - 23)
+    m = a / quantum
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = n * quantum
+    if v >= Fraction(2) ** 128:
+        return -math.inf if neg else math.inf
+    f = float(v)
+    return -f if neg else f
+
+
+def fma_f32(a: float, b: float, c: float) -> float:
+    """IEEE fused multiply-add in binary32, round to nearest even, from exact rationals.
+    An exact zero sum is -0 only when both addends are -0 (or a -0 product meets -0)."""
+    p = Fraction(a) * Fraction(b)
+    s = p + Fraction(c)
+    if s == 0:
+        p_neg = (math.copysign(1.0, a) * math.copysign(1.0, b) < 0) if p == 0 else p < 0
+        c_neg = math.copysign(1.0, c) < 0 if c == 0 else c < 0
+        return -0.0 if (p_neg and c_neg) else 0.0
+    return rne_f32(s)
+
+
+# ------------------------------------------------------------------ hand-worked golden examples
+
+def test_golden_layout_by_hand(orc, golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "layout_hand_T4_E4_G2_K2.json")))
+    idx = np.array(g["topk_idx"], np.int32)
+    L = orc.layout(idx, g["E"], g["G"])
+    assert L["status"] == 0
+    for name in ("expert_count", "expert_offset", "group_count", "group_offset"):
+        np.testing.assert_array_equal(L[name], g[name], err_msg=name)
+    np.testing.assert_array_equal(L["slot_e"], np.ravel(g["slot_e"]))
+    np.testing.assert_array_equal(L["slot_g"], np.ravel(g["slot_g"]))
+    np.testing.assert_array_equal(L["slot_tg"], np.ravel(g["slot_tg"]))
+    np.testing.assert_array_equal(L["tok_group_mask"], g["tok_group_mask"])
+    np.testing.assert_array_equal(L["recv_src_e"][:L["R_expert"]], g["recv_src_e"])
+    np.testing.assert_array_equal(L["recv_src_g"][:L["R_group"]], g["recv_src_g"])
+
+
+def test_golden_combine_by_hand(orc, golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "layout_hand_T4_E4_G2_K2.json")))
+    idx = np.array(g["topk_idx"], np.int32)
+    w = np.array(g["topk_w"], np.float32)
+    x = bf16_bits_of(g["x"])
+    L = orc.layout(idx, g["E"], g["G"])
+    epg = g["E"] // g["G"]
+    for mode in ("expert", "group"):
+        D = orc.dispatch_bf16(L, mode, x, w, idx)
+        out = orc.combine(L, mode, D["recv_x"], w)
+        np.testing.assert_array_equal(bf16_to_float(out), np.array(g["combine_identity"], np.float32))
+    # per-expert scaled expert: receive row r of expert e is x * (1 + e)
+    D = orc.dispatch_bf16(L, "expert", x, w, idx)
+    e_of_row = np.searchsorted(L["expert_offset"], np.arange(L["R_expert"]), side="right") - 1
+    y = bf16_bits_of(bf16_to_float(D["recv_x"]) * (1 + e_of_row)[:, None])
+    out = orc.combine(L, "expert", y, w)
+    np.testing.assert_array_equal(bf16_to_float(out), np.array(g["combine_expert_scaled"], np.float32))
+    # per-group scaled expert
+    D = orc.dispatch_bf16(L, "group", x, w, idx)
+    g_of_row = np.searchsorted(L["group_offset"], np.arange(L["R_group"]), side="right") - 1
+    y = bf16_bits_of(bf16_to_float(D["recv_x"]) * (1 + g_of_row)[:, None])
+    out = orc.combine(L, "group", y, w)
+    np.testing.assert_array_equal(bf16_to_float(out), np.array(g["combine_group_scaled"], np.float32))
+    assert epg == 2
+
+
+def test_golden_fp8_block_by_hand(orc, golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "fp8_block_hand.json")))
+    row = np.zeros(256, np.float32)
+    codes_a = np.zeros(128, np.uint8)
+    for i, (v, c) in enumerate(g["block_a"]):
+        row[i] = v
+        codes_a[i] = c
+    codes_b = np.zeros(128, np.uint8)
+    for i, (v, c) in enumerate(g["block_b"]):
+        row[128 + i] = v
+        codes_b[i] = c
+    bits = bf16_bits_of(row)
+    np.testing.assert_array_equal(bf16_to_float(bits), row)   # inputs are exact in bf16
+    q, s = orc.quantize_row_fp8(bits)
+    np.testing.assert_array_equal(q[:128], codes_a)
+    np.testing.assert_array_equal(q[128:], codes_b)
+    assert s[0] == np.float32(g["block_a_scale"])
+    assert s[1] == np.float32(1.0) / np.float32(448.0)
+
+
+# ------------------------------------------------------------------ layout: reductions to library routines
+
+def _shapes():
+    yield 1, 1, 1, 1
+    yield 5, 2, 8, 8
+    yield 37, 3, 12, 4
+    yield 300, 8, 256, 8
+    yield 513, 4, 64, 1
+    yield 129, 6, 96, 32
+    yield 64, 1, 7, 7
+
+
+@pytest.mark.parametrize("T,K,E,G", list(_shapes()))
+def test_layout_equals_stable_argsort(orc, T, K, E, G):
+    idx = si.make_inputs(T, 8, E, K, seed=T * 131 + K)["topk_idx"]
+    L = orc.layout(idx, E, G)
+    assert L["status"] == 0
+    flat = idx.ravel()
+    # expert histogram by bincount, receive order by a stable sort of the flat pair list
+    np.testing.assert_array_equal(L["expert_count"], np.bincount(flat, minlength=E))
+    order = np.argsort(flat, kind="stable")
+    np.testing.assert_array_equal(L["recv_src_e"], order)
+    inv = np.empty_like(order)
+    inv[order] = np.arange(order.size)
+    np.testing.assert_array_equal(L["slot_e"], inv)
+    # groups: the deduplicated (t, g) pairs, enumerated t-major, stably sorted by g
+    epg = E // G
+    pairs = sorted({(t, int(e) // epg) for t in range(T) for e in idx[t]})
+    tg = np.array(pairs, np.int64).reshape(-1, 2)
+    gorder = np.argsort(tg[:, 1], kind="stable")
+    np.testing.assert_array_equal(L["recv_src_g"][:len(pairs)], tg[gorder, 0])
+    np.testing.assert_array_equal(L["group_count"], np.bincount(tg[:, 1], minlength=G))
+    slot_tg = np.full((T, G), -1, np.int64)
+    slot_tg[tg[gorder, 0], tg[gorder, 1]] = np.arange(len(pairs))
+    np.testing.assert_array_equal(L["slot_tg"], slot_tg.ravel())
+
+
+def _brute_layout(idx, E, G):
+    """Python brute force, written from the definition with sets and sorted()."""
+    T, K = len(idx), (len(idx[0]) if len(idx) else 0)
+    epg = E // G
+    status = 0
+    valid = {}
+    for t in range(T):
+        seen = set()
+        for k in range(K):
+            e = idx[t][k]
+            if not (0 <= e < E):
+                status |= 1
+                valid[(t, k)] = False
+            elif e in seen:
+                status |= 2
+                valid[(t, k)] = False
+            else:
+                seen.add(e)
+                valid[(t, k)] = True
+    keys = sorted((idx[t][k], t, k) for t in range(T) for k in range(K) if valid[(t, k)])
+    slot_e = {(t, k): -1 for t in range(T) for k in range(K)}
+    for r, (_, t, k) in enumerate(keys):
+        slot_e[(t, k)] = r
+    gkeys = sorted({(idx[t][k] // epg, t) for t in range(T) for k in range(K) if valid[(t, k)]})
+    slot_tg = {(t, g): -1 for t in range(T) for g in range(G)}
+    for r, (g, t) in enumerate(gkeys):
+        slot_tg[(t, g)] = r
+    slot_g = {(t, k): (slot_tg[(t, idx[t][k] // epg)] if valid[(t, k)] else -1)
+              for t in range(T) for k in range(K)}
+    return status, keys, gkeys, slot_e, slot_tg, slot_g
+
+
+def test_layout_brute_force_with_invalid_entries(orc):
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        T = int(rng.integers(0, 9))
+        K = int(rng.integers(1, 5))
+        G = int(rng.choice([1, 2, 4]))
+        E = G * int(rng.integers(1, 4))
+        idx = rng.integers(-2, E + 2, size=(T, K)).astype(np.int32)
+        if trial % 3 == 0:
+            idx = rng.integers(0, E, size=(T, K)).astype(np.int32)   # repeats, all in range
+        L = orc.layout(idx, E, G)
+        status, keys, gkeys, slot_e, slot_tg, slot_g = _brute_layout(idx.tolist(), E, G)
+        assert L["status"] == status
+        assert L["R_expert"] == len(keys) and L["R_group"] == len(gkeys)
+        for (t, k), s in slot_e.items():
+            assert L["slot_e"][t * K + k] == s
+            assert L["slot_g"][t * K + k] == slot_g[(t, k)]
+        for (t, g), s in slot_tg.items():
+            assert L["slot_tg"][t * G + g] == s
+        for r, (_, t, k) in enumerate(keys):
+            assert L["recv_src_e"][r] == t * K + k
+        for r, (_, t) in enumerate(gkeys):
+            assert L["recv_src_g"][r] == t
+
+
+@pytest.mark.parametrize("name", ["tiny", "t256", "t4096", "skew"])
+def test_layout_invariants(orc, name):
+    wl = si.WORKLOADS[name]
+    idx = si.make_inputs(wl.T, 8, wl.E, wl.K, seed=wl.seed, routing=wl.routing,
+                         zipf_s=wl.zipf_s)["topk_idx"]
+    T, K, E, G = wl.T, wl.K, wl.E, wl.G
+    L = orc.layout(idx, E, G)
+    assert L["status"] == 0
+    assert L["expert_count"].sum() == T * K
+    P = L["group_count"].sum()
+    assert P <= T * min(K, G) and P <= T * G and P >= T
+    assert sorted(L["slot_e"].tolist()) == list(range(T * K))
+    v = L["slot_tg"][L["slot_tg"] >= 0]
+    assert sorted(v.tolist()) == list(range(P))
+    for e in range(E):
+        seg = L["recv_src_e"][L["expert_offset"][e]:L["expert_offset"][e + 1]]
+        assert np.all(np.diff(seg) > 0)
+        assert np.all(idx.ravel()[seg] == e)
+    for g in range(G):
+        seg = L["recv_src_g"][L["group_offset"][g]:L["group_offset"][g + 1]]
+        assert np.all(np.diff(seg) > 0)
+    epg = E // G
+    stg = L["slot_tg"].reshape(T, G)
+    np.testing.assert_array_equal(L["slot_g"].reshape(T, K), stg[np.arange(T)[:, None], idx // epg])
+    bits = np.array([[(m >> g) & 1 for g in range(G)] for m in L["tok_group_mask"]])
+    np.testing.assert_array_equal(bits.astype(bool), stg >= 0)
+
+
+def test_layout_special_cases(orc):
+    # one expert per group: the deduplicated layout is the per-expert layout
+    idx = si.make_inputs(64, 8, 16, 4, seed=11)["topk_idx"]
+    L = orc.layout(idx, 16, 16)
+    np.testing.assert_array_equal(L["slot_g"], L["slot_e"])
+    np.testing.assert_array_equal(L["group_count"], L["expert_count"])
+    np.testing.assert_array_equal(L["recv_src_g"], L["recv_src_e"] // 4)
+    # one group: every token is one row, in token order
+    L = orc.layout(idx, 16, 1)
+    np.testing.assert_array_equal(L["recv_src_g"][:64], np.arange(64))
+    np.testing.assert_array_equal(L["slot_g"], np.repeat(np.arange(64), 4))
+    # top-1: a counting sort of the tokens by expert
+    idx1 = si.make_inputs(100, 8, 10, 1, seed=12)["topk_idx"]
+    L = orc.layout(idx1, 10, 5)
+    np.testing.assert_array_equal(L["recv_src_e"], np.argsort(idx1[:, 0], kind="stable"))
+    # no tokens
+    L = orc.layout(np.zeros((0, 8), np.int32), 256, 8)
+    assert L["expert_count"].sum() == 0 and L["group_offset"][-1] == 0 and L["status"] == 0
+
+
+def test_generator_distinct_groups_closed_form():
+    """E[distinct groups per token] = G (1 - C(E-epg, K) / C(E, K)) for a uniform K-subset."""
+    E, G, K = 256, 8, 8
+    epg = E // G
+    expect = G * (1 - math.comb(E - epg, K) / math.comb(E, K))
+    assert abs(expect - 5.2947) < 1e-4
+    idx = si.make_inputs(4096, 8, E, K, seed=3)["topk_idx"]
+    P = len({(t, int(e) // epg) for t in range(idx.shape[0]) for e in idx[t]})
+    assert abs(P / 4096 - expect) < 0.05
+    # every token's K experts are distinct and in range
+    assert all(len(set(r)) == K for r in idx.tolist())
+
+
+def test_generator_zipf_is_skewed():
+    wl = si.WORKLOADS["skew"]
+    idx = si.make_inputs(wl.T, 8, wl.E, wl.K, seed=wl.seed, routing="zipf")["topk_idx"]
+    cnt = np.bincount(idx.ravel(), minlength=wl.E)
+    assert cnt.max() > 3000 and cnt.min() < 200 and cnt.sum() == wl.T * wl.K
+    assert all(len(set(r)) == wl.K for r in idx.tolist())
+
+
+# ------------------------------------------------------------------ dispatch
+
+@pytest.mark.parametrize("name", ["tiny", "t256"])
+def test_dispatch_bf16_against_sender_view(orc, name):
+    d = si.make_workload(name)
+    wl = d["workload"]
+    x, w, idx = d["x"], d["topk_w"], d["topk_idx"]
+    L = orc.layout(idx, wl.E, wl.G)
+    cap = wl.T * wl.K + 3
+    canary = 0xBEEF
+    D = orc.dispatch_bf16(L, "expert", x, w, idx, capacity=cap, fill=canary)
+    # sender view: token t's k-th row sits at slot_e[t, k]
+    se = L["slot_e"].reshape(wl.T, wl.K)
+    for t in range(wl.T):
+        for k in range(wl.K):
+            np.testing.assert_array_equal(D["recv_x"][se[t, k]], x[t])
+            np.testing.assert_array_equal(D["recv_w"][se[t, k]], w[t])
+            np.testing.assert_array_equal(D["recv_idx"][se[t, k]], idx[t])
+    assert np.all(D["recv_x"][wl.T * wl.K:] == canary)
+    # library route: rows of x gathered by a stable sort of the flat expert list
+    np.testing.assert_array_equal(D["recv_x"][:wl.T * wl.K],
+                                  x[np.argsort(idx.ravel(), kind="stable") // wl.K])
+    Dg = orc.dispatch_bf16(L, "group", x, w, idx)
+    stg = L["slot_tg"].reshape(wl.T, wl.G)
+    for t in range(wl.T):
+        for g in range(wl.G):
+            if stg[t, g] >= 0:
+                np.testing.assert_array_equal(Dg["recv_x"][stg[t, g]], x[t])
+                np.testing.assert_array_equal(Dg["recv_idx"][stg[t, g]], idx[t])
+
+
+def test_dispatch_one_group_is_identity_copy(orc):
+    d = si.make_inputs(50, 64, 16, 4, seed=5)
+    L = orc.layout(d["topk_idx"], 16, 1)
+    D = orc.dispatch_bf16(L, "group", d["x"], d["topk_w"], d["topk_idx"])
+    np.testing.assert_array_equal(D["recv_x"], d["x"])
+    np.testing.assert_array_equal(D["recv_w"], d["topk_w"])
+
+
+# ------------------------------------------------------------------ codecs
+
+def test_bf16_decode_exhaustive(orc):
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bf16_to_float(allbits)
+    got = np.array([orc.bf16_to_f32(int(b)) for b in allbits], np.float32)
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+    assert np.all(np.isnan(got[~np.isfinite(ref) & np.isnan(ref)]))
+
+
+def test_bf16_encode_against_torch(orc):
+    rng = np.random.default_rng(0)
+    a = rng.standard_normal(1 << 20).astype(np.float32) * np.float32(3.0)
+    b = (rng.integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32)).view(np.float32)
+    b = b[np.isfinite(b)]
+    # exact ties: bf16 value plus half its ulp (low 16 bits = 0x8000), both parities
+    hi = rng.integers(0, 0x7F7F, 1 << 16, dtype=np.uint32)
+    ties = ((hi << 16) | 0x8000).view(np.float32)
+    for arr in (a, b, ties, -ties):
+        ref = torch.from_numpy(arr).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(orc.f32_to_bf16_array(arr), ref)
+    # the tie 1 + 2^-8 goes to 1.0, and 1 + 3*2^-8 goes to 1 + 2^-6... up to even
+    assert orc.f32_to_bf16(1.0 + 2 ** -8) == 0x3F80
+    assert orc.f32_to_bf16(1.0 + 3 * 2 ** -8) == 0x3F82
+
+
+def test_e4m3_decode_all_codes(orc):
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        got = orc.e4m3_to_f32(c)
+        if e == 15 and m == 7:
+            assert math.isnan(got)
+            continue
+        v = (2.0 ** (e - 7)) * (1 + m / 8) if e else (2.0 ** -6) * (m / 8)
+        v = -v if s else v
+        assert got == v and math.copysign(1, got) == (-1 if s else 1), c
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    got = np.array([orc.e4m3_to_f32(c) for c in range(256)], np.float32)
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[fin], ref[fin])
+    assert np.isnan(got[~fin]).all()
+
+
+def test_e4m3_encode_against_torch_and_midpoints(orc):
+    rng = np.random.default_rng(1)
+    sweeps = [
+        np.linspace(-464, 464, 400001, dtype=np.float32),
+        (rng.standard_normal(1 << 20) * 60).astype(np.float32),
+        (rng.standard_normal(1 << 18) * 2e-3).astype(np.float32),   # subnormal region
+        np.float32(2.0) ** rng.uniform(-12, 8.8, 1 << 18).astype(np.float32),
+    ]
+    # every midpoint between neighbouring finite codes, both signs
+    vals = np.array([orc.e4m3_to_f32(c) for c in range(127)], np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    assert np.all(mids.astype(np.float64) == (vals[:-1] + vals[1:]) / 2)  # exact in fp32
+    sweeps += [mids, -mids]
+    for arr in sweeps:
+        arr = arr[np.abs(arr) <= 464]
+        ref = torch.from_numpy(arr).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(orc.f32_to_e4m3_array(arr), ref)
+    # midpoints go to the even code
+    enc = orc.f32_to_e4m3_array(mids)
+    assert np.all(enc % 2 == 0)
+    # saturation above the last midpoint (torch gives NaN there; the reading is satfinite)
+    assert orc.f32_to_e4m3(1e6) == 0x7E and orc.f32_to_e4m3(-500.0) == 0xFE
+    assert orc.f32_to_e4m3(-0.0) == 0x80 and orc.f32_to_e4m3(0.0) == 0
+
+
+def test_fp8_quantisation_bounds(orc):
+    d = si.make_inputs(64, 1024, 8, 2, seed=21)
+    x = d["x"]
+    xf = bf16_to_float(x)
+    for t in range(x.shape[0]):
+        q, s = orc.quantize_row_fp8(x[t])
+        for b in range(x.shape[1] // 128):
+            blk = xf[t, b * 128:(b + 1) * 128].astype(np.float64)
+            amax = np.abs(blk).max()
+            assert s[b] == np.float32(amax) / np.float32(448)
+            dq = np.array([orc.e4m3_to_f32(int(c)) for c in q[b * 128:(b + 1) * 128]])
+            # the largest element lands on +-448 exactly
+            j = int(np.abs(blk).argmax())
+            assert abs(dq[j]) == 448.0 and np.sign(dq[j]) == np.sign(blk[j])
+            rec = dq * float(s[b])
+            err = np.abs(rec - blk)
+            normal = np.abs(dq) >= 2 ** -6
+            assert np.all(err[normal] <= 2 ** -4 * np.abs(blk[normal]) * (1 + 1e-6) + 1e-30)
+            assert np.all(err[~normal] <= 2 ** -10 * float(s[b]) * (1 + 1e-6))
+
+
+def test_dequant_identity_on_exact_codes(orc):
+    # a row whose block amax is 448 has scale 1, so decode(q) * 1 recovers every
+    # input that is itself an e4m3 value
+    codes = np.arange(0, 126, dtype=np.uint8)
+    vals = np.array([orc.e4m3_to_f32(int(c)) for c in codes], np.float32)
+    row = np.zeros(128, np.float32)
+    row[:126] = vals
+    row[126] = 448.0
+    row[127] = -448.0
+    bits = bf16_bits_of(row)
+    q, s = orc.quantize_row_fp8(bits)
+    assert s[0] == 1.0
+    y = orc.dequant_fp8(q[None, :], s[None, :])
+    np.testing.assert_array_equal(y[0], bits)
+
+
+# ------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("name", ["tiny", "t256"])
+@pytest.mark.parametrize("mode", ["expert", "group"])
+def test_combine_identity_round_trip(orc, name, mode):
+    """Weights summing to 1 (to fp32 rounding) with identity experts give x back bit-exactly."""
+    d = si.make_workload(name)
+    wl = d["workload"]
+    L = orc.layout(d["topk_idx"], wl.E, wl.G)
+    D = orc.dispatch_bf16(L, mode, d["x"], d["topk_w"], d["topk_idx"])
+    out = orc.combine(L, mode, D["recv_x"], d["topk_w"])
+    np.testing.assert_array_equal(out, d["x"])
+
+
+def test_combine_scaled_expert_closed_form(orc):
+    """Expert e multiplies its rows by c_e = 1 + e/E; the result must be within
+    1 bf16 ulp of sum_k w_k c_{e_k} x_t computed in float64."""
+    T, H, E, G, K = 96, 256, 32, 4, 6
+    d = si.make_inputs(T, H, E, K, seed=31)
+    L = orc.layout(d["topk_idx"], E, G)
+    D = orc.dispatch_bf16(L, "expert", d["x"], d["topk_w"], d["topk_idx"])
+    e_of_row = np.searchsorted(L["expert_offset"], np.arange(L["R_expert"]), side="right") - 1
+    c = (1.0 + np.arange(E) / E).astype(np.float32)
+    y = bf16_bits_of(bf16_to_float(D["recv_x"]) * c[e_of_row][:, None])
+    out = bf16_to_float(orc.combine(L, "expert", y, d["topk_w"])).astype(np.float64)
+    yf = bf16_to_float(y).astype(np.float64)
+    se = L["slot_e"].reshape(T, K)
+    ref = np.zeros((T, H))
+    for k in range(K):
+        ref += d["topk_w"][:, k:k + 1].astype(np.float64) * yf[se[:, k]]
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert np.all(np.abs(out - ref) <= ulp)
+
+
+def test_combine_exact_fma_chain_brute_force(orc):
+    """Tiny inputs: the fp32 chain acc = fma(w_k, y_k, acc), k ascending from -0, then
+    one round to bf16 — emulated with exact rationals — equals the oracle bit for bit."""
+    rng = np.random.default_rng(5)
+    mism = 0
+    for trial in range(40):
+        T, H = 3, 16
+        E, G, K = 12, int(rng.choice([1, 3, 4, 12])), int(rng.integers(1, 6))
+        idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+        w = rng.standard_normal((T, K)).astype(np.float32)
+        L = orc.layout(idx, E, G)
+        for mode, R, slot in (("expert", L["R_expert"], L["slot_e"]),
+                              ("group", L["R_group"], L["slot_g"])):
+            y = bf16_bits_of(rng.standard_normal((R, H)).astype(np.float32) * 4)
+            y[rng.random(y.shape) < 0.05] = 0x8000       # some signed zeros
+            y[rng.random(y.shape) < 0.05] = 0x0000
+            yf = bf16_to_float(y)
+            out = orc.combine(L, mode, y, w)
+            ref = np.zeros((T, H), np.float32)
+            for t in range(T):
+                for i in range(H):
+                    acc = -0.0
+                    for k in range(K):
+                        acc = fma_f32(float(w[t, k]), float(yf[slot[t * K + k], i]), acc)
+                    ref[t, i] = acc
+            refb = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            mism += int((out != refb).sum())
+    assert mism == 0
+
+
+def test_combine_skips_invalid_entries(orc):
+    idx = np.array([[0, 0, 9], [1, 2, 3]], np.int32)   # repeat and out-of-range in token 0
+    w = np.array([[0.5, 0.25, 0.25], [0.5, 0.25, 0.25]], np.float32)
+    L = orc.layout(idx, 4, 2)
+    assert L["status"] == 3
+    assert L["slot_e"][1] == -1 and L["slot_e"][2] == -1
+    x = bf16_bits_of([[2.0, 4.0], [8.0, -8.0]])
+    D = orc.dispatch_bf16(L, "expert", x, w, idx)
+    out = bf16_to_float(orc.combine(L, "expert", D["recv_x"], w))
+    np.testing.assert_array_equal(out, np.array([[1.0, 2.0], [8.0, -8.0]], np.float32))
