@@ -1,0 +1,345 @@
+"""Benchmark of the MoE token path on one MI355X: layout -> dispatch -> combine.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t4096]
+
+One step = one pass of the hot path over one batch of synthetic input already
+resident in HBM: moe_layout (per-expert and per-group layout), moe_dispatch
+(bf16 rows into per-expert receive buffers) and moe_combine (fp32 weighted
+top-k sum back to bf16; the experts are identities, so combine reads the
+dispatched rows in place). Default workload: 4096 tokens x 7168 hidden bf16,
+256 experts in 8 groups, top-8 uniform routing.
+
+Prints ONE JSON line. `value` = algorithmic HBM bytes of a step (reads + writes,
+each byte counted once) / wall time per step. Per-kernel times come from HIP
+events recorded around every launch in the timed region, on the stream the
+kernels run on. The same line carries the roofline of the dominant kernel, the
+CPU oracle timed on host cores (a bounded sample of the same workload), and
+secondary measurements (the deduplicated per-group layout, FP8 dispatch on the
+FP8 workload, a plain copy ceiling, flushed-cache timings).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, 8 TB/s
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+
+def layout_bytes(T, K, E, G, P):
+    return T * K * 4 + (2 * E + 2 * G + 2) * 4 + T * 4 + 3 * T * K * 4 + T * G * 4 + P * 4
+
+
+def dispatch_bytes(T, H, K, G, R, mode, fp8=False):
+    reads = T * H * 2 + T * K * 8 + (T * K * 4 if mode == "expert" else T * G * 4)
+    row = (H + (H // 128) * 4 if fp8 else H * 2) + K * 8
+    return reads, R * row
+
+
+def combine_bytes(T, H, K, R):
+    return R * H * 2 + T * K * 4 + T * K * 4, T * H * 2
+
+
+# ------------------------------------------------------------------ helpers
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "combine_moe_layout_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        h.update(fn.encode())
+        h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str):
+    """HBM traffic of a kernel from committed rocprofv3 --pmc counters, if they were
+    taken on the current kernel sources; None otherwise."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    if d.get("source_hash") != source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("traffic_bytes")
+
+
+def stats(v):
+    import numpy as np
+    a = np.asarray(v, dtype=np.float64)
+    return {"median": float(np.median(a)), "mean": float(a.mean()), "std": float(a.std()),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+            "best": float(a.min())}
+
+
+class Dev:
+    """Device copies of one workload and its buffers."""
+
+    def __init__(self, moe, d, modes=("expert",), dtype="bf16"):
+        import numpy as np
+        import torch
+        wl = d["workload"]
+        self.wl = wl
+        self.x = torch.from_numpy(d["x"].view(np.int16)).cuda().view(torch.bfloat16)
+        self.w = torch.from_numpy(d["topk_w"]).cuda()
+        self.idx = torch.from_numpy(d["topk_idx"]).cuda()
+        self.L = moe.Layout.empty(wl.T, wl.K, wl.E, wl.G)
+        self.D = {m: moe.alloc_dispatch(self.L, wl.H, m, dtype) for m in modes}
+        self.out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+        self.y = {}
+
+
+def time_calls(fns, iters, flush=None):
+    """Median-able per-call times (µs) of each fn in fns, run in sequence per iteration,
+    each bracketed by events on the current stream; optional flush outside the events."""
+    import torch
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in fns] for _ in range(iters)]
+    for it in range(iters):
+        for j, fn in enumerate(fns):
+            if flush is not None:
+                flush()
+            a, b = ev[it][j]
+            a.record()
+            fn()
+            b.record()
+    torch.cuda.synchronize()
+    return [[ev[it][j][0].elapsed_time(ev[it][j][1]) * 1e3 for it in range(iters)]
+            for j in range(len(fns))]
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(d, budget_s=12.0):
+    """The oracle (single-threaded C, as it stands) on the same workload: whole steps
+    (layout + EXPERT dispatch + combine) repeated until the time budget is spent."""
+    import oracle
+    wl = d["workload"]
+    T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K
+    steps, t_layout, t_disp, t_comb, nbytes = 0, 0.0, 0.0, 0.0, 0
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        Lo = oracle.layout(d["topk_idx"], E, G)
+        t1 = time.perf_counter()
+        Do = oracle.dispatch_bf16(Lo, "expert", d["x"], d["topk_w"], d["topk_idx"])
+        t2 = time.perf_counter()
+        oracle.combine(Lo, "expert", Do["recv_x"], d["topk_w"])
+        t3 = time.perf_counter()
+        steps += 1
+        t_layout += t1 - t0
+        t_disp += t2 - t1
+        t_comb += t3 - t2
+        R = Lo["R_expert"]
+        nbytes += (layout_bytes(T, K, E, G, Lo["R_group"]) + sum(dispatch_bytes(T, H, K, G, R, "expert"))
+                   + sum(combine_bytes(T, H, K, R)))
+        del Do
+        if time.perf_counter() - t_start > budget_s or steps >= 50:
+            break
+    total = t_layout + t_disp + t_comb
+    return {
+        "value": nbytes / total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{steps} whole step(s) of the {wl.name} workload (layout + per-expert "
+                   f"dispatch + combine) by the single-threaded C oracle, {total:.1f} s"),
+        "ms_per_step": total / steps * 1e3,
+        "ms_layout": t_layout / steps * 1e3, "ms_dispatch": t_disp / steps * 1e3,
+        "ms_combine": t_comb / steps * 1e3,
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="t4096")
+    ap.add_argument("--no-extras", action="store_true", help="only the timed steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the expert groups of one EP rank live in one GPU's HBM)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import combine_moe_layout_amd as moe
+    import synth_inputs as si
+
+    torch.cuda.init()
+    d = si.make_workload(args.workload)
+    wl = d["workload"]
+    T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K
+    dv = Dev(moe, d, modes=("expert",))
+    L, D, out = dv.L, dv.D["expert"], dv.out
+
+    def launches():
+        return [
+            lambda: moe.moe_layout(dv.idx, E, G, out=L),
+            lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "expert", "bf16", out=D),
+            lambda: moe.moe_combine(L, D.recv_x, dv.w, "expert", out=out),
+        ]
+
+    fns = launches()
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        e = ev[s]
+        e[0].record()
+        fns[0]()
+        e[1].record()
+        fns[1]()
+        e[2].record()
+        fns[2]()
+        e[3].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+    us = {name: [ev[s][i].elapsed_time(ev[s][i + 1]) * 1e3 for s in range(args.steps)]
+          for i, name in enumerate(("layout", "dispatch", "combine"))}
+
+    assert int(L.status.item()) == 0
+    R = int(L.expert_offset[E].item())
+    P = int(L.group_offset[G].item())
+    b_layout = layout_bytes(T, K, E, G, P)
+    d_r, d_w = dispatch_bytes(T, H, K, G, R, "expert")
+    c_r, c_w = combine_bytes(T, H, K, R)
+    step_bytes = b_layout + d_r + d_w + c_r + c_w
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    avg = {k: float(np.mean(v)) for k, v in us.items()}
+    kern = {"dispatch": (d_r + d_w, avg["dispatch"]), "combine": (c_r + c_w, avg["combine"])}
+    dom = max(kern, key=lambda k: kern[k][1])
+    ach = kern[dom][0] / (kern[dom][1] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": load_traffic(f"{dom}_expert_bf16"),
+                "kernel": f"{dom} (per-expert bf16)", "algorithmic_bytes": kern[dom][0],
+                "avg_us": round(kern[dom][1], 2)}
+
+    result = {
+        "metric": "dispatch & combine HBM GB/s (and % peak) at 4096 tok×7168 bf16 top-8, 1 GPU",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {T} tokens x {H} hidden bf16, {E} experts in {G} groups, "
+                               f"top-{K} {wl.routing} routing, per-expert receive buffers",
+                   "tokens": T, "hidden": H, "experts": E, "groups": G, "topk": K,
+                   "routing": wl.routing, "receive_layout": "expert", "seed": wl.seed},
+        "roofline": roofline,
+        "kernels_us": {k: {kk: round(vv, 2) for kk, vv in stats(v).items()} for k, v in us.items()},
+        "kernels_gbs": {
+            "dispatch": round((d_r + d_w) / (avg["dispatch"] * 1e-6) / 1e9, 1),
+            "combine": round((c_r + c_w) / (avg["combine"] * 1e-6) / 1e9, 1),
+            "layout_us": round(avg["layout"], 2),
+            "dispatch_payload_gbs": round(R * H * 2 / (avg["dispatch"] * 1e-6) / 1e9, 1),
+            "combine_payload_gbs": round(R * H * 2 / (avg["combine"] * 1e-6) / 1e9, 1),
+        },
+        "bytes": {"layout": b_layout, "dispatch": d_r + d_w, "combine": c_r + c_w, "rows": R,
+                  "group_rows": P},
+        "source_hash": source_hash(),
+    }
+
+    if not args.no_extras:
+        result["extra"] = extras(moe, d, dv, args)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def extras(moe, d, dv, args):
+    """Secondary measurements (not part of `value`): GROUP layout, FP8 dispatch on
+    the FP8 workload, flushed-cache timings, and a plain copy ceiling."""
+    import numpy as np
+    import torch
+    import synth_inputs as si
+    wl = dv.wl
+    T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K
+    it = 30
+    res = {}
+    L = dv.L
+    moe.moe_layout(dv.idx, E, G, out=L)
+    P = int(L.group_offset[G].item())
+    R = int(L.expert_offset[E].item())
+    Dg = moe.alloc_dispatch(L, H, "group")
+    disp_g = lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "group", "bf16", out=Dg)
+    comb_g = lambda: moe.moe_combine(L, Dg.recv_x, dv.w, "group", out=dv.out)
+    disp_g(); comb_g()
+    tg = time_calls([disp_g, comb_g], it)
+    bd, bc = sum(dispatch_bytes(T, H, K, G, P, "group")), sum(combine_bytes(T, H, K, P))
+    res["group"] = {"rows": P, "dispatch_us": stats(tg[0])["median"], "combine_us": stats(tg[1])["median"],
+                    "dispatch_gbs": round(bd / stats(tg[0])["median"] / 1e3, 1),
+                    "combine_gbs": round(bc / stats(tg[1])["median"] / 1e3, 1)}
+    del Dg
+
+    # flushed-cache timing of the per-expert kernels (the 256 MB last-level cache is
+    # overwritten before every call, outside the timed events)
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = lambda: scratch.fill_(1)
+    De = dv.D["expert"]
+    disp_e = lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "expert", "bf16", out=De)
+    comb_e = lambda: moe.moe_combine(L, De.recv_x, dv.w, "expert", out=dv.out)
+    tc = time_calls([disp_e, comb_e], 15, flush=flush)
+    bde, bce = sum(dispatch_bytes(T, H, K, G, R, "expert")), sum(combine_bytes(T, H, K, R))
+    res["expert_flushed"] = {"dispatch_us": stats(tc[0])["median"], "combine_us": stats(tc[1])["median"],
+                             "dispatch_gbs": round(bde / stats(tc[0])["median"] / 1e3, 1),
+                             "combine_gbs": round(bce / stats(tc[1])["median"] / 1e3, 1)}
+
+    # plain copy ceiling: 2 x 512 MiB streaming copy
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(3)
+    cp = lambda: moe.moe_ref_copy(dst, src)
+    cp()
+    tcp = time_calls([cp], 20)
+    res["copy_ceiling"] = {"bytes": 2 * n, "us": stats(tcp[0])["median"],
+                           "gbs": round(2 * n / stats(tcp[0])["median"] / 1e3, 1)}
+    del src, dst, scratch
+
+    # FP8 dispatch on the FP8 workload (same shape, its own seed), both layouts
+    d8 = si.make_workload("fp8")
+    w8 = d8["workload"]
+    dv8 = Dev(moe, d8, modes=("expert", "group"), dtype="fp8")
+    moe.moe_layout(dv8.idx, w8.E, w8.G, out=dv8.L)
+    R8 = int(dv8.L.expert_offset[w8.E].item())
+    P8 = int(dv8.L.group_offset[w8.G].item())
+    f8 = {}
+    for mode, rows in (("expert", R8), ("group", P8)):
+        D8 = dv8.D[mode]
+        fn = lambda: moe.moe_dispatch(dv8.L, dv8.x, dv8.w, dv8.idx, mode, "fp8", out=D8)
+        fn()
+        t8 = time_calls([fn], it)
+        b8 = sum(dispatch_bytes(w8.T, w8.H, w8.K, w8.G, rows, mode, fp8=True))
+        f8[mode] = {"rows": rows, "dispatch_us": stats(t8[0])["median"],
+                    "dispatch_gbs": round(b8 / stats(t8[0])["median"] / 1e3, 1)}
+    res["fp8_dispatch"] = f8
+    del dv8
+    torch.cuda.synchronize()
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+"""MoE token path on one MI355X (gfx950): routing layout -> dispatch -> combine.
+
+A thin Python binding over the C ABI of libmoe_ep.so (include/moe_ep.h). It
+only marshals arguments: every step of the path runs in the library's HIP
+kernels, on the current torch stream. torch provides device memory and
+streams; the helpers below allocate outputs with torch when the caller does
+not pass them.
+
+The binding names follow the C ABI:
+    moe_layout(topk_idx, E, G)                          -> Layout
+    moe_dispatch(L, x, topk_w, topk_idx, mode, dtype)   -> Dispatched
+    moe_combine(L, y, topk_w, mode)                     -> bf16 [T, H]
+    moe_fp8_dequant(L, q, scale, mode)                  -> bf16 [capacity, H]
+If the library is missing this module raises on import; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+__all__ = [
+    "MoeError", "Layout", "Dispatched", "moe_layout", "moe_dispatch", "moe_combine",
+    "moe_fp8_dequant", "moe_ref_copy", "recv_rows_bound", "layout_workspace_bytes",
+    "library_path", "MODE_EXPERT", "MODE_GROUP", "DTYPE_BF16", "DTYPE_FP8",
+    "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libmoe_ep.so")
+
+MODE_EXPERT, MODE_GROUP = 0, 1
+DTYPE_BF16, DTYPE_FP8 = 0, 1
+STATUS_BAD_INDEX, STATUS_DUPLICATE, STATUS_Y_ROWS = 1, 2, 4
+_MODES = {"expert": MODE_EXPERT, "group": MODE_GROUP, MODE_EXPERT: MODE_EXPERT, MODE_GROUP: MODE_GROUP}
+_DTYPES = {"bf16": DTYPE_BF16, "fp8": DTYPE_FP8, DTYPE_BF16: DTYPE_BF16, DTYPE_FP8: DTYPE_FP8}
+
+_P = ctypes.c_void_p
+
+
+class _LayoutT(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("K", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("G", ctypes.c_int32)] + [(n, _P) for n in (
+                    "expert_count", "expert_offset", "group_count", "group_offset",
+                    "tok_group_mask", "slot_e", "slot_g", "slot_tg", "recv_src_e",
+                    "recv_src_g", "status")]
+
+
+def _load_library() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m combine_moe_layout_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    LP = ctypes.POINTER(_LayoutT)
+    sig = {
+        "moe_abi_version": (i32, []),
+        "moe_layout_workspace_bytes": (i32, [i32, i32, i32, i32, ctypes.POINTER(sz)]),
+        "moe_recv_rows_bound": (i64, [i32, i32, i32, i32]),
+        "moe_layout": (i32, [_P, LP, _P, sz, _P]),
+        "moe_dispatch": (i32, [LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, _P, i64, _P]),
+        "moe_combine": (i32, [LP, i32, i32, _P, i64, _P, _P, _P]),
+        "moe_fp8_dequant": (i32, [LP, i32, i32, _P, _P, _P, i64, _P]),
+        "moe_ref_copy": (i32, [_P, _P, i64, _P]),
+        "moe_status_string": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load_library()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {_lib.moe_status_string(code).decode()} (code {code})")
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise MoeError(rc, where)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _mode(mode) -> int:
+    if mode not in _MODES:
+        raise MoeError(-7, f"mode {mode!r}")
+    return _MODES[mode]
+
+
+def _dtype(dtype) -> int:
+    if dtype not in _DTYPES:
+        raise MoeError(-7, f"dtype {dtype!r}")
+    return _DTYPES[dtype]
+
+
+def recv_rows_bound(T: int, K: int, G: int, mode="expert") -> int:
+    r = _lib.moe_recv_rows_bound(T, K, G, _mode(mode))
+    if r < 0:
+        raise MoeError(int(r), "moe_recv_rows_bound")
+    return int(r)
+
+
+def layout_workspace_bytes(T: int, K: int, E: int, G: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_layout_workspace_bytes(T, K, E, G, ctypes.byref(n)), "moe_layout_workspace_bytes")
+    return int(n.value)
+
+
+@dataclasses.dataclass
+class Layout:
+    """Device arrays of one routing layout (see moe_layout_t in include/moe_ep.h)."""
+    T: int
+    K: int
+    E: int
+    G: int
+    expert_count: torch.Tensor
+    expert_offset: torch.Tensor
+    group_count: torch.Tensor
+    group_offset: torch.Tensor
+    tok_group_mask: torch.Tensor
+    slot_e: torch.Tensor
+    slot_g: torch.Tensor
+    slot_tg: torch.Tensor
+    recv_src_e: torch.Tensor
+    recv_src_g: torch.Tensor
+    status: torch.Tensor
+    workspace: torch.Tensor
+
+    @classmethod
+    def empty(cls, T: int, K: int, E: int, G: int, device="cuda") -> "Layout":
+        i32 = dict(dtype=torch.int32, device=device)
+        ws = layout_workspace_bytes(T, K, E, G)
+        return cls(T, K, E, G,
+                   torch.empty(E, **i32), torch.empty(E + 1, **i32),
+                   torch.empty(G, **i32), torch.empty(G + 1, **i32),
+                   torch.empty(T, **i32),    # uint32 bits, held as int32
+                   torch.empty(T * K, **i32), torch.empty(T * K, **i32),
+                   torch.empty(T * G, **i32), torch.empty(T * K, **i32),
+                   torch.empty(T * min(K, G), **i32), torch.zeros(1, **i32),
+                   torch.empty(max(ws, 1), dtype=torch.uint8, device=device))
+
+    def struct(self) -> _LayoutT:
+        return _LayoutT(self.T, self.K, self.E, self.G, *(self._addr(n) for n in (
+            "expert_count", "expert_offset", "group_count", "group_offset", "tok_group_mask",
+            "slot_e", "slot_g", "slot_tg", "recv_src_e", "recv_src_g", "status")))
+
+    def _addr(self, name: str) -> int:
+        return getattr(self, name).data_ptr()
+
+    def rows(self, mode="expert") -> torch.Tensor:
+        """Device scalar tensor: number of receive rows in `mode`."""
+        return self.expert_offset[self.E] if _mode(mode) == MODE_EXPERT else self.group_offset[self.G]
+
+    def slots(self, mode="expert") -> torch.Tensor:
+        return self.slot_e if _mode(mode) == MODE_EXPERT else self.slot_g
+
+
+def moe_layout(topk_idx: torch.Tensor, E: int, G: int, *, out: Layout | None = None,
+               stream=None) -> Layout:
+    """Routing layout of device int32 [T, K] expert indices (moe_layout)."""
+    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be a contiguous int32 [T, K] tensor")
+    T, K = topk_idx.shape
+    L = out if out is not None else Layout.empty(T, K, E, G, device=topk_idx.device)
+    if (L.T, L.K, L.E, L.G) != (T, K, E, G):
+        raise ValueError("layout buffers were made for other sizes")
+    st = L.struct()
+    _check(_lib.moe_layout(_ptr(topk_idx), ctypes.byref(st), _ptr(L.workspace),
+                           L.workspace.numel(), _stream(stream)), "moe_layout")
+    return L
+
+
+@dataclasses.dataclass
+class Dispatched:
+    recv_x: torch.Tensor          # bf16 [cap, H] or uint8 [cap, H]
+    recv_scale: torch.Tensor | None   # fp32 [cap, H/128] for FP8
+    recv_topk_w: torch.Tensor     # fp32 [cap, K]
+    recv_topk_idx: torch.Tensor   # int32 [cap, K]
+
+
+def alloc_dispatch(L: Layout, H: int, mode="expert", dtype="bf16", device="cuda",
+                   capacity: int | None = None) -> Dispatched:
+    cap = recv_rows_bound(L.T, L.K, L.G, mode) if capacity is None else capacity
+    fp8 = _dtype(dtype) == DTYPE_FP8
+    return Dispatched(
+        torch.empty((cap, H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=device),
+        torch.empty((cap, H // 128), dtype=torch.float32, device=device) if fp8 else None,
+        torch.empty((cap, L.K), dtype=torch.float32, device=device),
+        torch.empty((cap, L.K), dtype=torch.int32, device=device))
+
+
+def moe_dispatch(L: Layout, x: torch.Tensor, topk_w: torch.Tensor, topk_idx: torch.Tensor,
+                 mode="expert", dtype="bf16", *, out: Dispatched | None = None,
+                 stream=None) -> Dispatched:
+    """Scatter bf16 rows x [T, H] (+ weights, indices) into receive buffers (moe_dispatch)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [T, H] tensor")
+    for t, dt in ((topk_w, torch.float32), (topk_idx, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != (L.T, L.K):
+            raise ValueError("topk_w / topk_idx must be contiguous [T, K] fp32 / int32")
+    H = x.shape[1]
+    D = out if out is not None else alloc_dispatch(L, H, mode, dtype, x.device)
+    st = L.struct()
+    _check(_lib.moe_dispatch(ctypes.byref(st), _mode(mode), _dtype(dtype), H, _ptr(x),
+                             _ptr(topk_w), _ptr(topk_idx), _ptr(D.recv_x), _ptr(D.recv_scale),
+                             _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
+                             _stream(stream)), "moe_dispatch")
+    return D
+
+
+def moe_combine(L: Layout, y: torch.Tensor, topk_w: torch.Tensor, mode="expert", *,
+                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Weighted top-k sum of expert outputs y (bf16 [rows, H]) per token (moe_combine)."""
+    if y.dtype != torch.bfloat16 or y.dim() != 2 or not y.is_contiguous():
+        raise ValueError("y must be a contiguous bf16 [rows, H] tensor")
+    H = y.shape[1]
+    o = out if out is not None else torch.empty((L.T, H), dtype=torch.bfloat16, device=y.device)
+    st = L.struct()
+    _check(_lib.moe_combine(ctypes.byref(st), _mode(mode), H, _ptr(y), y.shape[0], _ptr(topk_w),
+                            _ptr(o), _stream(stream)), "moe_combine")
+    return o
+
+
+def moe_fp8_dequant(L: Layout, q: torch.Tensor, scale: torch.Tensor, mode="expert", *,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Identity expert on FP8 receive rows: bf16(decode(q) * scale) (moe_fp8_dequant)."""
+    cap, H = q.shape
+    y = out if out is not None else torch.empty((cap, H), dtype=torch.bfloat16, device=q.device)
+    st = L.struct()
+    _check(_lib.moe_fp8_dequant(ctypes.byref(st), _mode(mode), H, _ptr(q), _ptr(scale), _ptr(y),
+                                cap, _stream(stream)), "moe_fp8_dequant")
+    return y
+
+
+def moe_ref_copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int | None = None,
+                 stream=None) -> None:
+    """Plain 16-byte streaming copy (measurement reference, not part of the method)."""
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(_lib.moe_ref_copy(_ptr(dst), _ptr(src), n, _stream(stream)), "moe_ref_copy")

@@ -1,0 +1,194 @@
+// The C ABI of the MoE token path (declared in include/moe_ep.h): argument
+// checks on the host, then kernel launches on the caller's stream. Every
+// check happens before the first HIP call, so a rejected call touches neither
+// the device nor the HIP runtime.
+#include "moe_ep.h"
+
+#include "kernels.hpp"
+
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_hip_msg[160] = "";
+
+int hip_fail(hipError_t e)
+{
+    snprintf(g_hip_msg, sizeof g_hip_msg, "%s (%d)", hipGetErrorString(e), (int)e);
+    return MOE_ERR_HIP;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+int check_dims(int T, int K, int E, int G)
+{
+    if (T < 0 || K < 1 || K > MOE_MAX_TOPK || E < K || E > MOE_MAX_EXPERTS || G < 1 ||
+        G > MOE_MAX_GROUPS || E % G != 0)
+        return MOE_ERR_BAD_SHAPE;
+    const int64_t m = K > G ? K : G;
+    if ((int64_t)T * m >= (int64_t)1 << 30) return MOE_ERR_BAD_SHAPE;
+    return MOE_OK;
+}
+
+// The count / offset / status arrays are always required; the per-token
+// arrays only when there are tokens (T = 0 callers may pass NULL for them).
+int check_layout_ptrs(const moe_layout_t *L)
+{
+    if (!L) return MOE_ERR_NULL_PTR;
+    if (!L->expert_count || !L->expert_offset || !L->group_count || !L->group_offset || !L->status)
+        return MOE_ERR_NULL_PTR;
+    if (L->T > 0 && (!L->tok_group_mask || !L->slot_e || !L->slot_g || !L->slot_tg ||
+                     !L->recv_src_e || !L->recv_src_g))
+        return MOE_ERR_NULL_PTR;
+    return MOE_OK;
+}
+
+size_t layout_ws_bytes(int T, int E, int G)
+{
+    const size_t tiles = (size_t)moe::layout_tiles(T);
+    const size_t b = 4 * ((size_t)E + G + 1) * tiles;
+    return (b + 255) & ~(size_t)255;
+}
+
+int64_t rows_bound(int T, int K, int G, int mode)
+{
+    return mode == MOE_MODE_EXPERT ? (int64_t)T * K : (int64_t)T * (K < G ? K : G);
+}
+
+moe::LayoutPtrs ptrs_of(const moe_layout_t *L)
+{
+    return moe::LayoutPtrs{L->expert_count, L->expert_offset, L->group_count, L->group_offset,
+                           L->tok_group_mask, L->slot_e, L->slot_g, L->slot_tg,
+                           L->recv_src_e, L->recv_src_g, L->status};
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_EP_ABI_VERSION; }
+
+int moe_layout_workspace_bytes(int T, int K, int E, int G, size_t *bytes)
+{
+    if (!bytes) return MOE_ERR_NULL_PTR;
+    if (int rc = check_dims(T, K, E, G)) return rc;
+    *bytes = layout_ws_bytes(T, E, G);
+    return MOE_OK;
+}
+
+int64_t moe_recv_rows_bound(int T, int K, int G, int mode)
+{
+    if (mode != MOE_MODE_EXPERT && mode != MOE_MODE_GROUP) return MOE_ERR_BAD_MODE;
+    if (T < 0 || K < 1 || G < 1) return MOE_ERR_BAD_SHAPE;
+    return rows_bound(T, K, G, mode);
+}
+
+int moe_layout(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t ws_bytes,
+               void *stream)
+{
+    if (int rc = check_layout_ptrs(L)) return rc;
+    if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
+    if (L->T > 0) {
+        if (!topk_idx) return MOE_ERR_NULL_PTR;
+        if (!ws || ws_bytes < layout_ws_bytes(L->T, L->E, L->G)) return MOE_ERR_WORKSPACE;
+        if (!aligned4(topk_idx) || !aligned4(ws)) return MOE_ERR_MISALIGNED;
+    }
+    hipError_t e = moe::launch_layout(topk_idx, L->T, L->K, L->E, L->G, ptrs_of(L),
+                                      static_cast<int32_t *>(ws), (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *x,
+                 const float *topk_w, const int32_t *topk_idx, void *recv_x, float *recv_scale,
+                 float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity, void *stream)
+{
+    if (int rc = check_layout_ptrs(L)) return rc;
+    if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
+    if (mode != MOE_MODE_EXPERT && mode != MOE_MODE_GROUP) return MOE_ERR_BAD_MODE;
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_B128) return MOE_ERR_BAD_MODE;
+    if (H <= 0 || H % 8 != 0) return MOE_ERR_BAD_SHAPE;
+    if (dtype == MOE_DTYPE_FP8_E4M3_B128 && H % 128 != 0) return MOE_ERR_BAD_SHAPE;
+    if (L->T == 0) return MOE_OK;
+    if (!x || !topk_w || !topk_idx || !recv_x || !recv_topk_w || !recv_topk_idx)
+        return MOE_ERR_NULL_PTR;
+    if (dtype == MOE_DTYPE_FP8_E4M3_B128 && !recv_scale) return MOE_ERR_NULL_PTR;
+    if (recv_capacity < rows_bound(L->T, L->K, L->G, mode)) return MOE_ERR_CAPACITY;
+    if (!aligned16(x) || !aligned16(recv_x) || !aligned4(topk_w) || !aligned4(topk_idx) ||
+        !aligned4(recv_topk_w) || !aligned4(recv_topk_idx) ||
+        (recv_scale && !aligned4(recv_scale)))
+        return MOE_ERR_MISALIGNED;
+    const int nslot = mode == MOE_MODE_EXPERT ? L->K : L->G;
+    const int32_t *slots = mode == MOE_MODE_EXPERT ? L->slot_e : L->slot_tg;
+    hipError_t e;
+    if (dtype == MOE_DTYPE_BF16)
+        e = moe::launch_dispatch_bf16(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
+                                      recv_topk_w, recv_topk_idx, (hipStream_t)stream);
+    else
+        e = moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
+                                     recv_scale, recv_topk_w, recv_topk_idx, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_combine(const moe_layout_t *L, int mode, int H, const void *y, int64_t y_rows,
+                const float *topk_w, void *out, void *stream)
+{
+    if (int rc = check_layout_ptrs(L)) return rc;
+    if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
+    if (mode != MOE_MODE_EXPERT && mode != MOE_MODE_GROUP) return MOE_ERR_BAD_MODE;
+    if (H <= 0 || H % 8 != 0 || y_rows < 0) return MOE_ERR_BAD_SHAPE;
+    if (L->T == 0) return MOE_OK;
+    if (!y || !topk_w || !out) return MOE_ERR_NULL_PTR;
+    if (!aligned16(y) || !aligned16(out) || !aligned4(topk_w)) return MOE_ERR_MISALIGNED;
+    const int32_t *slot = mode == MOE_MODE_EXPERT ? L->slot_e : L->slot_g;
+    hipError_t e = moe::launch_combine(y, y_rows, L->T, H, L->K, slot, topk_w, out, L->status,
+                                       (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_fp8_dequant(const moe_layout_t *L, int mode, int H, const void *q, const float *scale,
+                    void *y, int64_t capacity, void *stream)
+{
+    if (int rc = check_layout_ptrs(L)) return rc;
+    if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
+    if (mode != MOE_MODE_EXPERT && mode != MOE_MODE_GROUP) return MOE_ERR_BAD_MODE;
+    if (H <= 0 || H % 128 != 0 || capacity < 0 || capacity >= ((int64_t)1 << 31))
+        return MOE_ERR_BAD_SHAPE;
+    if (L->T == 0 || capacity == 0) return MOE_OK;
+    if (!q || !scale || !y) return MOE_ERR_NULL_PTR;
+    if (!aligned16(q) || !aligned16(y) || !aligned4(scale)) return MOE_ERR_MISALIGNED;
+    const int32_t *nrows = mode == MOE_MODE_EXPERT ? L->expert_offset + L->E : L->group_offset + L->G;
+    hipError_t e = moe::launch_fp8_dequant(q, scale, y, capacity, H, nrows, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_ref_copy(void *dst, const void *src, int64_t bytes, void *stream)
+{
+    if (bytes < 0 || bytes % 16 != 0) return MOE_ERR_BAD_SHAPE;
+    if (bytes == 0) return MOE_OK;
+    if (!dst || !src) return MOE_ERR_NULL_PTR;
+    if (!aligned16(dst) || !aligned16(src)) return MOE_ERR_MISALIGNED;
+    hipError_t e = moe::launch_ref_copy(dst, src, bytes, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+const char *moe_status_string(int code)
+{
+    static thread_local char buf[256];
+    switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MOE_ERR_BAD_SHAPE: return "shape outside the supported range";
+    case MOE_ERR_MISALIGNED: return "buffer not aligned (rows need 16 bytes, others 4)";
+    case MOE_ERR_CAPACITY: return "receive buffer smaller than moe_recv_rows_bound()";
+    case MOE_ERR_WORKSPACE: return "layout workspace missing or smaller than moe_layout_workspace_bytes()";
+    case MOE_ERR_BAD_MODE: return "unknown mode or dtype";
+    case MOE_ERR_HIP:
+        snprintf(buf, sizeof buf, "HIP error: %s", g_hip_msg);
+        return buf;
+    default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

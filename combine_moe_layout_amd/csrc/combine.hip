@@ -1,0 +1,220 @@
+// Combine on gfx950: gather each token's expert outputs and reduce them as a
+// weighted top-k sum, accumulated in fp32 in fixed k order and rounded once
+// to bf16. Also the FP8 identity expert (dequantisation glue) and a plain
+// copy kernel used as a measurement reference.
+//
+// Combine is what "perf(ep): optimize IntraNode dispatch kernel for MI350X"
+// (ROCm/mori pull request 586) describes as reads of the expert rows plus FMA
+// accumulation with no routing phase ("Remaining gap — profiled root cause"):
+// the rows are found through the layout's cached slots. The single rounding
+// of an fp32 accumulator follows ROCm/vllm pull request 1297, Accuracy.
+//
+// Design. One workgroup per token; each lane owns 8 consecutive elements
+// (one 16-byte vector) of the output row per pass. For a token whose K slots
+// are all valid (the normal case) the K row vectors are loaded first — K
+// independent 16-byte loads in flight per lane — and then folded with K fmaf
+// per element in k order, starting from -0. Tokens with skipped entries take
+// a general loop with the same arithmetic. Nothing here is a dense
+// contraction (K <= 32 weights per row), so there is no MFMA: the kernel is
+// bound by the HBM reads of the expert rows.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "moe_ep.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kCombineBS = 128;
+constexpr int kMaxIter = 8;
+
+__device__ __forceinline__ void fma8(float (&acc)[8], float w, u32x4 v)
+{
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        acc[2 * m] = fmaf(w, bf16_lo(v[m]), acc[2 * m]);
+        acc[2 * m + 1] = fmaf(w, bf16_hi(v[m]), acc[2 * m + 1]);
+    }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float (&acc)[8])
+{
+    return u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+}
+
+// KT > 0: fast path compiled for exactly KT valid entries; KT == 0: general only.
+template <int ITER, int KT, bool NT, bool FULL>
+__global__ __launch_bounds__(kCombineBS) void combine_kernel(
+    const u32x4 *__restrict__ y, int64_t y_rows, int nvec, int K,
+    const int32_t *__restrict__ slot, const float *__restrict__ topk_w, u32x4 *__restrict__ out,
+    int32_t *__restrict__ status)
+{
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int32_t *ts = slot + (size_t)t * K;
+    const float *tw = topk_w + (size_t)t * K;
+    u32x4 *orow = out + (size_t)t * nvec;
+
+    bool fast = KT > 0 && KT == K;
+    if constexpr (KT > 0) {
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            const int s = ts[k];
+            fast = fast && s >= 0 && s < y_rows;
+        }
+    }
+
+    if constexpr (KT > 0) {
+        if (fast) {
+            const u32x4 *rows[KT];
+            float w[KT];
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                rows[k] = y + (size_t)ts[k] * nvec;
+                w[k] = tw[k];
+            }
+            for (int base = 0; base < nvec; base += kCombineBS * ITER) {
+#pragma unroll
+                for (int i = 0; i < ITER; ++i) {
+                    const int j = base + i * kCombineBS + tid;
+                    if (FULL || j < nvec) {
+                        u32x4 v[KT];
+#pragma unroll
+                        for (int k = 0; k < KT; ++k) v[k] = rows[k][j];
+                        float acc[8];
+#pragma unroll
+                        for (int m = 0; m < 8; ++m) acc[m] = -0.f;
+#pragma unroll
+                        for (int k = 0; k < KT; ++k) fma8(acc, w[k], v[k]);
+                        store16<NT>(orow + j, pack8(acc));
+                    }
+                }
+            }
+            return;
+        }
+    }
+
+    // General path: any K, entries with slot < 0 skipped, slots >= y_rows
+    // skipped and reported.
+    if (tid == 0) {
+        for (int k = 0; k < K; ++k)
+            if (ts[k] >= y_rows) { atomicOr(status, MOE_STATUS_Y_ROWS); break; }
+    }
+    for (int j = tid; j < nvec; j += kCombineBS) {
+        float acc[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) acc[m] = -0.f;
+        for (int k = 0; k < K; ++k) {
+            const int s = ts[k];
+            if (s < 0 || s >= y_rows) continue;
+            fma8(acc, tw[k], y[(size_t)s * nvec + j]);
+        }
+        store16<NT>(orow + j, pack8(acc));
+    }
+}
+
+template <int ITER, int KT>
+auto pick_full(bool nt, bool full)
+{
+    if (nt) return full ? combine_kernel<ITER, KT, true, true> : combine_kernel<ITER, KT, true, false>;
+    return full ? combine_kernel<ITER, KT, false, true> : combine_kernel<ITER, KT, false, false>;
+}
+
+template <int KT>
+auto pick_iter(int iter, bool nt, bool full)
+{
+    switch (iter) {
+    case 1: return pick_full<1, KT>(nt, full);
+    case 2: return pick_full<2, KT>(nt, full);
+    case 3: return pick_full<3, KT>(nt, full);
+    case 4: return pick_full<4, KT>(nt, full);
+    case 5: return pick_full<5, KT>(nt, full);
+    case 6: return pick_full<6, KT>(nt, full);
+    case 7: return pick_full<7, KT>(nt, full);
+    default: return pick_full<8, KT>(nt, full);
+    }
+}
+
+__global__ __launch_bounds__(256) void fp8_dequant_kernel(
+    const u32x4 *__restrict__ q, const float *__restrict__ scale, u32x4 *__restrict__ y, int nch,
+    const int32_t *__restrict__ nrows)
+{
+    const int r = blockIdx.x;
+    if (r >= *nrows) return;
+    const int nblk = nch / 8;
+    for (int j = threadIdx.x; j < nch; j += blockDim.x) {
+        const u32x4 v = q[(size_t)r * nch + j];
+        const float s = scale[(size_t)r * nblk + (j >> 3)];
+        uint32_t o[8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int word = (int)v[m];
+            const float f0 = __builtin_amdgcn_cvt_f32_fp8(word, 0) * s;
+            const float f1 = __builtin_amdgcn_cvt_f32_fp8(word, 1) * s;
+            const float f2 = __builtin_amdgcn_cvt_f32_fp8(word, 2) * s;
+            const float f3 = __builtin_amdgcn_cvt_f32_fp8(word, 3) * s;
+            o[2 * m] = pack_bf16x2(f0, f1);
+            o[2 * m + 1] = pack_bf16x2(f2, f3);
+        }
+        y[(size_t)r * nch * 2 + 2 * j] = u32x4{o[0], o[1], o[2], o[3]};
+        y[(size_t)r * nch * 2 + 2 * j + 1] = u32x4{o[4], o[5], o[6], o[7]};
+    }
+}
+
+__global__ __launch_bounds__(256) void ref_copy_kernel(const u32x4 *__restrict__ src,
+                                                       u32x4 *__restrict__ dst, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = src[i];
+}
+
+inline int iters_for(int n, int bs)
+{
+    const int it = (n + bs - 1) / bs;
+    return it < 1 ? 1 : (it > kMaxIter ? kMaxIter : it);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, const int32_t *slot,
+                          const float *topk_w, void *out, int32_t *status, hipStream_t stream)
+{
+    const int nvec = H / 8;
+    const int iter = iters_for(nvec, kCombineBS);
+    const bool full = nvec % (kCombineBS * iter) == 0;
+    const bool nt = tuning().nt_store;
+    void (*fn)(const u32x4 *, int64_t, int, int, const int32_t *, const float *, u32x4 *, int32_t *);
+    switch (K) {
+    case 2: fn = pick_iter<2>(iter, nt, full); break;
+    case 4: fn = pick_iter<4>(iter, nt, full); break;
+    case 6: fn = pick_iter<6>(iter, nt, full); break;
+    case 8: fn = pick_iter<8>(iter, nt, full); break;
+    default: fn = pick_iter<0>(iter, nt, full); break;
+    }
+    hipLaunchKernelGGL(fn, dim3(T), dim3(kCombineBS), 0, stream, (const u32x4 *)y, y_rows, nvec, K,
+                       slot, topk_w, (u32x4 *)out, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_fp8_dequant(const void *q, const float *scale, void *y, int64_t capacity, int H,
+                              const int32_t *nrows, hipStream_t stream)
+{
+    hipLaunchKernelGGL(fp8_dequant_kernel, dim3((unsigned)capacity), dim3(256), 0, stream,
+                       (const u32x4 *)q, scale, (u32x4 *)y, H / 16, nrows);
+    return hipGetLastError();
+}
+
+hipError_t launch_ref_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream)
+{
+    const int64_t n = bytes / 16;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(ref_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       (const u32x4 *)src, (u32x4 *)dst, n);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,261 @@
+// Dispatch on gfx950: scatter each source token's hidden row (bf16, or FP8
+// e4m3 with one fp32 scale per 1x128 block) plus its K weights and K indices
+// to every receive row the routing layout gave it.
+//
+// Design. One workgroup per source token. The workgroup reads the token's row
+// once into registers with 16-byte loads (each lane holds ITER vectors, so
+// the row is read exactly once from HBM), then writes those registers to each
+// destination row with 16-byte non-temporal stores: the traffic is one read
+// of x and R row writes, the minimum. This is the single-GPU form of the row
+// copy of "perf(ep): optimize IntraNode dispatch kernel for MI350X" (ROCm/mori
+// pull request 586): Technical Details 3 (a wave-wide vector copy whose
+// unroll must fit the hidden size — here ITER is chosen from H so the row is
+// covered in whole passes with no remainder loop) and 4 (the K weights and K
+// indices travel with each row, written by K lanes each). Destination slots
+// come from the layout's cached slots (Technical Details 1): a token reads K
+// (or G) integers instead of re-deriving its routing. Non-temporal stores and
+// 128-bit accesses follow "Optimized rocm specific multicast transpose kernel"
+// (ROCm/TransformerEngine pull request 586), Change Summary: CDNA4's L2
+// allocates on write, and rows written once should not evict useful lines.
+//
+// FP8: each lane holds 16 consecutive elements (two 16-byte loads); the 8
+// lanes of one 128-block reduce amax with three xor-shuffles; every lane then
+// forms scale = amax / 448 and inv = 448 / amax (IEEE fp32 divisions, as
+// compiled by default), multiplies, clamps to +-448 (which equals saturating
+// round-to-nearest-even for every finite input) and converts pairs with the
+// packed e4m3 conversion, giving one 16-byte store per lane per destination.
+// The quantisation runs once per source token, not once per destination.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <stdlib.h>
+
+namespace moe {
+
+namespace {
+
+constexpr int kDispatchBS = 128;   // threads per workgroup, bf16
+constexpr int kFp8BS = 64;         // threads per workgroup, fp8 (one wave)
+constexpr int kMaxIter = 8;
+
+template <int ITER, bool NT, bool NTL, bool FULL>
+__global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_kernel(
+    const u32x4 *__restrict__ x, int nvec, int K, int nslot, const int32_t *__restrict__ slots,
+    const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
+    u32x4 *__restrict__ recv_x, float *__restrict__ recv_w, int32_t *__restrict__ recv_idx)
+{
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const u32x4 *src = x + (size_t)t * nvec;
+    const int32_t *ts = slots + (size_t)t * nslot;
+
+    for (int base = 0; base < nvec; base += kDispatchBS * ITER) {
+        u32x4 v[ITER];
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int j = base + i * kDispatchBS + tid;
+            if (FULL || j < nvec) v[i] = load16<NTL>(src + j);
+        }
+        for (int d = 0; d < nslot; ++d) {
+            const int s = ts[d];
+            if (s < 0) continue;
+            u32x4 *dst = recv_x + (size_t)s * nvec;
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                const int j = base + i * kDispatchBS + tid;
+                if (FULL || j < nvec) store16<NT>(dst + j, v[i]);
+            }
+        }
+    }
+
+    // Metadata: lanes [0, K) carry the weights, lanes [K, 2K) the indices.
+    const bool wl = tid < K, il = tid >= K && tid < 2 * K;
+    float wv = 0.f;
+    int iv = 0;
+    if (wl) wv = topk_w[(size_t)t * K + tid];
+    if (il) iv = topk_idx[(size_t)t * K + tid - K];
+    for (int d = 0; d < nslot; ++d) {
+        const int s = ts[d];
+        if (s < 0) continue;
+        if (wl) recv_w[(size_t)s * K + tid] = wv;
+        if (il) recv_idx[(size_t)s * K + tid - K] = iv;
+    }
+}
+
+// Two packed e4m3 values into the low (HI = false) or high 16 bits of `old`.
+template <bool HI>
+__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
+{
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
+
+template <int ITER, bool NT, bool NTL, bool FULL>
+__global__ __launch_bounds__(kFp8BS) void dispatch_fp8_kernel(
+    const u32x4 *__restrict__ x, int nch, int K, int nslot, const int32_t *__restrict__ slots,
+    const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
+    u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, float *__restrict__ recv_w,
+    int32_t *__restrict__ recv_idx)
+{
+    // nch = H / 16 chunks of 16 elements; a row of x is 2 * nch vectors, a
+    // receive row nch vectors of 16 e4m3 bytes, and nch / 8 scales.
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const u32x4 *src = x + (size_t)t * nch * 2;
+    const int32_t *ts = slots + (size_t)t * nslot;
+    const int nblk = nch / 8;
+
+    for (int base = 0; base < nch; base += kFp8BS * ITER) {
+        u32x4 q[ITER];
+        float sc[ITER];
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int j = base + i * kFp8BS + tid;
+            const bool in = FULL || j < nch;
+            u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+            if (in) {
+                a = load16<NTL>(src + 2 * j);
+                b = load16<NTL>(src + 2 * j + 1);
+            }
+            float f[16];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f[2 * m] = bf16_lo(a[m]);
+                f[2 * m + 1] = bf16_hi(a[m]);
+                f[8 + 2 * m] = bf16_lo(b[m]);
+                f[8 + 2 * m + 1] = bf16_hi(b[m]);
+            }
+            float amax = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(f[m]));
+            // the 8 lanes of one 128-element block are lanes 8c .. 8c+7 of the wave
+            amax = fmaxf(amax, __shfl_xor(amax, 1));
+            amax = fmaxf(amax, __shfl_xor(amax, 2));
+            amax = fmaxf(amax, __shfl_xor(amax, 4));
+            const float scale = amax / 448.f;
+            const float inv = amax > 0.f ? 448.f / amax : 0.f;
+            int w[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                int p = cvt_pk_e4m3<false>(clamp448(f[4 * m] * inv), clamp448(f[4 * m + 1] * inv), 0);
+                p = cvt_pk_e4m3<true>(clamp448(f[4 * m + 2] * inv), clamp448(f[4 * m + 3] * inv), p);
+                w[m] = p;
+            }
+            q[i] = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+            sc[i] = scale;
+        }
+        for (int d = 0; d < nslot; ++d) {
+            const int s = ts[d];
+            if (s < 0) continue;
+            u32x4 *dst = recv_q + (size_t)s * nch;
+            float *dsc = recv_scale + (size_t)s * nblk;
+#pragma unroll
+            for (int i = 0; i < ITER; ++i) {
+                const int j = base + i * kFp8BS + tid;
+                if (FULL || j < nch) {
+                    store16<NT>(dst + j, q[i]);
+                    if ((tid & 7) == 0) dsc[j >> 3] = sc[i];
+                }
+            }
+        }
+    }
+
+    const bool wl = tid < K, il = tid >= K && tid < 2 * K;
+    float wv = 0.f;
+    int iv = 0;
+    if (wl) wv = topk_w[(size_t)t * K + tid];
+    if (il) iv = topk_idx[(size_t)t * K + tid - K];
+    for (int d = 0; d < nslot; ++d) {
+        const int s = ts[d];
+        if (s < 0) continue;
+        if (wl) recv_w[(size_t)s * K + tid] = wv;
+        if (il) recv_idx[(size_t)s * K + tid - K] = iv;
+    }
+}
+
+// Kernel instances by (ITER, NT store, NT load, FULL).
+template <int ITER, bool NT, bool NTL, bool FULL>
+struct Bf16Inst {
+    static constexpr auto fn = dispatch_bf16_kernel<ITER, NT, NTL, FULL>;
+};
+template <int ITER, bool NT, bool NTL, bool FULL>
+struct Fp8Inst {
+    static constexpr auto fn = dispatch_fp8_kernel<ITER, NT, NTL, FULL>;
+};
+
+template <template <int, bool, bool, bool> class Inst, int ITER>
+auto pick_flags(bool nt, bool ntl, bool full)
+{
+    if (nt) {
+        if (ntl) return full ? Inst<ITER, true, true, true>::fn : Inst<ITER, true, true, false>::fn;
+        return full ? Inst<ITER, true, false, true>::fn : Inst<ITER, true, false, false>::fn;
+    }
+    if (ntl) return full ? Inst<ITER, false, true, true>::fn : Inst<ITER, false, true, false>::fn;
+    return full ? Inst<ITER, false, false, true>::fn : Inst<ITER, false, false, false>::fn;
+}
+
+template <template <int, bool, bool, bool> class Inst>
+auto pick(int iter, bool nt, bool ntl, bool full)
+{
+    switch (iter) {
+    case 1: return pick_flags<Inst, 1>(nt, ntl, full);
+    case 2: return pick_flags<Inst, 2>(nt, ntl, full);
+    case 3: return pick_flags<Inst, 3>(nt, ntl, full);
+    case 4: return pick_flags<Inst, 4>(nt, ntl, full);
+    case 5: return pick_flags<Inst, 5>(nt, ntl, full);
+    case 6: return pick_flags<Inst, 6>(nt, ntl, full);
+    case 7: return pick_flags<Inst, 7>(nt, ntl, full);
+    default: return pick_flags<Inst, 8>(nt, ntl, full);
+    }
+}
+
+// Vectors per lane: the fewest whole passes of BS lanes that cover n vectors,
+// at most kMaxIter per pass (larger rows loop over passes).
+inline int iters_for(int n, int bs)
+{
+    const int it = (n + bs - 1) / bs;
+    return it < 1 ? 1 : (it > kMaxIter ? kMaxIter : it);
+}
+
+}  // namespace
+
+const Tuning &tuning()
+{
+    static const Tuning t = [] {
+        Tuning r;
+        if (const char *s = getenv("MOE_EP_NT_STORE")) r.nt_store = atoi(s) != 0;
+        if (const char *s = getenv("MOE_EP_NT_LOAD")) r.nt_load = atoi(s) != 0;
+        return r;
+    }();
+    return t;
+}
+
+hipError_t launch_dispatch_bf16(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
+                                const float *topk_w, const int32_t *topk_idx, void *recv_x,
+                                float *recv_w, int32_t *recv_idx, hipStream_t stream)
+{
+    const int nvec = H / 8;
+    const int iter = iters_for(nvec, kDispatchBS);
+    const bool full = nvec % (kDispatchBS * iter) == 0;
+    auto fn = pick<Bf16Inst>(iter, tuning().nt_store, tuning().nt_load, full);
+    hipLaunchKernelGGL(fn, dim3(T), dim3(kDispatchBS), 0, stream, (const u32x4 *)x, nvec, K, nslot,
+                       slots, topk_w, topk_idx, (u32x4 *)recv_x, recv_w, recv_idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
+                               const float *topk_w, const int32_t *topk_idx, void *recv_q,
+                               float *recv_scale, float *recv_w, int32_t *recv_idx,
+                               hipStream_t stream)
+{
+    const int nch = H / 16;
+    const int iter = iters_for(nch, kFp8BS);
+    const bool full = nch % (kFp8BS * iter) == 0;
+    auto fn = pick<Fp8Inst>(iter, tuning().nt_store, tuning().nt_load, full);
+    hipLaunchKernelGGL(fn, dim3(T), dim3(kFp8BS), 0, stream, (const u32x4 *)x, nch, K, nslot, slots,
+                       topk_w, topk_idx, (u32x4 *)recv_q, recv_scale, recv_w, recv_idx);
+    return hipGetLastError();
+}
+
+}  // namespace moe

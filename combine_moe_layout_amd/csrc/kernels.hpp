@@ -1,0 +1,53 @@
+// Host-side launchers of the gfx950 kernels. Arguments are already validated
+// by the C ABI (api.hip); each launcher only picks a kernel instance and
+// launches it on `stream`, returning the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Tokens per layout tile (= threads per layout workgroup).
+constexpr int kLayoutTile = 256;
+
+inline int layout_tiles(int T) { return (T + kLayoutTile - 1) / kLayoutTile; }
+
+struct LayoutPtrs {
+    int32_t *expert_count, *expert_offset, *group_count, *group_offset;
+    uint32_t *tok_group_mask;
+    int32_t *slot_e, *slot_g, *slot_tg, *recv_src_e, *recv_src_g, *status;
+};
+
+// Workspace: tile_cnt_e [E][tiles], tile_cnt_g [G][tiles], tile_err [tiles].
+hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L,
+                         int32_t *ws, hipStream_t stream);
+
+struct Tuning {
+    bool nt_store = true;   // non-temporal stores for receive rows / combine output
+    bool nt_load = false;   // non-temporal loads of source rows
+};
+const Tuning &tuning();
+
+// BF16 dispatch. slots: [T, nslot] (slot_e with nslot = K, or slot_tg with nslot = G).
+hipError_t launch_dispatch_bf16(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
+                                const float *topk_w, const int32_t *topk_idx, void *recv_x,
+                                float *recv_w, int32_t *recv_idx, hipStream_t stream);
+
+hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
+                               const float *topk_w, const int32_t *topk_idx, void *recv_q,
+                               float *recv_scale, float *recv_w, int32_t *recv_idx,
+                               hipStream_t stream);
+
+// Combine. slot: [T, K] (slot_e or slot_g).
+hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, const int32_t *slot,
+                          const float *topk_w, void *out, int32_t *status, hipStream_t stream);
+
+// FP8 identity expert; rows to convert = *nrows (device), grid covers `capacity` rows.
+hipError_t launch_fp8_dequant(const void *q, const float *scale, void *y, int64_t capacity, int H,
+                              const int32_t *nrows, hipStream_t stream);
+
+hipError_t launch_ref_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream);
+
+}  // namespace moe

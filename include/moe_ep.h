@@ -1,0 +1,194 @@
+/*
+ * moe_ep.h — C ABI of the MoE token path on one MI355X (gfx950):
+ * routing layout -> dispatch -> combine.
+ *
+ * The expert-parallel "ranks" of an EP group are expert groups inside one
+ * GPU's HBM: expert e belongs to group g = e / (E / G). Every call is
+ * asynchronous on the caller's HIP stream and is ordered only by that stream.
+ * The library allocates no device memory and keeps no state between calls:
+ * every array is owned by the caller (device memory unless stated), and the
+ * receive buffers are sized at the bounds given by moe_recv_rows_bound(), so no
+ * device-to-host synchronisation is needed anywhere on the path.
+ *
+ * Errors. Every entry point returns 0 (MOE_OK) or a negative moe_error code.
+ * All argument checks happen on the host before anything is launched; a call
+ * that returns an error has launched nothing. Problems found in the data
+ * itself (an expert index out of range, an expert repeated within a token, a
+ * combine slot beyond the rows supplied) set bits in the device word
+ * layout->status; entries found invalid are skipped, never read or written
+ * out of bounds. Read the status after synchronising the stream.
+ *
+ * T = 0 is valid: moe_layout() then only zeroes the counts, offsets and
+ * status (the per-token arrays may be NULL), and the other calls do nothing.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_EP_ABI_VERSION 1
+
+/* Limits checked at the boundary. */
+#define MOE_MAX_EXPERTS 1024 /* E */
+#define MOE_MAX_GROUPS 32    /* G: a token's groups form one 32-bit mask */
+#define MOE_MAX_TOPK 32      /* K */
+
+enum moe_error {
+    MOE_OK = 0,
+    MOE_ERR_NULL_PTR = -1,   /* a required pointer is NULL */
+    MOE_ERR_BAD_SHAPE = -2,  /* T, K, E, G or H outside the supported range */
+    MOE_ERR_MISALIGNED = -3, /* a row buffer is not 16-byte aligned */
+    MOE_ERR_CAPACITY = -4,   /* a receive buffer is smaller than its bound */
+    MOE_ERR_WORKSPACE = -5,  /* workspace missing or too small */
+    MOE_ERR_HIP = -6,        /* a HIP runtime call or launch failed */
+    MOE_ERR_BAD_MODE = -7    /* unknown mode or dtype */
+};
+
+/* Bits of layout->status (device int32). */
+#define MOE_STATUS_BAD_INDEX 1 /* some topk_idx entry outside [0, E) */
+#define MOE_STATUS_DUPLICATE 2 /* some token lists one expert twice */
+#define MOE_STATUS_Y_ROWS 4    /* combine met a slot >= the rows of y */
+
+/* Receive-buffer layouts.
+ * EXPERT: one row per valid (token, k) pair, rows ordered by expert, then
+ *         token, then k; expert e owns rows [expert_offset[e], expert_offset[e+1]).
+ * GROUP:  one row per (token, group) the token reaches — a token routed to
+ *         several experts of one group is sent to it once — ordered by group,
+ *         then token; group g owns rows [group_offset[g], group_offset[g+1]).
+ * Source: "perf(ep): optimize IntraNode dispatch kernel for MI350X" (ROCm/mori
+ * pull request 586), Motivation (per-destination deduplication, destination =
+ * expert / experts-per-rank); "Optimizing Distributed Inference Kernels for AMD
+ * DEVELOPER CHALLENGE 2025", section 3.1 (per-local-expert receive buffers). */
+enum moe_mode { MOE_MODE_EXPERT = 0, MOE_MODE_GROUP = 1 };
+
+/* Element type of the dispatched rows.
+ * BF16: rows are bitwise copies of x.
+ * FP8_E4M3_B128: rows are OCP e4m3fn bytes with one fp32 scale per 1x128
+ * block: amax = max |x| over the block, scale = amax / 448,
+ * q = e4m3fn_rne_satfinite(x * (448 / amax)) (q = 0 when amax = 0).
+ * Source: "Optimized rocm specific multicast transpose kernel"
+ * (ROCm/TransformerEngine pull request 586), Change Summary (fused amax,
+ * packed FP8 conversion). */
+enum moe_dtype { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3_B128 = 1 };
+
+/* The routing layout: a plain struct of dimensions and caller-owned device
+ * pointers. moe_layout() fills the arrays; moe_dispatch() and moe_combine()
+ * read them (the cached destination slots of "Cached routing", mori pull
+ * request 586, Technical Details 1). The struct itself is read on the host at
+ * each call and may live on the stack.
+ *
+ * Array                 elements               meaning
+ * expert_count          E                      valid pairs routed to expert e
+ * expert_offset         E + 1                  exclusive prefix; [E] = rows in EXPERT mode
+ * group_count           G                      tokens that reach group g
+ * group_offset          G + 1                  exclusive prefix; [G] = rows in GROUP mode
+ * tok_group_mask        T   (uint32)           bit g set iff token t reaches group g
+ * slot_e                T*K                    EXPERT row of pair (t, k), -1 if invalid
+ * slot_g                T*K                    GROUP row of pair (t, k), -1 if invalid
+ * slot_tg               T*G                    GROUP row of (t, g), -1 if t misses g
+ * recv_src_e            T*K                    pair id t*K + k of EXPERT row r
+ * recv_src_g            T*min(K, G)            token id of GROUP row r
+ * status                1                      MOE_STATUS_* bits of the last layout/combine
+ *
+ * recv_src_e / recv_src_g hold valid data in their first expert_offset[E] /
+ * group_offset[G] entries; the rest is left untouched. */
+typedef struct moe_layout_t {
+    int32_t T, K, E, G;
+    int32_t *expert_count, *expert_offset;
+    int32_t *group_count, *group_offset;
+    uint32_t *tok_group_mask;
+    int32_t *slot_e, *slot_g, *slot_tg;
+    int32_t *recv_src_e, *recv_src_g;
+    int32_t *status;
+} moe_layout_t;
+
+/* Bytes of device workspace moe_layout() needs for these sizes (written to
+ * *bytes). The workspace holds per-tile expert and group counts and per-tile
+ * error bits; its contents need no initialisation and are dead after the call.
+ * Returns MOE_ERR_BAD_SHAPE for sizes outside the limits. */
+int moe_layout_workspace_bytes(int T, int K, int E, int G, size_t *bytes);
+
+/* Rows a receive buffer must hold for moe_dispatch() in `mode`: T*K for
+ * EXPERT (exact when all entries are valid), T*min(K, G) for GROUP (an upper
+ * bound on the deduplicated pairs). Returns a negative moe_error on bad input. */
+int64_t moe_recv_rows_bound(int T, int K, int G, int mode);
+
+/* Routing layout of topk_idx (device int32 [T, K], row-major) into L's arrays.
+ * Stable order: inside every expert (group) segment rows are in ascending
+ * token order, and ascending k within a token. An entry is valid iff it is in
+ * [0, E) and does not repeat an earlier entry of the same token; invalid
+ * entries get slot -1, are not counted, and set status bits.
+ * Requires 1 <= K <= MOE_MAX_TOPK, K <= E <= MOE_MAX_EXPERTS,
+ * 1 <= G <= MOE_MAX_GROUPS, E % G == 0, T >= 0, T * max(K, G) < 2^30.
+ * ws: device workspace of at least moe_layout_workspace_bytes() bytes.
+ * stream: a hipStream_t (NULL = the null stream).
+ * Source: mori pull request 586, Motivation and Technical Details 1; the
+ * separate routing launch is the one its profiling section proposes. */
+int moe_layout(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t ws_bytes,
+               void *stream);
+
+/* Dispatch: for every source token t and each of its destination rows r
+ * (slot_e[t, k] for valid k in EXPERT mode; slot_tg[t, g] >= 0 in GROUP mode):
+ *   recv_x[r, :]        = x[t, :]               (BF16: bitwise copy)
+ *                         or e4m3 bytes of x[t, :] with recv_scale[r, :] (FP8)
+ *   recv_topk_w[r, :]   = topk_w[t, :]          (all K weights)
+ *   recv_topk_idx[r, :] = topk_idx[t, :]        (all K indices, as given)
+ * Rows beyond the layout's row count are not written.
+ * x:          device bf16 [T, H] (raw 16-bit), 16-byte aligned, H % 8 == 0.
+ * topk_w:     device fp32 [T, K]; topk_idx: the int32 [T, K] given to moe_layout.
+ * recv_x:     device [recv_capacity, H] bf16 (BF16) or uint8 (FP8), 16-byte aligned.
+ * recv_scale: device fp32 [recv_capacity, H / 128] (FP8 only; NULL for BF16).
+ * recv_topk_w / recv_topk_idx: device [recv_capacity, K].
+ * recv_capacity >= moe_recv_rows_bound(T, K, G, mode), else MOE_ERR_CAPACITY.
+ * FP8 needs H % 128 == 0. L must hold the layout of topk_idx.
+ * Source: mori pull request 586, Technical Details 3 (wave-wide row copy) and
+ * 4 (vectorised metadata copies); the challenge write-up, section 3.1. */
+int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *x,
+                 const float *topk_w, const int32_t *topk_idx, void *recv_x, float *recv_scale,
+                 float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
+                 void *stream);
+
+/* Combine: out[t, i] = bf16_rne( acc ), where acc starts at -0 and, for
+ * k = 0 .. K-1 in order with slot(t, k) >= 0,
+ *   acc = fmaf(topk_w[t, k], y[slot(t, k), i], acc)        (fp32)
+ * slot = slot_e (EXPERT) or slot_g (GROUP; a row shared by several k is
+ * weighted once per k). Slots >= y_rows are skipped and set MOE_STATUS_Y_ROWS.
+ * y:   device bf16 [y_rows, H], 16-byte aligned (the expert outputs, in the
+ *      receive layout of `mode`).
+ * out: device bf16 [T, H], 16-byte aligned; must not overlap y.
+ * Source: mori pull request 586, "Remaining gap — profiled root cause" (combine
+ * gathers the expert rows and accumulates with FMAs); ROCm/vllm pull request
+ * 1297, Accuracy (fp32 accumulation, one rounding on the store). */
+int moe_combine(const moe_layout_t *L, int mode, int H, const void *y, int64_t y_rows,
+                const float *topk_w, void *out, void *stream);
+
+/* Identity expert for FP8 rows (glue between dispatch and combine, not part
+ * of the timed path): y[r, i] = bf16_rne(e4m3_decode(q[r, i]) * scale[r, i / 128])
+ * for r < the layout's row count in `mode` (read on the device); rows beyond
+ * it are not written. q: device uint8 [capacity, H]; scale: fp32
+ * [capacity, H / 128]; y: bf16 [capacity, H]. H % 128 == 0. */
+int moe_fp8_dequant(const moe_layout_t *L, int mode, int H, const void *q, const float *scale,
+                    void *y, int64_t capacity, void *stream);
+
+/* Measurement aid, not part of the method: a plain 16-byte-vector streaming
+ * copy of `bytes` bytes (bytes % 16 == 0, both pointers 16-byte aligned). It
+ * calibrates hardware traffic counters and gives a measured copy ceiling. */
+int moe_ref_copy(void *dst, const void *src, int64_t bytes, void *stream);
+
+/* Text for a moe_error code (static storage). For MOE_ERR_HIP the text of the
+ * last HIP error seen by this library on the calling thread is appended. */
+const char *moe_status_string(int code);
+
+/* MOE_EP_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

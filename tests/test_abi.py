@@ -1,0 +1,137 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call (so these
+run without a GPU). No compute is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    from combine_moe_layout_amd import build
+    if build.is_stale():
+        build.build()
+    import combine_moe_layout_amd as m
+    return m
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe_ep.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_[a-z0-9_]+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_three_calls():
+    names = header_functions()
+    for n in ("moe_layout", "moe_dispatch", "moe_combine", "moe_layout_workspace_bytes",
+              "moe_recv_rows_bound", "moe_status_string"):
+        assert n in names
+    assert len(names) >= 9
+
+
+def test_library_exports_every_declared_symbol(moe):
+    lib = ctypes.CDLL(moe.library_path())
+    missing = [n for n in header_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert moe._lib.moe_abi_version() == 1
+
+
+def test_query_functions(moe):
+    assert moe.recv_rows_bound(4096, 8, 8, "expert") == 32768
+    assert moe.recv_rows_bound(4096, 8, 8, "group") == 32768
+    assert moe.recv_rows_bound(16, 2, 8, "group") == 32
+    assert moe.recv_rows_bound(100, 8, 4, "group") == 400
+    assert moe.recv_rows_bound(0, 8, 4, "expert") == 0
+    assert moe.layout_workspace_bytes(4096, 8, 256, 8) >= 4 * (256 + 8 + 1) * 16
+    assert moe.layout_workspace_bytes(0, 8, 256, 8) == 0
+    with pytest.raises(moe.MoeError):
+        moe.layout_workspace_bytes(16, 8, 255, 8)       # E % G != 0
+    with pytest.raises(moe.MoeError):
+        moe.layout_workspace_bytes(16, 33, 256, 8)      # K > 32
+    with pytest.raises(moe.MoeError):
+        moe.layout_workspace_bytes(16, 8, 2048, 8)      # E > 1024
+    with pytest.raises(moe.MoeError):
+        moe.layout_workspace_bytes(16, 8, 256, 64)      # G > 32
+    with pytest.raises(moe.MoeError):
+        moe.layout_workspace_bytes(1 << 27, 8, 256, 8)  # T * K >= 2^30
+    with pytest.raises(moe.MoeError):
+        moe.recv_rows_bound(16, 2, 8, 5)
+
+
+def _fake_layout(moe, T=16, K=2, E=8, G=8, null=None):
+    """A moe_layout_t whose pointers are fake but aligned non-NULL addresses: the
+    calls below must return before dereferencing or launching anything."""
+    addr = 1 << 20
+    vals = {}
+    for n in ("expert_count", "expert_offset", "group_count", "group_offset", "tok_group_mask",
+              "slot_e", "slot_g", "slot_tg", "recv_src_e", "recv_src_g", "status"):
+        vals[n] = None if n == null else addr
+        addr += 1 << 16
+    return moe._LayoutT(T, K, E, G, *vals.values())
+
+
+def test_host_validation_errors(moe):
+    lib = moe._lib
+    P = ctypes.c_void_p
+    A = P(1 << 24)          # aligned fake device address (never dereferenced)
+    M = P((1 << 24) + 2)    # misaligned
+    NULL = None
+    L = _fake_layout(moe)
+    ref = ctypes.byref
+    # layout
+    assert lib.moe_layout(A, ref(_fake_layout(moe, null="slot_e")), A, 1 << 20, NULL) == -1
+    assert lib.moe_layout(A, ref(_fake_layout(moe, E=9)), A, 1 << 20, NULL) == -2
+    assert lib.moe_layout(A, ref(_fake_layout(moe, K=0)), A, 1 << 20, NULL) == -2
+    assert lib.moe_layout(A, ref(_fake_layout(moe, T=-1)), A, 1 << 20, NULL) == -2
+    assert lib.moe_layout(A, ref(L), A, 0, NULL) == -5
+    assert lib.moe_layout(A, ref(L), NULL, 1 << 20, NULL) == -5
+    assert lib.moe_layout(NULL, ref(L), A, 1 << 20, NULL) == -1
+    assert lib.moe_layout(M, ref(L), A, 1 << 20, NULL) == -3
+    # dispatch: mode, dtype, H, capacity, alignment, null
+    d = lambda mode=0, dt=0, H=2048, x=A, rx=A, sc=NULL, cap=32, Lp=L: lib.moe_dispatch(
+        ref(Lp), mode, dt, H, x, A, A, rx, sc, A, A, cap, NULL)
+    assert d() != -7
+    assert d(mode=2) == -7
+    assert d(dt=3) == -7
+    assert d(H=2047) == -2
+    assert d(H=0) == -2
+    assert d(dt=1, H=1000, sc=A) == -2        # FP8 needs H % 128 == 0
+    assert d(dt=1, H=1024, sc=NULL) == -1      # FP8 needs scales
+    assert d(cap=31) == -4                      # EXPERT bound is T*K = 32
+    assert d(mode=1, cap=31) == -4              # GROUP bound is T*min(K,G) = 32
+    assert d(x=M) == -3 and d(rx=M) == -3
+    assert d(x=NULL) == -1
+    assert d(Lp=_fake_layout(moe, T=0), x=NULL) == 0
+    # combine
+    c = lambda mode=0, H=2048, y=A, rows=32, out=A, Lp=L: lib.moe_combine(
+        ref(Lp), mode, H, y, rows, A, out, NULL)
+    assert c(mode=3) == -7
+    assert c(H=12) == -2
+    assert c(rows=-1) == -2
+    assert c(y=M) == -3 and c(out=M) == -3
+    assert c(y=NULL) == -1
+    assert c(Lp=_fake_layout(moe, null="status")) == -1
+    assert c(Lp=_fake_layout(moe, T=0), y=NULL) == 0
+    # dequant and copy
+    assert lib.moe_fp8_dequant(ref(L), 0, 1000, A, A, A, 32, NULL) == -2
+    assert lib.moe_fp8_dequant(ref(L), 0, 1024, M, A, A, 32, NULL) == -3
+    assert lib.moe_ref_copy(A, A, 15, NULL) == -2
+    assert lib.moe_ref_copy(A, M, 16, NULL) == -3
+    assert lib.moe_ref_copy(A, A, 0, NULL) == 0
+    for code in range(-7, 1):
+        assert lib.moe_status_string(code)
+
+
+def test_package_has_no_cpu_fallback():
+    """The binding must not route through the oracle or any CPU path."""
+    pkg = os.path.join(ROOT, "combine_moe_layout_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert "import oracle" not in src and "from oracle" not in src, fn

@@ -1,0 +1,421 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element
+by element, on the same seeded inputs.
+
+Bar: layout arrays, dispatched rows, metadata, FP8 bytes and scales are
+bit-exact; combine is held to <= 1 bf16 ulp and its count of non-identical
+elements is asserted to be 0 (both sides run the same fp32 fma chain).
+Shapes: every named workload at full size (the sizes bench.py times), small
+shapes spanning several layout tiles with ragged tails, and edge cases
+(T = 0 / 1, K = 1 / 32, G = 1 / E, ragged and multi-pass H, invalid entries).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["tiny", "t256", "t4096", "skew", "fp8"]
+MODES = ["expert", "group"]
+CANARY16 = np.uint16(0xBEEF)
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import combine_moe_layout_amd as m
+    return m
+
+
+@pytest.fixture(scope="module")
+def orc():
+    import oracle
+    return oracle
+
+
+def dev_bf16(x_u16):
+    return torch.from_numpy(np.ascontiguousarray(x_u16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+_cache = {}
+
+
+def workload(name):
+    if name not in _cache:
+        _cache[name] = si.make_workload(name)
+    return _cache[name]
+
+
+LAYOUT_ARRAYS = ("expert_count", "expert_offset", "group_count", "group_offset", "slot_e",
+                 "slot_g", "slot_tg")
+
+
+def check_layout(L, Lo):
+    torch.cuda.synchronize()
+    assert int(L.status.item()) == Lo["status"]
+    for n in LAYOUT_ARRAYS:
+        np.testing.assert_array_equal(getattr(L, n).cpu().numpy(), Lo[n], err_msg=n)
+    np.testing.assert_array_equal(L.tok_group_mask.cpu().numpy().view(np.uint32),
+                                  Lo["tok_group_mask"])
+    np.testing.assert_array_equal(L.recv_src_e[:Lo["R_expert"]].cpu().numpy(),
+                                  Lo["recv_src_e"][:Lo["R_expert"]])
+    np.testing.assert_array_equal(L.recv_src_g[:Lo["R_group"]].cpu().numpy(),
+                                  Lo["recv_src_g"][:Lo["R_group"]])
+
+
+def ulp_diff_bf16(a_u16, b_u16):
+    """Distance in bf16 ulps between two bf16 bit arrays (monotone integer map)."""
+    def key(u):
+        u = u.astype(np.int32)
+        return np.where(u & 0x8000, 0x8000 - (u & 0x7FFF), 0x8000 + (u & 0x7FFF))
+    return np.abs(key(a_u16) - key(b_u16))
+
+
+def assert_combine_equal(got_u16, ref_u16):
+    d = ulp_diff_bf16(got_u16, ref_u16)
+    assert d.max(initial=0) <= 1, f"max ulp diff {d.max()}"
+    assert int((got_u16 != ref_u16).sum()) == 0, f"{int((d > 0).sum())} elements differ by 1 ulp"
+
+
+# ------------------------------------------------------------------ layout
+
+@pytest.mark.parametrize("name", FULL)
+def test_layout_full_workloads(moe, orc, name):
+    d = workload(name)
+    wl = d["workload"]
+    L = moe.moe_layout(to_dev(d["topk_idx"]), wl.E, wl.G)
+    check_layout(L, orc.layout(d["topk_idx"], wl.E, wl.G))
+
+
+EDGE_SHAPES = [
+    (0, 8, 256, 8), (1, 8, 256, 8), (1, 1, 1, 1), (255, 8, 256, 8), (256, 8, 256, 8),
+    (257, 8, 256, 8), (1000, 1, 7, 7), (777, 32, 64, 32), (513, 6, 1024, 32), (4097, 8, 256, 1),
+    (300, 2, 8, 8), (2000, 3, 12, 4), (1025, 8, 1000, 8), (600, 16, 16, 16),
+]
+
+
+@pytest.mark.parametrize("T,K,E,G", EDGE_SHAPES)
+def test_layout_edge_shapes(moe, orc, T, K, E, G):
+    idx = si.make_inputs(T, 8, E, K, seed=1000 + T + K + E)["topk_idx"]
+    L = moe.moe_layout(to_dev(idx), E, G)
+    check_layout(L, orc.layout(idx, E, G))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_layout_invalid_entries(moe, orc, seed):
+    rng = np.random.default_rng(seed)
+    T, K, E, G = int(rng.integers(200, 900)), int(rng.integers(2, 9)), 64, 8
+    idx = rng.integers(0, E, size=(T, K)).astype(np.int32)           # repeats likely
+    bad = rng.random((T, K)) < 0.05
+    idx[bad] = rng.choice([-1, -7, E, E + 5, 1 << 30], size=int(bad.sum()))
+    L = moe.moe_layout(to_dev(idx), E, G)
+    Lo = orc.layout(idx, E, G)
+    assert Lo["status"] == 3
+    check_layout(L, Lo)
+
+
+def test_layout_reuses_buffers_without_stale_state(moe, orc):
+    """A layout written into buffers that hold an earlier, different layout equals a
+    fresh one (the stale-map hazard of cached routing)."""
+    a = si.make_inputs(1500, 8, 256, 8, seed=41)["topk_idx"]
+    b = si.make_inputs(1500, 8, 256, 8, seed=42)["topk_idx"]
+    b[:7, 3] = 999                                                    # invalid entries in b
+    L = moe.moe_layout(to_dev(a), 256, 8)
+    L = moe.moe_layout(to_dev(b), 256, 8, out=L)
+    check_layout(L, orc.layout(b, 256, 8))
+    L = moe.moe_layout(to_dev(a), 256, 8, out=L)
+    check_layout(L, orc.layout(a, 256, 8))                           # status cleared again
+
+
+# ------------------------------------------------------------------ dispatch
+
+def dispatch_with_canary(moe, L, x, w, idx, mode, dtype="bf16"):
+    H = x.shape[1]
+    D = moe.alloc_dispatch(L, H, mode, dtype, device="cuda")
+    if dtype == "bf16":
+        D.recv_x.view(torch.int16).fill_(int(CANARY16.astype(np.int16)))
+    else:
+        D.recv_x.fill_(0xA5)
+        D.recv_scale.fill_(-1.5)
+    D.recv_topk_w.fill_(-3.0)
+    D.recv_topk_idx.fill_(-77)
+    return moe.moe_dispatch(L, x, w, idx, mode, dtype, out=D)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", FULL)
+def test_dispatch_bf16_full_workloads(moe, orc, name, mode):
+    d = workload(name)
+    wl = d["workload"]
+    idx_d = to_dev(d["topk_idx"])
+    L = moe.moe_layout(idx_d, wl.E, wl.G)
+    D = dispatch_with_canary(moe, L, dev_bf16(d["x"]), to_dev(d["topk_w"]), idx_d, mode)
+    Lo = orc.layout(d["topk_idx"], wl.E, wl.G)
+    Do = orc.dispatch_bf16(Lo, mode, d["x"], d["topk_w"], d["topk_idx"])
+    R = Do["R"]
+    got = host_u16(D.recv_x)
+    np.testing.assert_array_equal(got[:R], Do["recv_x"])
+    assert np.all(got[R:] == CANARY16)
+    w_got = D.recv_topk_w.cpu().numpy()
+    np.testing.assert_array_equal(w_got[:R].view(np.uint32), Do["recv_w"].view(np.uint32))
+    assert np.all(w_got[R:] == -3.0)
+    i_got = D.recv_topk_idx.cpu().numpy()
+    np.testing.assert_array_equal(i_got[:R], Do["recv_idx"])
+    assert np.all(i_got[R:] == -77)
+
+
+DISPATCH_EDGE = [  # (T, H, E, G, K): ragged / multi-pass hidden sizes, one group, one expert per group
+    (1, 8, 8, 8, 2), (3, 520, 16, 4, 3), (129, 1024, 32, 8, 4), (40, 16392, 64, 8, 8),
+    (300, 4096, 128, 1, 8), (77, 2048, 8, 8, 2), (513, 7168, 256, 8, 8), (50, 8200, 16, 16, 16),
+]
+
+
+@pytest.mark.parametrize("T,H,E,G,K", DISPATCH_EDGE)
+@pytest.mark.parametrize("mode", MODES)
+def test_dispatch_bf16_edge_shapes(moe, orc, T, H, E, G, K, mode):
+    d = si.make_inputs(T, H, E, K, seed=T + H + K)
+    idx_d = to_dev(d["topk_idx"])
+    L = moe.moe_layout(idx_d, E, G)
+    D = dispatch_with_canary(moe, L, dev_bf16(d["x"]), to_dev(d["topk_w"]), idx_d, mode)
+    Lo = orc.layout(d["topk_idx"], E, G)
+    Do = orc.dispatch_bf16(Lo, mode, d["x"], d["topk_w"], d["topk_idx"])
+    got = host_u16(D.recv_x)
+    np.testing.assert_array_equal(got[:Do["R"]], Do["recv_x"])
+    assert np.all(got[Do["R"]:] == CANARY16)
+    np.testing.assert_array_equal(D.recv_topk_idx.cpu().numpy()[:Do["R"]], Do["recv_idx"])
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_dispatch_with_invalid_entries(moe, orc, mode):
+    rng = np.random.default_rng(9)
+    T, H, E, G, K = 333, 1024, 32, 4, 6
+    d = si.make_inputs(T, H, E, K, seed=9)
+    idx = d["topk_idx"].copy()
+    idx[rng.random((T, K)) < 0.04] = 40          # out of range
+    idx[5, 1] = idx[5, 0]                        # repeat
+    idx_d = to_dev(idx)
+    L = moe.moe_layout(idx_d, E, G)
+    D = dispatch_with_canary(moe, L, dev_bf16(d["x"]), to_dev(d["topk_w"]), idx_d, mode)
+    Lo = orc.layout(idx, E, G)
+    Do = orc.dispatch_bf16(Lo, mode, d["x"], d["topk_w"], idx)
+    got = host_u16(D.recv_x)
+    np.testing.assert_array_equal(got[:Do["R"]], Do["recv_x"])
+    assert np.all(got[Do["R"]:] == CANARY16)
+    np.testing.assert_array_equal(D.recv_topk_idx.cpu().numpy()[:Do["R"]], Do["recv_idx"])
+    assert int(L.status.item()) == 3
+
+
+def fp8_check(D, Do):
+    R = Do["R"]
+    q = D.recv_x.cpu().numpy()
+    np.testing.assert_array_equal(q[:R], Do["recv_q"])
+    assert np.all(q[R:] == 0xA5)
+    s = D.recv_scale.cpu().numpy()
+    np.testing.assert_array_equal(s[:R].view(np.uint32), Do["recv_scale"].view(np.uint32))
+    assert np.all(s[R:] == -1.5)
+    np.testing.assert_array_equal(D.recv_topk_w.cpu().numpy()[:R].view(np.uint32),
+                                  Do["recv_w"].view(np.uint32))
+    np.testing.assert_array_equal(D.recv_topk_idx.cpu().numpy()[:R], Do["recv_idx"])
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", ["fp8", "t256", "skew", "tiny"])
+def test_dispatch_fp8_full_workloads(moe, orc, name, mode):
+    d = workload(name)
+    wl = d["workload"]
+    idx_d = to_dev(d["topk_idx"])
+    L = moe.moe_layout(idx_d, wl.E, wl.G)
+    D = dispatch_with_canary(moe, L, dev_bf16(d["x"]), to_dev(d["topk_w"]), idx_d, mode, "fp8")
+    Lo = orc.layout(d["topk_idx"], wl.E, wl.G)
+    fp8_check(D, orc.dispatch_fp8(Lo, mode, d["x"], d["topk_w"], d["topk_idx"]))
+
+
+def adversarial_rows(T, H, seed):
+    """bf16 rows whose 128-blocks stress the conversion: amax exactly 448 (scale 1,
+    codes = RNE of the inputs), e4m3 midpoints, subnormal codes, signed zeros,
+    all-zero blocks, huge and tiny magnitudes, bf16 subnormals next to normals."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((T, H)) * rng.choice([1e-3, 1, 30, 1e4], size=(T, 1))).astype(np.float32)
+    codes = np.array([oracle.e4m3_to_f32(c) for c in range(127)], np.float64)
+    mids = ((codes[:-1] + codes[1:]) / 2).astype(np.float32)
+    nb = H // 128
+    for t in range(T):
+        for b in range(nb):
+            kind = (t * nb + b) % 6
+            blk = x[t, b * 128:(b + 1) * 128]
+            if kind == 0:          # amax 448, midpoints and codes themselves
+                blk[:] = rng.choice(np.concatenate([mids, -mids, codes.astype(np.float32)]), 128)
+                blk[rng.integers(128)] = 448.0 * rng.choice([-1, 1])
+            elif kind == 1:        # zeros of both signs, one block all zero
+                blk[:] = 0.0 if t % 2 else -0.0
+            elif kind == 2:        # one large element, the rest land on subnormal e4m3 codes
+                blk[:] = rng.standard_normal(128) * 0.3
+                blk[rng.integers(128)] = 3.0e4
+            elif kind == 3:        # bf16 subnormals next to a unit element
+                blk[:] = rng.standard_normal(128).astype(np.float32) * np.float32(1e-39)
+                blk[0] = 1.0
+            elif kind == 4:        # huge magnitudes
+                blk[:] = rng.standard_normal(128) * 1e30
+    import torch as _t
+    return _t.from_numpy(x).to(_t.bfloat16).view(_t.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("T,H,E,G,K", [(96, 1024, 16, 4, 4), (50, 8320, 32, 8, 8), (7, 128, 8, 8, 2)])
+def test_dispatch_fp8_adversarial_blocks(moe, orc, mode, T, H, E, G, K):
+    d = si.make_inputs(T, 8, E, K, seed=T + H)
+    x = adversarial_rows(T, H, seed=H)
+    idx_d = to_dev(d["topk_idx"])
+    L = moe.moe_layout(idx_d, E, G)
+    D = dispatch_with_canary(moe, L, dev_bf16(x), to_dev(d["topk_w"]), idx_d, mode, "fp8")
+    Lo = orc.layout(d["topk_idx"], E, G)
+    fp8_check(D, orc.dispatch_fp8(Lo, mode, x, d["topk_w"], d["topk_idx"]))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_fp8_dequant_matches_oracle(moe, orc, mode):
+    d = workload("fp8") if mode == "expert" else workload("t256")
+    wl = d["workload"]
+    idx_d = to_dev(d["topk_idx"])
+    L = moe.moe_layout(idx_d, wl.E, wl.G)
+    D = moe.moe_dispatch(L, dev_bf16(d["x"]), to_dev(d["topk_w"]), idx_d, mode, "fp8")
+    y = torch.full((D.recv_x.shape[0], wl.H), 7.0, dtype=torch.bfloat16, device="cuda")
+    moe.moe_fp8_dequant(L, D.recv_x, D.recv_scale, mode, out=y)
+    Lo = orc.layout(d["topk_idx"], wl.E, wl.G)
+    Do = orc.dispatch_fp8(Lo, mode, d["x"], d["topk_w"], d["topk_idx"])
+    yo = orc.dequant_fp8(Do["recv_q"], Do["recv_scale"])
+    got = host_u16(y)
+    np.testing.assert_array_equal(got[:Do["R"]], yo)
+    assert np.all(got[Do["R"]:] == host_u16(torch.tensor([7.0], dtype=torch.bfloat16))[0])
+
+
+# ------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", FULL)
+def test_combine_full_workloads(moe, orc, name, mode):
+    """Expert outputs y: the dispatched rows (identity) for bf16 workloads, the
+    dequantised FP8 rows for the FP8 workload, each compared with the oracle's
+    fma chain; plus a non-identity y (random rows) to exercise every slot."""
+    d = workload(name)
+    wl = d["workload"]
+    idx_d, w_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"])
+    L = moe.moe_layout(idx_d, wl.E, wl.G)
+    Lo = orc.layout(d["topk_idx"], wl.E, wl.G)
+    if wl.fp8:
+        D = moe.moe_dispatch(L, dev_bf16(d["x"]), w_d, idx_d, mode, "fp8")
+        y = moe.moe_fp8_dequant(L, D.recv_x, D.recv_scale, mode)
+        Do = orc.dispatch_fp8(Lo, mode, d["x"], d["topk_w"], d["topk_idx"])
+        y_ref = orc.dequant_fp8(Do["recv_q"], Do["recv_scale"])
+    else:
+        D = moe.moe_dispatch(L, dev_bf16(d["x"]), w_d, idx_d, mode)
+        y = D.recv_x
+        y_ref = orc.dispatch_bf16(Lo, mode, d["x"], d["topk_w"], d["topk_idx"])["recv_x"]
+    out = moe.moe_combine(L, y, w_d, mode)
+    ref = orc.combine(Lo, mode, y_ref, d["topk_w"])
+    got = host_u16(out)
+    assert_combine_equal(got, ref)
+    if not wl.fp8:
+        np.testing.assert_array_equal(got, d["x"])           # identity round trip
+    # random expert outputs (every receive row different from its source)
+    rng = np.random.default_rng(wl.seed)
+    R = y_ref.shape[0]
+    yr = torch.from_numpy(rng.standard_normal((R, wl.H), dtype=np.float32)).to(torch.bfloat16)
+    yr_u16 = yr.view(torch.int16).numpy().view(np.uint16)
+    out = moe.moe_combine(L, dev_bf16(yr_u16), w_d, mode)
+    assert_combine_equal(host_u16(out), orc.combine(Lo, mode, yr_u16, d["topk_w"]))
+
+
+COMBINE_EDGE = [(1, 8, 8, 8, 2), (3, 520, 16, 4, 3), (200, 1024, 32, 8, 5), (40, 16392, 64, 8, 8),
+                (300, 4096, 128, 1, 8), (100, 2048, 64, 32, 32), (77, 7168, 256, 8, 4),
+                (90, 3072, 96, 4, 6)]
+
+
+@pytest.mark.parametrize("T,H,E,G,K", COMBINE_EDGE)
+@pytest.mark.parametrize("mode", MODES)
+def test_combine_edge_shapes(moe, orc, T, H, E, G, K, mode):
+    d = si.make_inputs(T, H, E, K, seed=5 * T + H)
+    idx_d, w_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"])
+    L = moe.moe_layout(idx_d, E, G)
+    Lo = orc.layout(d["topk_idx"], E, G)
+    R = Lo["R_expert"] if mode == "expert" else Lo["R_group"]
+    rng = np.random.default_rng(T)
+    w = (rng.standard_normal((T, K)) * 2).astype(np.float32)        # any weights, any sign
+    y = torch.from_numpy(rng.standard_normal((R, H), dtype=np.float32)).to(torch.bfloat16)
+    y_u16 = y.view(torch.int16).numpy().view(np.uint16)
+    out = moe.moe_combine(L, dev_bf16(y_u16), to_dev(w), mode)
+    assert_combine_equal(host_u16(out), orc.combine(Lo, mode, y_u16, w))
+
+
+def test_combine_skips_invalid_and_short_y(moe, orc):
+    T, H, E, G, K = 150, 1024, 32, 4, 8
+    d = si.make_inputs(T, H, E, K, seed=3)
+    idx = d["topk_idx"].copy()
+    idx[::7, 2] = -1
+    idx[3, 5] = idx[3, 4]
+    idx_d, w_d = to_dev(idx), to_dev(d["topk_w"])
+    L = moe.moe_layout(idx_d, E, G)
+    Lo = orc.layout(idx, E, G)
+    for mode in MODES:
+        D = moe.moe_dispatch(L, dev_bf16(d["x"]), w_d, idx_d, mode)
+        R = Lo["R_expert"] if mode == "expert" else Lo["R_group"]
+        y_ref = orc.dispatch_bf16(Lo, mode, d["x"], d["topk_w"], idx)["recv_x"]
+        out = moe.moe_combine(L, D.recv_x, w_d, mode)
+        assert_combine_equal(host_u16(out), orc.combine(Lo, mode, y_ref, d["topk_w"]))
+        assert int(L.status.item()) == 3
+        # y with too few rows: slots beyond it are skipped and reported
+        short = R - 10
+        out = moe.moe_combine(L, D.recv_x[:short].contiguous(), w_d, mode)
+        torch.cuda.synchronize()
+        assert int(L.status.item()) & moe.STATUS_Y_ROWS
+        slot = (Lo["slot_e"] if mode == "expert" else Lo["slot_g"]).copy()
+        slot[slot >= short] = -1
+        Lc = dict(Lo, slot_e=slot, slot_g=slot)
+        assert_combine_equal(host_u16(out), orc.combine(Lc, mode, y_ref, d["topk_w"]))
+        moe.moe_layout(idx_d, E, G, out=L)      # restore status for the next mode
+
+
+# ------------------------------------------------------------------ whole path
+
+@pytest.mark.parametrize("name", ["t256", "skew"])
+def test_path_is_deterministic(moe, name):
+    d = workload(name)
+    wl = d["workload"]
+    idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
+    first = None
+    for _ in range(20):
+        L = moe.moe_layout(idx_d, wl.E, wl.G)
+        outs = []
+        for mode in MODES:
+            D = moe.moe_dispatch(L, x_d, w_d, idx_d, mode)
+            outs.append(host_u16(moe.moe_combine(L, D.recv_x, w_d, mode)))
+            outs.append(L.slot_e.cpu().numpy().copy())
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                np.testing.assert_array_equal(a, b)
+
+
+def test_stream_ordering_on_side_stream(moe, orc):
+    """Calls on a non-default stream are ordered by that stream alone."""
+    d = workload("t256")
+    wl = d["workload"]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
+        L = moe.moe_layout(idx_d, wl.E, wl.G)
+        D = moe.moe_dispatch(L, x_d, w_d, idx_d, "group")
+        out = moe.moe_combine(L, D.recv_x, w_d, "group")
+    s.synchronize()
+    np.testing.assert_array_equal(host_u16(out), d["x"])
