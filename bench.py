@@ -170,6 +170,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the plain reference copy (256 MiB, 5 times): a known byte "
+                         "count for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -184,6 +187,16 @@ def main():
     import synth_inputs as si
 
     torch.cuda.init()
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.full((n,), 3, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(5):
+            moe.moe_ref_copy(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy": {"bytes_read": n, "bytes_written": n, "launches": 5}}))
+        return
     d = si.make_workload(args.workload)
     wl = d["workload"]
     T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K

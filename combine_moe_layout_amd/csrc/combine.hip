@@ -44,7 +44,8 @@ __device__ __forceinline__ u32x4 pack8(const float (&acc)[8])
 }
 
 // KT > 0: fast path compiled for exactly KT valid entries; KT == 0: general only.
-template <int ITER, int KT, bool NT, bool FULL>
+// NTL / NT: non-temporal row loads / output stores.
+template <int ITER, int KT, bool NTL, bool NT, bool FULL>
 __global__ __launch_bounds__(kCombineBS) void combine_kernel(
     const u32x4 *__restrict__ y, int64_t y_rows, int nvec, int K,
     const int32_t *__restrict__ slot, const float *__restrict__ topk_w, u32x4 *__restrict__ out,
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kCombineBS) void combine_kernel(
                     if (FULL || j < nvec) {
                         u32x4 v[KT];
 #pragma unroll
-                        for (int k = 0; k < KT; ++k) v[k] = rows[k][j];
+                        for (int k = 0; k < KT; ++k) v[k] = load16<NTL>(rows[k] + j);
                         float acc[8];
 #pragma unroll
                         for (int m = 0; m < 8; ++m) acc[m] = -0.f;
@@ -108,31 +109,37 @@ __global__ __launch_bounds__(kCombineBS) void combine_kernel(
         for (int k = 0; k < K; ++k) {
             const int s = ts[k];
             if (s < 0 || s >= y_rows) continue;
-            fma8(acc, tw[k], y[(size_t)s * nvec + j]);
+            fma8(acc, tw[k], load16<NTL>(y + (size_t)s * nvec + j));
         }
         store16<NT>(orow + j, pack8(acc));
     }
 }
 
-template <int ITER, int KT>
+template <int ITER, int KT, bool NTL>
 auto pick_full(bool nt, bool full)
 {
-    if (nt) return full ? combine_kernel<ITER, KT, true, true> : combine_kernel<ITER, KT, true, false>;
-    return full ? combine_kernel<ITER, KT, false, true> : combine_kernel<ITER, KT, false, false>;
+    if (nt) return full ? combine_kernel<ITER, KT, NTL, true, true> : combine_kernel<ITER, KT, NTL, true, false>;
+    return full ? combine_kernel<ITER, KT, NTL, false, true> : combine_kernel<ITER, KT, NTL, false, false>;
+}
+
+template <int ITER, int KT>
+auto pick_ntl(bool ntl, bool nt, bool full)
+{
+    return ntl ? pick_full<ITER, KT, true>(nt, full) : pick_full<ITER, KT, false>(nt, full);
 }
 
 template <int KT>
-auto pick_iter(int iter, bool nt, bool full)
+auto pick_iter(int iter, bool ntl, bool nt, bool full)
 {
     switch (iter) {
-    case 1: return pick_full<1, KT>(nt, full);
-    case 2: return pick_full<2, KT>(nt, full);
-    case 3: return pick_full<3, KT>(nt, full);
-    case 4: return pick_full<4, KT>(nt, full);
-    case 5: return pick_full<5, KT>(nt, full);
-    case 6: return pick_full<6, KT>(nt, full);
-    case 7: return pick_full<7, KT>(nt, full);
-    default: return pick_full<8, KT>(nt, full);
+    case 1: return pick_ntl<1, KT>(ntl, nt, full);
+    case 2: return pick_ntl<2, KT>(ntl, nt, full);
+    case 3: return pick_ntl<3, KT>(ntl, nt, full);
+    case 4: return pick_ntl<4, KT>(ntl, nt, full);
+    case 5: return pick_ntl<5, KT>(ntl, nt, full);
+    case 6: return pick_ntl<6, KT>(ntl, nt, full);
+    case 7: return pick_ntl<7, KT>(ntl, nt, full);
+    default: return pick_ntl<8, KT>(ntl, nt, full);
     }
 }
 
@@ -184,14 +191,14 @@ hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, co
     const int nvec = H / 8;
     const int iter = iters_for(nvec, kCombineBS);
     const bool full = nvec % (kCombineBS * iter) == 0;
-    const bool nt = tuning().nt_store;
+    const bool nt = tuning().combine_nt_store, ntl = tuning().combine_nt_load;
     void (*fn)(const u32x4 *, int64_t, int, int, const int32_t *, const float *, u32x4 *, int32_t *);
     switch (K) {
-    case 2: fn = pick_iter<2>(iter, nt, full); break;
-    case 4: fn = pick_iter<4>(iter, nt, full); break;
-    case 6: fn = pick_iter<6>(iter, nt, full); break;
-    case 8: fn = pick_iter<8>(iter, nt, full); break;
-    default: fn = pick_iter<0>(iter, nt, full); break;
+    case 2: fn = pick_iter<2>(iter, ntl, nt, full); break;
+    case 4: fn = pick_iter<4>(iter, ntl, nt, full); break;
+    case 6: fn = pick_iter<6>(iter, ntl, nt, full); break;
+    case 8: fn = pick_iter<8>(iter, ntl, nt, full); break;
+    default: fn = pick_iter<0>(iter, ntl, nt, full); break;
     }
     hipLaunchKernelGGL(fn, dim3(T), dim3(kCombineBS), 0, stream, (const u32x4 *)y, y_rows, nvec, K,
                        slot, topk_w, (u32x4 *)out, status);

@@ -5,18 +5,20 @@
 // Design. One workgroup per source token. The workgroup reads the token's row
 // once into registers with 16-byte loads (each lane holds ITER vectors, so
 // the row is read exactly once from HBM), then writes those registers to each
-// destination row with 16-byte non-temporal stores: the traffic is one read
-// of x and R row writes, the minimum. This is the single-GPU form of the row
+// destination row with 16-byte stores: the traffic is one read of x and R
+// row writes, the minimum. This is the single-GPU form of the row
 // copy of "perf(ep): optimize IntraNode dispatch kernel for MI350X" (ROCm/mori
 // pull request 586): Technical Details 3 (a wave-wide vector copy whose
 // unroll must fit the hidden size — here ITER is chosen from H so the row is
 // covered in whole passes with no remainder loop) and 4 (the K weights and K
 // indices travel with each row, written by K lanes each). Destination slots
 // come from the layout's cached slots (Technical Details 1): a token reads K
-// (or G) integers instead of re-deriving its routing. Non-temporal stores and
-// 128-bit accesses follow "Optimized rocm specific multicast transpose kernel"
-// (ROCm/TransformerEngine pull request 586), Change Summary: CDNA4's L2
-// allocates on write, and rows written once should not evict useful lines.
+// (or G) integers instead of re-deriving its routing. The cache policy of the
+// row accesses is chosen by measurement on MI355X, not copied from the
+// non-temporal stores of "Optimized rocm specific multicast transpose kernel"
+// (ROCm/TransformerEngine pull request 586, Change Summary): there, CDNA4's
+// write-allocate L2 made NT stores pay; here a plain streaming store sustains
+// more write bandwidth than an NT one, while NT loads read markedly faster.
 //
 // FP8: each lane holds 16 consecutive elements (two 16-byte loads); the 8
 // lanes of one 128-block reduce amax with three xor-shuffles; every lane then
@@ -224,8 +226,13 @@ const Tuning &tuning()
 {
     static const Tuning t = [] {
         Tuning r;
-        if (const char *s = getenv("MOE_EP_NT_STORE")) r.nt_store = atoi(s) != 0;
-        if (const char *s = getenv("MOE_EP_NT_LOAD")) r.nt_load = atoi(s) != 0;
+        auto env = [](const char *name, bool &v) {
+            if (const char *s = getenv(name)) v = atoi(s) != 0;
+        };
+        env("MOE_EP_DISPATCH_NT_LOAD", r.dispatch_nt_load);
+        env("MOE_EP_DISPATCH_NT_STORE", r.dispatch_nt_store);
+        env("MOE_EP_COMBINE_NT_LOAD", r.combine_nt_load);
+        env("MOE_EP_COMBINE_NT_STORE", r.combine_nt_store);
         return r;
     }();
     return t;
@@ -238,7 +245,7 @@ hipError_t launch_dispatch_bf16(const void *x, int T, int H, int K, int nslot, c
     const int nvec = H / 8;
     const int iter = iters_for(nvec, kDispatchBS);
     const bool full = nvec % (kDispatchBS * iter) == 0;
-    auto fn = pick<Bf16Inst>(iter, tuning().nt_store, tuning().nt_load, full);
+    auto fn = pick<Bf16Inst>(iter, tuning().dispatch_nt_store, tuning().dispatch_nt_load, full);
     hipLaunchKernelGGL(fn, dim3(T), dim3(kDispatchBS), 0, stream, (const u32x4 *)x, nvec, K, nslot,
                        slots, topk_w, topk_idx, (u32x4 *)recv_x, recv_w, recv_idx);
     return hipGetLastError();
@@ -252,7 +259,7 @@ hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, co
     const int nch = H / 16;
     const int iter = iters_for(nch, kFp8BS);
     const bool full = nch % (kFp8BS * iter) == 0;
-    auto fn = pick<Fp8Inst>(iter, tuning().nt_store, tuning().nt_load, full);
+    auto fn = pick<Fp8Inst>(iter, tuning().dispatch_nt_store, tuning().dispatch_nt_load, full);
     hipLaunchKernelGGL(fn, dim3(T), dim3(kFp8BS), 0, stream, (const u32x4 *)x, nch, K, nslot, slots,
                        topk_w, topk_idx, (u32x4 *)recv_q, recv_scale, recv_w, recv_idx);
     return hipGetLastError();

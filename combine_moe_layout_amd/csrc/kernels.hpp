@@ -24,9 +24,14 @@ struct LayoutPtrs {
 hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L,
                          int32_t *ws, hipStream_t stream);
 
+// Cache policy of the row loads and stores, per kernel. Defaults are the
+// measured best on MI355X; MOE_EP_{DISPATCH,COMBINE}_NT_{LOAD,STORE}=0/1 in the
+// environment override them (read once per process) for A/B runs.
 struct Tuning {
-    bool nt_store = true;   // non-temporal stores for receive rows / combine output
-    bool nt_load = false;   // non-temporal loads of source rows
+    bool dispatch_nt_load = true;    // x rows are read once
+    bool dispatch_nt_store = false;  // receive rows
+    bool combine_nt_load = true;     // expert rows are read once per (token, k)
+    bool combine_nt_store = false;   // output rows
 };
 const Tuning &tuning();
 
