@@ -15,7 +15,8 @@ events recorded around every launch in the timed region, on the stream the
 kernels run on. The same line carries the roofline of the dominant kernel, the
 CPU oracle timed on host cores (a bounded sample of the same workload), and
 secondary measurements (the deduplicated per-group layout, FP8 dispatch on the
-FP8 workload, a plain copy ceiling, flushed-cache timings).
+FP8 workload, a plain copy ceiling, each kernel repeated alone, cold-cache
+timings).
 """
 from __future__ import annotations
 
@@ -307,15 +308,23 @@ def extras(moe, d, dv, args):
                     "combine_gbs": round(bc / stats(tg[1])["median"] / 1e3, 1)}
     del Dg
 
-    # flushed-cache timing of the per-expert kernels (the 256 MB last-level cache is
-    # overwritten before every call, outside the timed events)
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    flush = lambda: scratch.fill_(1)
     De = dv.D["expert"]
     disp_e = lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "expert", "bf16", out=De)
     comb_e = lambda: moe.moe_combine(L, De.recv_x, dv.w, "expert", out=dv.out)
-    tc = time_calls([disp_e, comb_e], 15, flush=flush)
     bde, bce = sum(dispatch_bytes(T, H, K, G, R, "expert")), sum(combine_bytes(T, H, K, R))
+    # each kernel repeated on its own (no other kernel's write-back in between)
+    td = time_calls([disp_e], it)
+    tcb = time_calls([comb_e], it)
+    res["expert_alone"] = {"dispatch_us": stats(td[0])["median"], "combine_us": stats(tcb[0])["median"],
+                           "dispatch_gbs": round(bde / stats(td[0])["median"] / 1e3, 1),
+                           "combine_gbs": round(bce / stats(tcb[0])["median"] / 1e3, 1)}
+
+    # cold-cache timing of the per-expert kernels: 1 GiB is read before every call
+    # (outside the timed events), so the 256 MB last-level cache holds only clean,
+    # unrelated lines when the kernel starts
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush = lambda: scratch.sum()
+    tc = time_calls([disp_e, comb_e], 15, flush=flush)
     res["expert_flushed"] = {"dispatch_us": stats(tc[0])["median"], "combine_us": stats(tc[1])["median"],
                              "dispatch_gbs": round(bde / stats(tc[0])["median"] / 1e3, 1),
                              "combine_gbs": round(bce / stats(tc[1])["median"] / 1e3, 1)}

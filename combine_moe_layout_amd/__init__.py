@@ -29,7 +29,8 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libmoe_ep.so")
+# MOE_EP_LIB selects another build of the same library (e.g. a tuning variant).
+_LIB_PATH = os.environ.get("MOE_EP_LIB") or os.path.join(_PKG, "libmoe_ep.so")
 
 MODE_EXPERT, MODE_GROUP = 0, 1
 DTYPE_BF16, DTYPE_FP8 = 0, 1

@@ -46,30 +46,34 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, save_temps: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+def _compile(src: str, save_temps: bool, build_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *(f"-D{d}" for d in defines), "-I", INCLUDE, "-I", CSRC, "-c",
+           src, "-o", obj]
     if save_temps:
         cmd += ["-save-temps=obj"]
-    r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)
+    r = subprocess.run(cmd, capture_output=True, text=True, cwd=build_dir)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(save_temps: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(save_temps: bool = False, jobs: int | None = None, out: str = LIB,
+          build_dir: str = BUILD, defines=()) -> str:
+    """Compile and link the library. `out`, `build_dir` and `defines` (NAME=VALUE
+    compile-time knobs) make tuning variants without touching the default build."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, save_temps), srcs))
-    tmp = LIB + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, save_temps, build_dir, defines), srcs))
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def is_stale() -> bool:

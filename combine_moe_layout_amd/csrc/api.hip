@@ -142,8 +142,8 @@ int moe_combine(const moe_layout_t *L, int mode, int H, const void *y, int64_t y
     if (!y || !topk_w || !out) return MOE_ERR_NULL_PTR;
     if (!aligned16(y) || !aligned16(out) || !aligned4(topk_w)) return MOE_ERR_MISALIGNED;
     const int32_t *slot = mode == MOE_MODE_EXPERT ? L->slot_e : L->slot_g;
-    hipError_t e = moe::launch_combine(y, y_rows, L->T, H, L->K, slot, topk_w, out, L->status,
-                                       (hipStream_t)stream);
+    hipError_t e = moe::launch_combine(y, y_rows, L->T, H, L->K, slot, mode == MOE_MODE_GROUP,
+                                       topk_w, out, L->status, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

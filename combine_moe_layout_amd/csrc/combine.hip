@@ -9,12 +9,14 @@
 // the rows are found through the layout's cached slots. The single rounding
 // of an fp32 accumulator follows ROCm/vllm pull request 1297, Accuracy.
 //
-// Design. One workgroup per token; each lane owns 8 consecutive elements
-// (one 16-byte vector) of the output row per pass. For a token whose K slots
-// are all valid (the normal case) the K row vectors are loaded first — K
-// independent 16-byte loads in flight per lane — and then folded with K fmaf
-// per element in k order, starting from -0. Tokens with skipped entries take
-// a general loop with the same arithmetic. Nothing here is a dense
+// Design. One workgroup per token; each lane owns ITER 16-byte vectors (8
+// elements each) of the output row per pass and keeps their fp32
+// accumulators in registers. For a token whose K slots are all valid (the
+// normal case) the rows are read either row by row in contiguous bursts
+// (per-expert layout) or column by column with the next column prefetched
+// (per-group layout, where rows repeat), and folded with one fmaf per element
+// and k, in k order, starting from -0. Tokens with skipped entries take a
+// general loop with the same arithmetic. Nothing here is a dense
 // contraction (K <= 32 weights per row), so there is no MFMA: the kernel is
 // bound by the HBM reads of the expert rows.
 #include "common.hpp"
@@ -44,8 +46,11 @@ __device__ __forceinline__ u32x4 pack8(const float (&acc)[8])
 }
 
 // KT > 0: fast path compiled for exactly KT valid entries; KT == 0: general only.
-// NTL / NT: non-temporal row loads / output stores.
-template <int ITER, int KT, bool NTL, bool NT, bool FULL>
+// ROWWISE: traversal of the fast path (see below). Rows are read with
+// non-temporal loads (each byte of y is read once in the per-expert layout)
+// and the output is written with plain stores, the faster pair measured on
+// MI355X.
+template <int ITER, int KT, bool ROWWISE, bool FULL>
 __global__ __launch_bounds__(kCombineBS) void combine_kernel(
     const u32x4 *__restrict__ y, int64_t y_rows, int nvec, int K,
     const int32_t *__restrict__ slot, const float *__restrict__ topk_w, u32x4 *__restrict__ out,
@@ -75,20 +80,77 @@ __global__ __launch_bounds__(kCombineBS) void combine_kernel(
                 rows[k] = y + (size_t)ts[k] * nvec;
                 w[k] = tw[k];
             }
-            for (int base = 0; base < nvec; base += kCombineBS * ITER) {
+            if constexpr (ROWWISE && FULL) {
+                // Row-wise: wave w owns the contiguous span of ITER * 64 vectors
+                // starting at w * ITER * 64 of every pass; it reads that span of
+                // row k (ITER loads of 1 KiB, back to back in memory), folds it
+                // into ITER x 8 fp32 accumulators, then moves to row k + 1. Each
+                // row is thus visited in long contiguous bursts, and the fma
+                // chain of every element still runs in k order.
+                const int wave = tid / kWave, lane = tid % kWave;
+                for (int base = 0; base < nvec; base += kCombineBS * ITER) {
+                    const int j0 = base + wave * (kWave * ITER) + lane;
+                    float acc[ITER][8];
 #pragma unroll
-                for (int i = 0; i < ITER; ++i) {
-                    const int j = base + i * kCombineBS + tid;
-                    if (FULL || j < nvec) {
-                        u32x4 v[KT];
+                    for (int i = 0; i < ITER; ++i)
 #pragma unroll
-                        for (int k = 0; k < KT; ++k) v[k] = load16<NTL>(rows[k] + j);
+                        for (int m = 0; m < 8; ++m) acc[i][m] = -0.f;
+#pragma unroll
+                    for (int k = 0; k < KT; ++k) {
+                        u32x4 v[ITER];
+#pragma unroll
+                        for (int i = 0; i < ITER; ++i) v[i] = load16<true>(rows[k] + j0 + i * kWave);
+#pragma unroll
+                        for (int i = 0; i < ITER; ++i) fma8(acc[i], w[k], v[i]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < ITER; ++i) store16<false>(orow + j0 + i * kWave, pack8(acc[i]));
+                }
+            } else if constexpr (FULL) {
+                // Column-wise, double-buffered: pass i reads one vector of each
+                // of the K rows; the K loads of pass i + 1 are issued before the
+                // FMAs of pass i, so 2K row loads per lane stay in flight. Used
+                // for the per-group layout, where one token's K slots repeat
+                // rows: the repeats are loaded back to back, while still cached.
+                for (int base = 0; base < nvec; base += kCombineBS * ITER) {
+                    u32x4 cur[KT], nxt[KT];
+#pragma unroll
+                    for (int k = 0; k < KT; ++k) cur[k] = load16<true>(rows[k] + base + tid);
+#pragma unroll
+                    for (int i = 0; i < ITER; ++i) {
+                        const int j = base + i * kCombineBS + tid;
+                        if (i + 1 < ITER) {
+#pragma unroll
+                            for (int k = 0; k < KT; ++k) nxt[k] = load16<true>(rows[k] + j + kCombineBS);
+                        }
                         float acc[8];
 #pragma unroll
                         for (int m = 0; m < 8; ++m) acc[m] = -0.f;
 #pragma unroll
-                        for (int k = 0; k < KT; ++k) fma8(acc, w[k], v[k]);
-                        store16<NT>(orow + j, pack8(acc));
+                        for (int k = 0; k < KT; ++k) fma8(acc, w[k], cur[k]);
+                        store16<false>(orow + j, pack8(acc));
+                        if (i + 1 < ITER) {
+#pragma unroll
+                            for (int k = 0; k < KT; ++k) cur[k] = nxt[k];
+                        }
+                    }
+                }
+            } else {
+                for (int base = 0; base < nvec; base += kCombineBS * ITER) {
+#pragma unroll
+                    for (int i = 0; i < ITER; ++i) {
+                        const int j = base + i * kCombineBS + tid;
+                        if (FULL || j < nvec) {
+                            u32x4 v[KT];
+#pragma unroll
+                            for (int k = 0; k < KT; ++k) v[k] = load16<true>(rows[k] + j);
+                            float acc[8];
+#pragma unroll
+                            for (int m = 0; m < 8; ++m) acc[m] = -0.f;
+#pragma unroll
+                            for (int k = 0; k < KT; ++k) fma8(acc, w[k], v[k]);
+                            store16<false>(orow + j, pack8(acc));
+                        }
                     }
                 }
             }
@@ -109,37 +171,31 @@ __global__ __launch_bounds__(kCombineBS) void combine_kernel(
         for (int k = 0; k < K; ++k) {
             const int s = ts[k];
             if (s < 0 || s >= y_rows) continue;
-            fma8(acc, tw[k], load16<NTL>(y + (size_t)s * nvec + j));
+            fma8(acc, tw[k], load16<true>(y + (size_t)s * nvec + j));
         }
-        store16<NT>(orow + j, pack8(acc));
+        store16<false>(orow + j, pack8(acc));
     }
 }
 
-template <int ITER, int KT, bool NTL>
-auto pick_full(bool nt, bool full)
-{
-    if (nt) return full ? combine_kernel<ITER, KT, NTL, true, true> : combine_kernel<ITER, KT, NTL, true, false>;
-    return full ? combine_kernel<ITER, KT, NTL, false, true> : combine_kernel<ITER, KT, NTL, false, false>;
-}
-
 template <int ITER, int KT>
-auto pick_ntl(bool ntl, bool nt, bool full)
+auto pick_variant(bool rowwise, bool full)
 {
-    return ntl ? pick_full<ITER, KT, true>(nt, full) : pick_full<ITER, KT, false>(nt, full);
+    if (rowwise) return full ? combine_kernel<ITER, KT, true, true> : combine_kernel<ITER, KT, true, false>;
+    return full ? combine_kernel<ITER, KT, false, true> : combine_kernel<ITER, KT, false, false>;
 }
 
 template <int KT>
-auto pick_iter(int iter, bool ntl, bool nt, bool full)
+auto pick_iter(int iter, bool rowwise, bool full)
 {
     switch (iter) {
-    case 1: return pick_ntl<1, KT>(ntl, nt, full);
-    case 2: return pick_ntl<2, KT>(ntl, nt, full);
-    case 3: return pick_ntl<3, KT>(ntl, nt, full);
-    case 4: return pick_ntl<4, KT>(ntl, nt, full);
-    case 5: return pick_ntl<5, KT>(ntl, nt, full);
-    case 6: return pick_ntl<6, KT>(ntl, nt, full);
-    case 7: return pick_ntl<7, KT>(ntl, nt, full);
-    default: return pick_ntl<8, KT>(ntl, nt, full);
+    case 1: return pick_variant<1, KT>(rowwise, full);
+    case 2: return pick_variant<2, KT>(rowwise, full);
+    case 3: return pick_variant<3, KT>(rowwise, full);
+    case 4: return pick_variant<4, KT>(rowwise, full);
+    case 5: return pick_variant<5, KT>(rowwise, full);
+    case 6: return pick_variant<6, KT>(rowwise, full);
+    case 7: return pick_variant<7, KT>(rowwise, full);
+    default: return pick_variant<8, KT>(rowwise, full);
     }
 }
 
@@ -186,19 +242,20 @@ inline int iters_for(int n, int bs)
 }  // namespace
 
 hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, const int32_t *slot,
-                          const float *topk_w, void *out, int32_t *status, hipStream_t stream)
+                          bool rows_repeat, const float *topk_w, void *out, int32_t *status,
+                          hipStream_t stream)
 {
     const int nvec = H / 8;
     const int iter = iters_for(nvec, kCombineBS);
     const bool full = nvec % (kCombineBS * iter) == 0;
-    const bool nt = tuning().combine_nt_store, ntl = tuning().combine_nt_load;
+    const bool rowwise = !rows_repeat;
     void (*fn)(const u32x4 *, int64_t, int, int, const int32_t *, const float *, u32x4 *, int32_t *);
     switch (K) {
-    case 2: fn = pick_iter<2>(iter, ntl, nt, full); break;
-    case 4: fn = pick_iter<4>(iter, ntl, nt, full); break;
-    case 6: fn = pick_iter<6>(iter, ntl, nt, full); break;
-    case 8: fn = pick_iter<8>(iter, ntl, nt, full); break;
-    default: fn = pick_iter<0>(iter, ntl, nt, full); break;
+    case 2: fn = pick_iter<2>(iter, rowwise, full); break;
+    case 4: fn = pick_iter<4>(iter, rowwise, full); break;
+    case 6: fn = pick_iter<6>(iter, rowwise, full); break;
+    case 8: fn = pick_iter<8>(iter, rowwise, full); break;
+    default: fn = pick_iter<0>(iter, rowwise, full); break;
     }
     hipLaunchKernelGGL(fn, dim3(T), dim3(kCombineBS), 0, stream, (const u32x4 *)y, y_rows, nvec, K,
                        slot, topk_w, (u32x4 *)out, status);

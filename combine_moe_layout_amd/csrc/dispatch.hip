@@ -231,8 +231,6 @@ const Tuning &tuning()
         };
         env("MOE_EP_DISPATCH_NT_LOAD", r.dispatch_nt_load);
         env("MOE_EP_DISPATCH_NT_STORE", r.dispatch_nt_store);
-        env("MOE_EP_COMBINE_NT_LOAD", r.combine_nt_load);
-        env("MOE_EP_COMBINE_NT_STORE", r.combine_nt_store);
         return r;
     }();
     return t;

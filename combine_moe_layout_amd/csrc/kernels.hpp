@@ -20,18 +20,17 @@ struct LayoutPtrs {
     int32_t *slot_e, *slot_g, *slot_tg, *recv_src_e, *recv_src_g, *status;
 };
 
-// Workspace: tile_cnt_e [E][tiles], tile_cnt_g [G][tiles], tile_err [tiles].
+// Workspace: a tile-major table [tiles][E + G + 1] of expert counts, group
+// counts and error bits per tile.
 hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L,
                          int32_t *ws, hipStream_t stream);
 
-// Cache policy of the row loads and stores, per kernel. Defaults are the
-// measured best on MI355X; MOE_EP_{DISPATCH,COMBINE}_NT_{LOAD,STORE}=0/1 in the
+// Cache policy of the dispatch row loads and stores. Defaults are the
+// measured best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1 in the
 // environment override them (read once per process) for A/B runs.
 struct Tuning {
     bool dispatch_nt_load = true;    // x rows are read once
     bool dispatch_nt_store = false;  // receive rows
-    bool combine_nt_load = true;     // expert rows are read once per (token, k)
-    bool combine_nt_store = false;   // output rows
 };
 const Tuning &tuning();
 
@@ -45,9 +44,10 @@ hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, co
                                float *recv_scale, float *recv_w, int32_t *recv_idx,
                                hipStream_t stream);
 
-// Combine. slot: [T, K] (slot_e or slot_g).
+// Combine. slot: [T, K] (slot_e, or slot_g whose entries may repeat within a token).
 hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, const int32_t *slot,
-                          const float *topk_w, void *out, int32_t *status, hipStream_t stream);
+                          bool rows_repeat, const float *topk_w, void *out, int32_t *status,
+                          hipStream_t stream);
 
 // FP8 identity expert; rows to convert = *nrows (device), grid covers `capacity` rows.
 hipError_t launch_fp8_dequant(const void *q, const float *scale, void *y, int64_t capacity, int H,

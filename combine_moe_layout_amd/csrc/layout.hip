@@ -21,12 +21,14 @@
 // which is the stable token-ascending order, and a token's repeated expert is
 // seen as its own bit already set. Groups use one ballot per group per wave.
 //
-// Kernel 1 (count): per tile, expert and group counts + error bits -> workspace.
-// Kernel 2 (place): every tile re-reads the [E][tiles] count table it needs
-// (tiny: E * tiles ints), forms global offsets = exclusive prefix over experts
-// of the totals + prefix over earlier tiles, rebuilds its LDS words and
-// writes the slots and receive-source lists. Tile 0 also writes the counts,
-// offsets and status.
+// Kernel 1 (count): per tile, expert and group counts + error bits -> one row
+// of a tile-major table in the workspace.
+// Kernel 2 (place): every tile reads the table column-wise (tiny: (E+G+1) x
+// tiles ints, coalesced), forms global offsets = exclusive prefix over experts
+// of the totals + prefix over earlier tiles, rebuilds its LDS words and writes
+// the slots and receive-source lists. Tile 0 also writes the counts, offsets
+// and status. Global loads are issued ahead of their first use, so each kernel
+// costs about one memory round trip plus its LDS work.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,47 +38,82 @@ namespace {
 
 constexpr int kWaves = kLayoutTile / kWave;   // 4
 constexpr int kMaxG = 32;
+constexpr int kMaxEChunks = (1024 + kLayoutTile - 1) / kLayoutTile;   // E <= 1024
 
-// Insert token t's valid experts into the LDS words; returns the bitmask of
-// k positions that are invalid (out of range, or a repeat of an earlier k),
-// and ORs error bits into err and the token's groups into gm.
-__device__ __forceinline__ uint32_t insert_token(const int32_t *__restrict__ row, int K, int E,
-                                                 int epg, unsigned long long *emask, int wave,
-                                                 int lane, int &err, uint32_t &gm)
+// Group of expert x: a shift when experts-per-group is a power of two.
+__device__ __forceinline__ int group_of(int x, int epg, int epg_shift)
 {
-    const unsigned long long bit = 1ull << lane;
-    uint32_t bad = 0;
-    for (int k = 0; k < K; ++k) {
-        const int e = row[k];
-        if ((unsigned)e >= (unsigned)E) { err |= 1; bad |= 1u << k; continue; }
-        const unsigned long long old = atomicOr(&emask[e * kWaves + wave], bit);
-        if (old & bit) { err |= 2; bad |= 1u << k; continue; }
-        gm |= 1u << (e / epg);
-    }
-    return bad;
+    return epg_shift >= 0 ? (x >> epg_shift) : (x / epg);
 }
 
+// A token's K expert indices, loaded into registers at kernel entry so the
+// loads overlap the LDS initialisation. Entries k >= K are -1.
+template <int KMAX>
+__device__ __forceinline__ void load_row(const int32_t *__restrict__ idx, int t, int T, int K,
+                                         int (&e)[KMAX])
+{
+    const int32_t *row = idx + (size_t)t * K;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) e[k] = (t < T && k < K) ? row[k] : -1;
+}
+
+// What inserting one token found: k positions out of range, k positions that
+// repeat an earlier k, and the groups the token reaches.
+struct Inserted {
+    uint32_t oor, dup, gm;
+    __device__ int err() const { return (oor ? 1 : 0) | (dup ? 2 : 0); }
+    __device__ uint32_t bad() const { return oor | dup; }
+};
+
+// Insert a token's valid experts into the LDS words. A token is handled by one
+// lane, in k order, so "earlier k" is well defined. (Results are returned by
+// value: with reference out-parameters the compiler merged the updates into
+// a dynamically indexed private array, i.e. scratch memory.)
+template <int KMAX>
+__device__ __forceinline__ Inserted insert_token(const int (&e)[KMAX], bool live, int K, int E,
+                                                 int epg, int epg_shift,
+                                                 unsigned long long *emask, int wave, int lane)
+{
+    const unsigned long long bit = 1ull << lane;
+    uint32_t oor = 0, dup = 0, gm = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int x = e[k];
+        const bool in = live && k < K && (unsigned)x < (unsigned)E;
+        oor |= (live && k < K && !in) ? 1u << k : 0u;
+        if (in) {
+            const unsigned long long old = atomicOr(&emask[x * kWaves + wave], bit);
+            const bool rep = (old & bit) != 0;
+            dup |= rep ? 1u << k : 0u;
+            gm |= rep ? 0u : 1u << group_of(x, epg, epg_shift);
+        }
+    }
+    return Inserted{oor, dup, gm};
+}
+
+// Count kernel: one tile per workgroup. Writes row `tile` of the tile-major
+// count table: E expert counts, G group counts, then the tile's error bits.
+template <int KMAX>
 __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
-    const int32_t *__restrict__ idx, int T, int K, int E, int G, int epg, int ntiles,
-    uint32_t *__restrict__ tok_group_mask, int32_t *__restrict__ tile_cnt_e,
-    int32_t *__restrict__ tile_cnt_g, int32_t *__restrict__ tile_err)
+    const int32_t *__restrict__ idx, int T, int K, int E, int G, int epg, int epg_shift,
+    uint32_t *__restrict__ tok_group_mask, int32_t *__restrict__ table)
 {
     extern __shared__ unsigned long long emask[];   // [E][kWaves]
     __shared__ int gcnt[kMaxG][kWaves];
     __shared__ int s_err;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int tile = blockIdx.x;
+    const int t = tile * kLayoutTile + tid;
+    int e[KMAX];
+    load_row<KMAX>(idx, t, T, K, e);
     for (int i = tid; i < E * kWaves; i += kLayoutTile) emask[i] = 0ull;
     if (tid == 0) s_err = 0;
     __syncthreads();
 
-    const int t = tile * kLayoutTile + tid;
-    int err = 0;
-    uint32_t gm = 0;
-    if (t < T) {
-        insert_token(idx + (size_t)t * K, K, E, epg, emask, wave, lane, err, gm);
-        tok_group_mask[t] = gm;
-    }
+    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, epg, epg_shift, emask, wave, lane);
+    const uint32_t gm = ins.gm;
+    const int err = ins.err();
+    if (t < T) tok_group_mask[t] = gm;
     for (int g = 0; g < G; ++g) {
         const uint64_t b = __ballot((gm >> g) & 1u);
         if (lane == 0) gcnt[g][wave] = __popcll(b);
@@ -84,23 +121,17 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     if (err) atomicOr(&s_err, err);
     __syncthreads();
 
-    for (int e = tid; e < E; e += kLayoutTile) {
-        int c = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) c += __popcll(emask[e * kWaves + w]);
-        tile_cnt_e[(size_t)e * ntiles + tile] = c;
+    int32_t *row = table + (size_t)tile * (E + G + 1);
+    for (int x = tid; x < E; x += kLayoutTile) {
+        const unsigned long long *m = emask + x * kWaves;
+        row[x] = __popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]);
     }
-    if (tid < G) {
-        int c = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) c += gcnt[tid][w];
-        tile_cnt_g[(size_t)tid * ntiles + tile] = c;
-    }
-    if (tid == 0) tile_err[tile] = s_err;
+    if (tid < G) row[E + tid] = gcnt[tid][0] + gcnt[tid][1] + gcnt[tid][2] + gcnt[tid][3];
+    if (tid == 0) row[E + G] = s_err;
 }
 
-// Exclusive prefix sum over the 256 threads of the workgroup.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave_tot)
+// Exclusive prefix sum over the 256 threads of the workgroup; *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave_tot, int *total)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     int x = v;
@@ -109,72 +140,103 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave_tot)
         const int y = __shfl_up(x, o);
         if (lane >= o) x += y;
     }
+    __syncthreads();   // s_wave_tot free (a previous scan may still be reading it)
     if (lane == kWave - 1) s_wave_tot[wave] = x;
     __syncthreads();
-    int base = 0;
-    for (int w = 0; w < wave; ++w) base += s_wave_tot[w];
+    int base = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const int c = s_wave_tot[w];
+        base += w < wave ? c : 0;
+        all += c;
+    }
+    *total = all;
     return base + x - v;
 }
 
-__global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
-    const int32_t *__restrict__ idx, int T, int K, int E, int G, int epg, int ntiles,
-    const int32_t *__restrict__ tile_cnt_e, const int32_t *__restrict__ tile_cnt_g,
-    const int32_t *__restrict__ tile_err, LayoutPtrs L)
+// Sum of table column `col` over tiles, and over the tiles before `tile`.
+// Loads are issued eight tiles at a time, so a column costs ceil(tiles / 8)
+// memory round trips.
+__device__ __forceinline__ void column_sums(const int32_t *__restrict__ table, int rows, int col,
+                                            int ntiles, int tile, int &tot, int &pre)
 {
-    extern __shared__ unsigned long long emask[];   // [E][kWaves], then int base_e[E]
-    int *base_e = reinterpret_cast<int *>(emask + E * kWaves);
+    tot = 0;
+    pre = 0;
+    for (int b0 = 0; b0 < ntiles; b0 += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = (b0 + u < ntiles) ? table[(size_t)(b0 + u) * rows + col] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            tot += c[u];
+            pre += (b0 + u < tile) ? c[u] : 0;
+        }
+    }
+}
+
+// Place kernel: one tile per workgroup. Global offsets of the tile = exclusive
+// prefix over experts of the totals + prefix over earlier tiles (read from
+// the table, coalesced: thread x reads column x); then the tile's LDS words
+// are rebuilt exactly as the count kernel built them, and each pair's slot is
+// its expert's offset for this (tile, wave) plus its rank among the wave's
+// lanes.
+template <int KMAX>
+__global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
+    const int32_t *__restrict__ idx, int T, int K, int E, int G, int epg, int epg_shift,
+    int ntiles, const int32_t *__restrict__ table, LayoutPtrs L)
+{
+    extern __shared__ unsigned long long emask[];   // [E][kWaves], then int off_e[E][kWaves]
+    int *off_e = reinterpret_cast<int *>(emask + E * kWaves);
     __shared__ int s_wave_tot[kWaves];
     __shared__ int base_g[kMaxG];
     __shared__ int tot_g[kMaxG];
+    __shared__ int off_g[kMaxG][kWaves];
     __shared__ uint64_t gball[kMaxG][kWaves];
+    __shared__ int s_err;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int tile = blockIdx.x;
+    const int t = tile * kLayoutTile + tid;
+    const int rows = E + G + 1;
 
+    int e[KMAX];
+    load_row<KMAX>(idx, t, T, K, e);
     for (int i = tid; i < E * kWaves; i += kLayoutTile) emask[i] = 0ull;
+    if (tid == 0) s_err = 0;
 
-    // Global offsets of this tile: experts e = tid*ept .. tid*ept+ept-1 per thread.
-    const int ept = (E + kLayoutTile - 1) / kLayoutTile;   // <= 4
-    int tot[4] = {0, 0, 0, 0}, pre[4] = {0, 0, 0, 0};
-    int local = 0;
+    // expert offsets: experts are owned in chunks of 256 (x = chunk * 256 + tid)
+    int tot[kMaxEChunks], pre[kMaxEChunks];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = tid * ept + j;
-        if (j < ept && e < E) {
-            const int32_t *row = tile_cnt_e + (size_t)e * ntiles;
-            for (int b = 0; b < ntiles; ++b) {
-                const int c = row[b];
-                tot[j] += c;
-                if (b < tile) pre[j] += c;
-            }
-            local += tot[j];
-        }
+    for (int j = 0; j < kMaxEChunks; ++j) {
+        tot[j] = pre[j] = 0;
+        const int x = j * kLayoutTile + tid;
+        if (x < E) column_sums(table, rows, x, ntiles, tile, tot[j], pre[j]);
     }
-    const int excl = block_exclusive_scan(local, s_wave_tot);
-    int run = excl;
+    if (tid < G) column_sums(table, rows, E + tid, ntiles, tile, tot_g[tid], base_g[tid]);
+    if (tile == 0) {
+        int er = 0;
+        for (int b = tid; b < ntiles; b += kLayoutTile) er |= table[(size_t)b * rows + E + G];
+        if (er) atomicOr(&s_err, er);
+    }
+    int carry = 0;
+    int base[kMaxEChunks];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = tid * ept + j;
-        if (j < ept && e < E) {
-            base_e[e] = run + pre[j];
-            if (tile == 0) {
-                L.expert_count[e] = tot[j];
-                L.expert_offset[e] = run;
+    for (int j = 0; j < kMaxEChunks; ++j) {
+        base[j] = 0;
+        if (j * kLayoutTile < E) {   // uniform
+            int all;
+            const int excl = block_exclusive_scan(tot[j], s_wave_tot, &all);
+            const int x = j * kLayoutTile + tid;
+            if (x < E) {
+                base[j] = carry + excl + pre[j];
+                if (tile == 0) {
+                    L.expert_count[x] = tot[j];
+                    L.expert_offset[x] = carry + excl;
+                }
             }
-            run += tot[j];
+            carry += all;
         }
     }
-    if (tile == 0 && tid == kLayoutTile - 1) L.expert_offset[E] = excl + local;
-
-    if (tid < G) {
-        int tg = 0, pg = 0;
-        for (int b = 0; b < ntiles; ++b) {
-            const int c = tile_cnt_g[(size_t)tid * ntiles + b];
-            tg += c;
-            if (b < tile) pg += c;
-        }
-        tot_g[tid] = tg;
-        base_g[tid] = pg;
-    }
+    if (tile == 0 && tid == 0) L.expert_offset[E] = carry;
     __syncthreads();
     if (tid == 0) {
         int off = 0;
@@ -188,50 +250,65 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
         }
         if (tile == 0) {
             L.group_offset[G] = off;
-            int st = 0;
-            for (int b = 0; b < ntiles; ++b) st |= tile_err[b];
-            *L.status = st;
+            *L.status = s_err;
         }
     }
 
-    // Rebuild the tile's LDS words exactly as the count kernel did.
-    const int t = tile * kLayoutTile + tid;
-    const int32_t *row = idx + (size_t)t * K;
-    int err = 0;
-    uint32_t gm = 0, bad = 0;
-    if (t < T) bad = insert_token(row, K, E, epg, emask, wave, lane, err, gm);
+    // Rebuild the tile's LDS words.
+    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, epg, epg_shift, emask, wave, lane);
+    const uint32_t gm = ins.gm, bad = ins.bad();
     for (int g = 0; g < G; ++g) {
         const uint64_t b = __ballot((gm >> g) & 1u);
         if (lane == 0) gball[g][wave] = b;
     }
     __syncthreads();
+
+    // Offsets per (expert, wave) and (group, wave): base + lanes of earlier waves.
+#pragma unroll
+    for (int j = 0; j < kMaxEChunks; ++j) {
+        const int x = j * kLayoutTile + tid;
+        if (x < E) {
+            const unsigned long long *m = emask + x * kWaves;
+            int r = base[j];
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                off_e[x * kWaves + w] = r;
+                r += __popcll(m[w]);
+            }
+        }
+    }
+    if (tid < G) {
+        int r = base_g[tid];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            off_g[tid][w] = r;
+            r += __popcll(gball[tid][w]);
+        }
+    }
+    __syncthreads();
     if (t >= T) return;
 
     const uint64_t below = lanemask_lt(lane);
-    auto group_slot = [&](int g) {
-        int r = base_g[g];
-        for (int w = 0; w < wave; ++w) r += __popcll(gball[g][w]);
-        return r + __popcll(gball[g][wave] & below);
-    };
-    for (int k = 0; k < K; ++k) {
-        const size_t p = (size_t)t * K + k;
-        if ((bad >> k) & 1u) {
-            L.slot_e[p] = -1;
-            L.slot_g[p] = -1;
-            continue;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        if (k < K) {
+            const size_t p = (size_t)t * K + k;
+            int se = -1, sg = -1;
+            if (!((bad >> k) & 1u)) {
+                const int x = e[k];
+                se = off_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
+                L.recv_src_e[se] = (int32_t)p;
+                const int g = group_of(x, epg, epg_shift);
+                sg = off_g[g][wave] + __popcll(gball[g][wave] & below);
+            }
+            L.slot_e[p] = se;
+            L.slot_g[p] = sg;
         }
-        const int e = row[k];
-        int r = base_e[e];
-        for (int w = 0; w < wave; ++w) r += __popcll(emask[e * kWaves + w]);
-        r += __popcll(emask[e * kWaves + wave] & below);
-        L.slot_e[p] = r;
-        L.recv_src_e[r] = (int32_t)p;
-        L.slot_g[p] = group_slot(e / epg);
     }
     for (int g = 0; g < G; ++g) {
         int s = -1;
         if ((gm >> g) & 1u) {
-            s = group_slot(g);
+            s = off_g[g][wave] + __popcll(gball[g][wave] & below);
             L.recv_src_g[s] = t;
         }
         L.slot_tg[(size_t)t * G + g] = s;
@@ -263,17 +340,17 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
     }
     const int ntiles = layout_tiles(T);
     const int epg = E / G;
-    int32_t *tile_cnt_e = ws;
-    int32_t *tile_cnt_g = tile_cnt_e + (size_t)E * ntiles;
-    int32_t *tile_err = tile_cnt_g + (size_t)G * ntiles;
+    const int epg_shift = (epg & (epg - 1)) == 0 ? __builtin_ctz((unsigned)epg) : -1;
     const size_t lds1 = (size_t)E * kWaves * sizeof(unsigned long long);
-    const size_t lds2 = lds1 + (size_t)E * sizeof(int);
-    hipLaunchKernelGGL(layout_count_kernel, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K,
-                       E, G, epg, ntiles, L.tok_group_mask, tile_cnt_e, tile_cnt_g, tile_err);
+    const size_t lds2 = lds1 + (size_t)E * kWaves * sizeof(int);
+    auto count = K <= 8 ? layout_count_kernel<8> : layout_count_kernel<32>;
+    auto place = K <= 8 ? layout_place_kernel<8> : layout_place_kernel<32>;
+    hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G, epg,
+                       epg_shift, L.tok_group_mask, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(layout_place_kernel, dim3(ntiles), dim3(kLayoutTile), lds2, stream, idx, T, K,
-                       E, G, epg, ntiles, tile_cnt_e, tile_cnt_g, tile_err, L);
+    hipLaunchKernelGGL(place, dim3(ntiles), dim3(kLayoutTile), lds2, stream, idx, T, K, E, G, epg,
+                       epg_shift, ntiles, static_cast<const int32_t *>(ws), L);
     return hipGetLastError();
 }
 
