@@ -40,10 +40,12 @@ constexpr int kWaves = kLayoutTile / kWave;   // 4
 constexpr int kMaxG = 32;
 constexpr int kMaxEChunks = (1024 + kLayoutTile - 1) / kLayoutTile;   // E <= 1024
 
-// Group of expert x: a shift when experts-per-group is a power of two.
-__device__ __forceinline__ int group_of(int x, int epg, int epg_shift)
+// Group of expert x, floor(x / epg), without a division: a multiply-high by
+// magic = floor(2^32 / epg) + 1 (for x < 2^16 the product's error is below
+// 2^-16 and cannot cross an integer), or x itself when epg = 1.
+__device__ __forceinline__ int group_of(int x, uint32_t magic)
 {
-    return epg_shift >= 0 ? (x >> epg_shift) : (x / epg);
+    return magic == 0 ? x : (int)__umulhi((uint32_t)x, magic);
 }
 
 // A token's K expert indices, loaded into registers at kernel entry so the
@@ -71,7 +73,7 @@ struct Inserted {
 // a dynamically indexed private array, i.e. scratch memory.)
 template <int KMAX>
 __device__ __forceinline__ Inserted insert_token(const int (&e)[KMAX], bool live, int K, int E,
-                                                 int epg, int epg_shift,
+                                                 uint32_t gmagic,
                                                  unsigned long long *emask, int wave, int lane)
 {
     const unsigned long long bit = 1ull << lane;
@@ -85,7 +87,7 @@ __device__ __forceinline__ Inserted insert_token(const int (&e)[KMAX], bool live
             const unsigned long long old = atomicOr(&emask[x * kWaves + wave], bit);
             const bool rep = (old & bit) != 0;
             dup |= rep ? 1u << k : 0u;
-            gm |= rep ? 0u : 1u << group_of(x, epg, epg_shift);
+            gm |= rep ? 0u : 1u << group_of(x, gmagic);
         }
     }
     return Inserted{oor, dup, gm};
@@ -93,14 +95,15 @@ __device__ __forceinline__ Inserted insert_token(const int (&e)[KMAX], bool live
 
 // Count kernel: one tile per workgroup. Writes row `tile` of the tile-major
 // count table: E expert counts, G group counts, then the tile's error bits.
-template <int KMAX>
+template <int KMAX, bool EXACT>
 __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
-    const int32_t *__restrict__ idx, int T, int K, int E, int G, int epg, int epg_shift,
+    const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic,
     uint32_t *__restrict__ tok_group_mask, int32_t *__restrict__ table)
 {
     extern __shared__ unsigned long long emask[];   // [E][kWaves]
     __shared__ int gcnt[kMaxG][kWaves];
     __shared__ int s_err;
+    const int K = EXACT ? KMAX : Krt;   // a compile-time constant for the common top-k
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int tile = blockIdx.x;
     const int t = tile * kLayoutTile + tid;
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     if (tid == 0) s_err = 0;
     __syncthreads();
 
-    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, epg, epg_shift, emask, wave, lane);
+    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, gmagic, emask, wave, lane);
     const uint32_t gm = ins.gm;
     const int err = ins.err();
     if (t < T) tok_group_mask[t] = gm;
@@ -180,9 +183,9 @@ __device__ __forceinline__ void column_sums(const int32_t *__restrict__ table, i
 // are rebuilt exactly as the count kernel built them, and each pair's slot is
 // its expert's offset for this (tile, wave) plus its rank among the wave's
 // lanes.
-template <int KMAX>
+template <int KMAX, bool EXACT>
 __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
-    const int32_t *__restrict__ idx, int T, int K, int E, int G, int epg, int epg_shift,
+    const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic,
     int ntiles, const int32_t *__restrict__ table, LayoutPtrs L)
 {
     extern __shared__ unsigned long long emask[];   // [E][kWaves], then int off_e[E][kWaves]
@@ -193,6 +196,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     __shared__ int off_g[kMaxG][kWaves];
     __shared__ uint64_t gball[kMaxG][kWaves];
     __shared__ int s_err;
+    const int K = EXACT ? KMAX : Krt;   // a compile-time constant for the common top-k
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int tile = blockIdx.x;
     const int t = tile * kLayoutTile + tid;
@@ -237,25 +241,29 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
         }
     }
     if (tile == 0 && tid == 0) L.expert_offset[E] = carry;
-    __syncthreads();
-    if (tid == 0) {
-        int off = 0;
-        for (int g = 0; g < G; ++g) {
+    // Group offsets: an exclusive scan over the G <= 32 groups in wave 0.
+    if (wave == 0) {
+        const int gt = lane < G ? tot_g[lane] : 0;
+        int incl = gt;
+#pragma unroll
+        for (int o = 1; o < kMaxG; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane < G) {
+            const int goff = incl - gt;
             if (tile == 0) {
-                L.group_count[g] = tot_g[g];
-                L.group_offset[g] = off;
+                L.group_count[lane] = gt;
+                L.group_offset[lane] = goff;
             }
-            base_g[g] += off;
-            off += tot_g[g];
+            base_g[lane] += goff;
         }
-        if (tile == 0) {
-            L.group_offset[G] = off;
-            *L.status = s_err;
-        }
+        if (tile == 0 && lane == G - 1) L.group_offset[G] = incl;
+        if (tile == 0 && lane == 0) *L.status = s_err;
     }
 
     // Rebuild the tile's LDS words.
-    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, epg, epg_shift, emask, wave, lane);
+    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, gmagic, emask, wave, lane);
     const uint32_t gm = ins.gm, bad = ins.bad();
     for (int g = 0; g < G; ++g) {
         const uint64_t b = __ballot((gm >> g) & 1u);
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
                 const int x = e[k];
                 se = off_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
                 L.recv_src_e[se] = (int32_t)p;
-                const int g = group_of(x, epg, epg_shift);
+                const int g = group_of(x, gmagic);
                 sg = off_g[g][wave] + __popcll(gball[g][wave] & below);
             }
             L.slot_e[p] = se;
@@ -340,17 +348,27 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
     }
     const int ntiles = layout_tiles(T);
     const int epg = E / G;
-    const int epg_shift = (epg & (epg - 1)) == 0 ? __builtin_ctz((unsigned)epg) : -1;
+    const uint32_t gmagic = epg == 1 ? 0u : (uint32_t)((1ull << 32) / (unsigned)epg) + 1u;
     const size_t lds1 = (size_t)E * kWaves * sizeof(unsigned long long);
     const size_t lds2 = lds1 + (size_t)E * kWaves * sizeof(int);
-    auto count = K <= 8 ? layout_count_kernel<8> : layout_count_kernel<32>;
-    auto place = K <= 8 ? layout_place_kernel<8> : layout_place_kernel<32>;
-    hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G, epg,
-                       epg_shift, L.tok_group_mask, ws);
+    using CountFn = void (*)(const int32_t *, int, int, int, int, uint32_t, uint32_t *, int32_t *);
+    using PlaceFn = void (*)(const int32_t *, int, int, int, int, uint32_t, int, const int32_t *, LayoutPtrs);
+    CountFn count;
+    PlaceFn place;
+    switch (K) {
+    case 2: count = layout_count_kernel<2, true>; place = layout_place_kernel<2, true>; break;
+    case 4: count = layout_count_kernel<4, true>; place = layout_place_kernel<4, true>; break;
+    case 8: count = layout_count_kernel<8, true>; place = layout_place_kernel<8, true>; break;
+    default:
+        if (K <= 8) { count = layout_count_kernel<8, false>; place = layout_place_kernel<8, false>; }
+        else { count = layout_count_kernel<32, false>; place = layout_place_kernel<32, false>; }
+    }
+    hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G, gmagic,
+                       L.tok_group_mask, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(place, dim3(ntiles), dim3(kLayoutTile), lds2, stream, idx, T, K, E, G, epg,
-                       epg_shift, ntiles, static_cast<const int32_t *>(ws), L);
+    hipLaunchKernelGGL(place, dim3(ntiles), dim3(kLayoutTile), lds2, stream, idx, T, K, E, G, gmagic,
+                       ntiles, static_cast<const int32_t *>(ws), L);
     return hipGetLastError();
 }
 
