@@ -20,8 +20,9 @@
 // write-allocate L2 made NT stores pay; here a plain streaming store sustains
 // more write bandwidth than an NT one, while NT loads read markedly faster.
 //
-// FP8: each lane holds 16 consecutive elements (two 16-byte loads); the 8
-// lanes of one 128-block reduce amax with three xor-shuffles; every lane then
+// FP8: each lane holds 16 consecutive elements (two 16-byte loads), one chunk
+// per pass, in a workgroup sized to the row; the 8 lanes of one 128-block
+// reduce amax with three xor-shuffles; every lane then
 // forms scale = amax / 448 and inv = 448 / amax (IEEE fp32 divisions, as
 // compiled by default), multiplies, clamps to +-448 (which equals saturating
 // round-to-nearest-even for every finite input) and converts pairs with the
@@ -37,7 +38,7 @@ namespace moe {
 namespace {
 
 constexpr int kDispatchBS = 128;   // threads per workgroup, bf16
-constexpr int kFp8BS = 64;         // threads per workgroup, fp8 (one wave)
+constexpr int kFp8MaxBS = 1024;    // threads per workgroup, fp8: up to one per 16-element chunk
 constexpr int kMaxIter = 8;
 
 template <int ITER, bool NT, bool NTL, bool FULL>
@@ -93,8 +94,11 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
-template <int ITER, bool NT, bool NTL, bool FULL>
-__global__ __launch_bounds__(kFp8BS) void dispatch_fp8_kernel(
+// One 16-element chunk per lane per pass; the workgroup has as many lanes as
+// the row has chunks (rounded up to whole waves, at most kFp8MaxBS), so a
+// lane holds one chunk's state and occupancy stays high.
+template <bool NT, bool NTL, bool FULL>
+__global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, int nch, int K, int nslot, const int32_t *__restrict__ slots,
     const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
     u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, float *__restrict__ recv_w,
@@ -104,61 +108,49 @@ __global__ __launch_bounds__(kFp8BS) void dispatch_fp8_kernel(
     // receive row nch vectors of 16 e4m3 bytes, and nch / 8 scales.
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int bs = blockDim.x;
     const u32x4 *src = x + (size_t)t * nch * 2;
     const int32_t *ts = slots + (size_t)t * nslot;
     const int nblk = nch / 8;
 
-    for (int base = 0; base < nch; base += kFp8BS * ITER) {
-        u32x4 q[ITER];
-        float sc[ITER];
-#pragma unroll
-        for (int i = 0; i < ITER; ++i) {
-            const int j = base + i * kFp8BS + tid;
-            const bool in = FULL || j < nch;
-            u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-            if (in) {
-                a = load16<NTL>(src + 2 * j);
-                b = load16<NTL>(src + 2 * j + 1);
-            }
-            float f[16];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f[2 * m] = bf16_lo(a[m]);
-                f[2 * m + 1] = bf16_hi(a[m]);
-                f[8 + 2 * m] = bf16_lo(b[m]);
-                f[8 + 2 * m + 1] = bf16_hi(b[m]);
-            }
-            float amax = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(f[m]));
-            // the 8 lanes of one 128-element block are lanes 8c .. 8c+7 of the wave
-            amax = fmaxf(amax, __shfl_xor(amax, 1));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
-            amax = fmaxf(amax, __shfl_xor(amax, 4));
-            const float scale = amax / 448.f;
-            const float inv = amax > 0.f ? 448.f / amax : 0.f;
-            int w[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                int p = cvt_pk_e4m3<false>(clamp448(f[4 * m] * inv), clamp448(f[4 * m + 1] * inv), 0);
-                p = cvt_pk_e4m3<true>(clamp448(f[4 * m + 2] * inv), clamp448(f[4 * m + 3] * inv), p);
-                w[m] = p;
-            }
-            q[i] = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
-            sc[i] = scale;
+    for (int j = tid; FULL ? j < nch : j - tid < nch; j += bs) {
+        const bool in = FULL || j < nch;
+        u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+        if (in) {
+            a = load16<NTL>(src + 2 * j);
+            b = load16<NTL>(src + 2 * j + 1);
         }
-        for (int d = 0; d < nslot; ++d) {
-            const int s = ts[d];
-            if (s < 0) continue;
-            u32x4 *dst = recv_q + (size_t)s * nch;
-            float *dsc = recv_scale + (size_t)s * nblk;
+        float f[16];
 #pragma unroll
-            for (int i = 0; i < ITER; ++i) {
-                const int j = base + i * kFp8BS + tid;
-                if (FULL || j < nch) {
-                    store16<NT>(dst + j, q[i]);
-                    if ((tid & 7) == 0) dsc[j >> 3] = sc[i];
-                }
+        for (int m = 0; m < 4; ++m) {
+            f[2 * m] = bf16_lo(a[m]);
+            f[2 * m + 1] = bf16_hi(a[m]);
+            f[8 + 2 * m] = bf16_lo(b[m]);
+            f[8 + 2 * m + 1] = bf16_hi(b[m]);
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(f[m]));
+        // the 8 lanes of one 128-element block are lanes 8c .. 8c+7 of a wave
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        const float scale = amax / 448.f;
+        const float inv = amax > 0.f ? 448.f / amax : 0.f;
+        int w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            int p = cvt_pk_e4m3<false>(clamp448(f[4 * m] * inv), clamp448(f[4 * m + 1] * inv), 0);
+            p = cvt_pk_e4m3<true>(clamp448(f[4 * m + 2] * inv), clamp448(f[4 * m + 3] * inv), p);
+            w[m] = p;
+        }
+        const u32x4 q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+        if (in) {
+            for (int d = 0; d < nslot; ++d) {
+                const int s = ts[d];
+                if (s < 0) continue;
+                store16<NT>(recv_q + (size_t)s * nch + j, q);
+                if ((tid & 7) == 0) recv_scale[(size_t)s * nblk + (j >> 3)] = scale;
             }
         }
     }
@@ -180,10 +172,6 @@ __global__ __launch_bounds__(kFp8BS) void dispatch_fp8_kernel(
 template <int ITER, bool NT, bool NTL, bool FULL>
 struct Bf16Inst {
     static constexpr auto fn = dispatch_bf16_kernel<ITER, NT, NTL, FULL>;
-};
-template <int ITER, bool NT, bool NTL, bool FULL>
-struct Fp8Inst {
-    static constexpr auto fn = dispatch_fp8_kernel<ITER, NT, NTL, FULL>;
 };
 
 template <template <int, bool, bool, bool> class Inst, int ITER>
@@ -255,10 +243,15 @@ hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, co
                                hipStream_t stream)
 {
     const int nch = H / 16;
-    const int iter = iters_for(nch, kFp8BS);
-    const bool full = nch % (kFp8BS * iter) == 0;
-    auto fn = pick<Fp8Inst>(iter, tuning().dispatch_nt_store, tuning().dispatch_nt_load, full);
-    hipLaunchKernelGGL(fn, dim3(T), dim3(kFp8BS), 0, stream, (const u32x4 *)x, nch, K, nslot, slots,
+    int bs = (nch + kWave - 1) / kWave * kWave;
+    if (bs > kFp8MaxBS) bs = kFp8MaxBS;
+    const bool full = nch % bs == 0;
+    const bool nt = tuning().dispatch_nt_store, ntl = tuning().dispatch_nt_load;
+    auto fn = nt ? (ntl ? (full ? dispatch_fp8_kernel<true, true, true> : dispatch_fp8_kernel<true, true, false>)
+                        : (full ? dispatch_fp8_kernel<true, false, true> : dispatch_fp8_kernel<true, false, false>))
+                 : (ntl ? (full ? dispatch_fp8_kernel<false, true, true> : dispatch_fp8_kernel<false, true, false>)
+                        : (full ? dispatch_fp8_kernel<false, false, true> : dispatch_fp8_kernel<false, false, false>));
+    hipLaunchKernelGGL(fn, dim3(T), dim3(bs), 0, stream, (const u32x4 *)x, nch, K, nslot, slots,
                        topk_w, topk_idx, (u32x4 *)recv_q, recv_scale, recv_w, recv_idx);
     return hipGetLastError();
 }
