@@ -360,7 +360,74 @@ def extras(moe, d, dv, args):
     res["fp8_dispatch"] = f8
     del dv8
     torch.cuda.synchronize()
+    res["workloads"] = workload_table(moe)
     return res
+
+
+def workload_table(moe, names=("tiny", "t256", "t4096", "skew", "fp8"), it=30):
+    """Per-workload timings of every call in both receive layouts (median µs over `it`
+    event-timed calls; GB/s = algorithmic bytes / median), plus, for each workload, the
+    per-expert step (layout + dispatch + combine) replayed from a captured HIP graph,
+    which removes the host's launch cost from small workloads."""
+    import numpy as np
+    import torch
+    import synth_inputs as si
+    out = {}
+    for name in names:
+        d = si.make_workload(name)
+        wl = d["workload"]
+        T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K
+        dt = "fp8" if wl.fp8 else "bf16"
+        dv = Dev(moe, d, modes=("expert", "group"), dtype=dt)
+        L = dv.L
+        lay = lambda: moe.moe_layout(dv.idx, E, G, out=L)
+        lay()
+        torch.cuda.synchronize()
+        R, P = int(L.expert_offset[E].item()), int(L.group_offset[G].item())
+        row = {"T": T, "H": H, "E": E, "G": G, "K": K, "routing": wl.routing, "dtype": dt,
+               "layout_us": round(stats(time_calls([lay], it)[0])["median"], 2)}
+        for mode, nrows in (("expert", R), ("group", P)):
+            D = dv.D[mode]
+            disp = lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, mode, dt, out=D)
+            disp()
+            y = moe.moe_fp8_dequant(L, D.recv_x, D.recv_scale, mode) if wl.fp8 else D.recv_x
+            comb = lambda: moe.moe_combine(L, y, dv.w, mode, out=dv.out)
+            comb()
+            td, tc = time_calls([disp, comb], it)
+            bd = sum(dispatch_bytes(T, H, K, G, nrows, mode, fp8=wl.fp8))
+            bc = sum(combine_bytes(T, H, K, nrows))
+            md, mc = stats(td)["median"], stats(tc)["median"]
+            row[mode] = {"rows": nrows, "dispatch_us": round(md, 2), "combine_us": round(mc, 2),
+                         "dispatch_gbs": round(bd / md / 1e3, 1), "combine_gbs": round(bc / mc / 1e3, 1),
+                         "dispatch_frac": round(bd / md / 1e3 / PEAK_HBM_GBS, 4),
+                         "combine_frac": round(bc / mc / 1e3 / PEAK_HBM_GBS, 4),
+                         "dispatch_payload_gbs": round(nrows * H * (1 if wl.fp8 else 2) / md / 1e3, 1)}
+        # HIP-graph replay of the per-expert step
+        De = dv.D["expert"]
+        ye = De.recv_x if not wl.fp8 else None
+        if not wl.fp8:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for _ in range(2):
+                    lay(); moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "expert", dt, out=De)
+                    moe.moe_combine(L, ye, dv.w, "expert", out=dv.out)
+            torch.cuda.current_stream().wait_stream(s)
+            with torch.cuda.graph(g):
+                lay()
+                moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "expert", dt, out=De)
+                moe.moe_combine(L, ye, dv.w, "expert", out=dv.out)
+            g.replay()
+            torch.cuda.synchronize()
+            row["graph_step_us"] = round(stats(time_calls([g.replay], it)[0])["median"], 2)
+            del g
+        out[name] = row
+        del dv, D, De
+        torch.cuda.synchronize()
+    steps = [v["layout_us"] + v["expert"]["dispatch_us"] + v["expert"]["combine_us"] for v in out.values()]
+    out["geomean_step_us_expert"] = round(float(np.exp(np.mean(np.log(steps)))), 2)
+    return out
 
 
 if __name__ == "__main__":

@@ -11,7 +11,8 @@
 //
 // Design. One workgroup per token; each lane owns ITER 16-byte vectors (8
 // elements each) of the output row per pass and keeps their fp32
-// accumulators in registers. For a token whose K slots are all valid (the
+// accumulators in registers (ITER = 2 with the workgroup sized to the row
+// where it divides evenly into waves, which measured best). For a token whose K slots are all valid (the
 // normal case) the rows are read either row by row in contiguous bursts
 // (per-expert layout) or column by column with the next column prefetched
 // (per-group layout, where rows repeat), and folded with one fmaf per element
@@ -27,7 +28,8 @@ namespace moe {
 
 namespace {
 
-constexpr int kCombineBS = 128;
+constexpr int kCombineBS = 128;      // workgroup size of the general shape
+constexpr int kCombineMaxBS = 1024;
 constexpr int kMaxIter = 8;
 
 __device__ __forceinline__ void fma8(float (&acc)[8], float w, u32x4 v)
@@ -51,13 +53,14 @@ __device__ __forceinline__ u32x4 pack8(const float (&acc)[8])
 // and the output is written with plain stores, the faster pair measured on
 // MI355X.
 template <int ITER, int KT, bool ROWWISE, bool FULL>
-__global__ __launch_bounds__(kCombineBS) void combine_kernel(
+__global__ __launch_bounds__(kCombineMaxBS) void combine_kernel(
     const u32x4 *__restrict__ y, int64_t y_rows, int nvec, int K,
     const int32_t *__restrict__ slot, const float *__restrict__ topk_w, u32x4 *__restrict__ out,
     int32_t *__restrict__ status)
 {
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
+    const int bs = blockDim.x;   // a multiple of 64; bs * ITER vectors per pass
     const int32_t *ts = slot + (size_t)t * K;
     const float *tw = topk_w + (size_t)t * K;
     u32x4 *orow = out + (size_t)t * nvec;
@@ -88,7 +91,7 @@ __global__ __launch_bounds__(kCombineBS) void combine_kernel(
                 // row is thus visited in long contiguous bursts, and the fma
                 // chain of every element still runs in k order.
                 const int wave = tid / kWave, lane = tid % kWave;
-                for (int base = 0; base < nvec; base += kCombineBS * ITER) {
+                for (int base = 0; base < nvec; base += bs * ITER) {
                     const int j0 = base + wave * (kWave * ITER) + lane;
                     float acc[ITER][8];
 #pragma unroll
@@ -112,16 +115,16 @@ __global__ __launch_bounds__(kCombineBS) void combine_kernel(
                 // FMAs of pass i, so 2K row loads per lane stay in flight. Used
                 // for the per-group layout, where one token's K slots repeat
                 // rows: the repeats are loaded back to back, while still cached.
-                for (int base = 0; base < nvec; base += kCombineBS * ITER) {
+                for (int base = 0; base < nvec; base += bs * ITER) {
                     u32x4 cur[KT], nxt[KT];
 #pragma unroll
                     for (int k = 0; k < KT; ++k) cur[k] = load16<true>(rows[k] + base + tid);
 #pragma unroll
                     for (int i = 0; i < ITER; ++i) {
-                        const int j = base + i * kCombineBS + tid;
+                        const int j = base + i * bs + tid;
                         if (i + 1 < ITER) {
 #pragma unroll
-                            for (int k = 0; k < KT; ++k) nxt[k] = load16<true>(rows[k] + j + kCombineBS);
+                            for (int k = 0; k < KT; ++k) nxt[k] = load16<true>(rows[k] + j + bs);
                         }
                         float acc[8];
 #pragma unroll
@@ -136,10 +139,10 @@ __global__ __launch_bounds__(kCombineBS) void combine_kernel(
                     }
                 }
             } else {
-                for (int base = 0; base < nvec; base += kCombineBS * ITER) {
+                for (int base = 0; base < nvec; base += bs * ITER) {
 #pragma unroll
                     for (int i = 0; i < ITER; ++i) {
-                        const int j = base + i * kCombineBS + tid;
+                        const int j = base + i * bs + tid;
                         if (FULL || j < nvec) {
                             u32x4 v[KT];
 #pragma unroll
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(kCombineBS) void combine_kernel(
         for (int k = 0; k < K; ++k)
             if (ts[k] >= y_rows) { atomicOr(status, MOE_STATUS_Y_ROWS); break; }
     }
-    for (int j = tid; j < nvec; j += kCombineBS) {
+    for (int j = tid; j < nvec; j += bs) {
         float acc[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) acc[m] = -0.f;
@@ -245,9 +248,19 @@ hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, co
                           bool rows_repeat, const float *topk_w, void *out, int32_t *status,
                           hipStream_t stream)
 {
+    // Shape: two vectors per lane and one workgroup lane per pair of vectors
+    // when the row splits that way into whole waves (e.g. 448 threads at
+    // H = 7168), else 128 threads with up to kMaxIter vectors per lane.
     const int nvec = H / 8;
-    const int iter = iters_for(nvec, kCombineBS);
-    const bool full = nvec % (kCombineBS * iter) == 0;
+    int bs, iter;
+    if (nvec % (2 * kWave) == 0 && nvec / 2 <= kCombineMaxBS) {
+        bs = nvec / 2;
+        iter = 2;
+    } else {
+        bs = kCombineBS;
+        iter = iters_for(nvec, kCombineBS);
+    }
+    const bool full = nvec % (bs * iter) == 0;
     const bool rowwise = !rows_repeat;
     void (*fn)(const u32x4 *, int64_t, int, int, const int32_t *, const float *, u32x4 *, int32_t *);
     switch (K) {
@@ -257,7 +270,7 @@ hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, co
     case 8: fn = pick_iter<8>(iter, rowwise, full); break;
     default: fn = pick_iter<0>(iter, rowwise, full); break;
     }
-    hipLaunchKernelGGL(fn, dim3(T), dim3(kCombineBS), 0, stream, (const u32x4 *)y, y_rows, nvec, K,
+    hipLaunchKernelGGL(fn, dim3(T), dim3(bs), 0, stream, (const u32x4 *)y, y_rows, nvec, K,
                        slot, topk_w, (u32x4 *)out, status);
     return hipGetLastError();
 }
