@@ -51,29 +51,38 @@ def combine_bytes(T, H, K, R):
 
 # ------------------------------------------------------------------ helpers
 
-def source_hash() -> str:
+# Source files that define each timed kernel (plus the shared device helpers).
+KERNEL_SOURCES = {
+    "dispatch": ("dispatch.hip", "common.hpp", "kernels.hpp"),
+    "combine": ("combine.hip", "common.hpp", "kernels.hpp"),
+    "layout": ("layout.hip", "common.hpp", "kernels.hpp"),
+}
+
+
+def source_hash(kernel: str | None = None) -> str:
+    """Hash of the sources of one kernel (or of all kernel sources)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_moe_layout_amd", "csrc")
-    for fn in sorted(os.listdir(csrc)):
+    files = KERNEL_SOURCES[kernel] if kernel else sorted(os.listdir(csrc))
+    for fn in files:
         h.update(fn.encode())
         h.update(open(os.path.join(csrc, fn), "rb").read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key: str):
-    """HBM traffic of a kernel from committed rocprofv3 --pmc counters, if they were
-    taken on the current kernel sources; None otherwise."""
+def load_traffic(kernel: str, key: str):
+    """HBM traffic (bytes per launch) of a kernel from the committed rocprofv3 --pmc
+    counters, if they were taken on that kernel's current sources; None otherwise."""
     p = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(p):
         return None
     try:
-        d = json.load(open(p))
+        k = json.load(open(p)).get("kernels", {}).get(key)
     except ValueError:
         return None
-    if d.get("source_hash") != source_hash():
+    if not k or k.get("source_hash") != source_hash(kernel):
         return None
-    k = d.get("kernels", {}).get(kernel_key)
-    return None if k is None else k.get("traffic_bytes")
+    return k.get("traffic_bytes")
 
 
 def stats(v):
@@ -249,7 +258,7 @@ def main():
     dom = max(kern, key=lambda k: kern[k][1])
     ach = kern[dom][0] / (kern[dom][1] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": load_traffic(f"{dom}_expert_bf16"),
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom, f"{dom}_expert_bf16"),
                 "kernel": f"{dom} (per-expert bf16)", "algorithmic_bytes": kern[dom][0],
                 "avg_us": round(kern[dom][1], 2)}
 
@@ -422,6 +431,26 @@ def workload_table(moe, names=("tiny", "t256", "t4096", "skew", "fp8"), it=30):
             torch.cuda.synchronize()
             row["graph_step_us"] = round(stats(time_calls([g.replay], it)[0])["median"], 2)
             del g
+            if T <= moe.FUSED_MAX_TOKENS and T * K <= moe.FUSED_MAX_PAIRS:
+                # the low-latency form: layout + dispatch in one launch
+                fused = lambda: moe.moe_layout_dispatch(dv.idx, E, G, dv.x, dv.w, "expert", dt,
+                                                        out_layout=L, out=De)
+                fused()
+                row["fused_layout_dispatch_us"] = round(stats(time_calls([fused], it)[0])["median"], 2)
+                g = torch.cuda.CUDAGraph()
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    for _ in range(2):
+                        fused(); moe.moe_combine(L, ye, dv.w, "expert", out=dv.out)
+                torch.cuda.current_stream().wait_stream(s)
+                with torch.cuda.graph(g):
+                    fused()
+                    moe.moe_combine(L, ye, dv.w, "expert", out=dv.out)
+                g.replay()
+                torch.cuda.synchronize()
+                row["graph_step_fused_us"] = round(stats(time_calls([g.replay], it)[0])["median"], 2)
+                del g
         out[name] = row
         del dv, D, De
         torch.cuda.synchronize()

@@ -9,6 +9,7 @@ not pass them.
 The binding names follow the C ABI:
     moe_layout(topk_idx, E, G)                          -> Layout
     moe_dispatch(L, x, topk_w, topk_idx, mode, dtype)   -> Dispatched
+    moe_layout_dispatch(topk_idx, E, G, x, topk_w, mode, dtype) -> (Layout, Dispatched)
     moe_combine(L, y, topk_w, mode)                     -> bf16 [T, H]
     moe_fp8_dequant(L, q, scale, mode)                  -> bf16 [capacity, H]
 If the library is missing this module raises on import; there is no fallback.
@@ -23,6 +24,7 @@ import torch
 
 __all__ = [
     "MoeError", "Layout", "Dispatched", "moe_layout", "moe_dispatch", "moe_combine",
+    "moe_layout_dispatch",
     "moe_fp8_dequant", "moe_ref_copy", "recv_rows_bound", "layout_workspace_bytes",
     "library_path", "MODE_EXPERT", "MODE_GROUP", "DTYPE_BF16", "DTYPE_FP8",
     "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS",
@@ -52,7 +54,7 @@ class _LayoutT(ctypes.Structure):
 def _load_library() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with `python -m combine_moe_layout_amd.build` "
+            f"{_LIB_PATH} is missing: build it with `python combine_moe_layout_amd/build.py` "
             "(or __graft_entry__.build()); there is no fallback path")
     lib = ctypes.CDLL(_LIB_PATH)
     i32, i64, sz = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -64,6 +66,7 @@ def _load_library() -> ctypes.CDLL:
         "moe_layout": (i32, [_P, LP, _P, sz, _P]),
         "moe_dispatch": (i32, [LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, _P, i64, _P]),
         "moe_combine": (i32, [LP, i32, i32, _P, i64, _P, _P, _P]),
+        "moe_layout_dispatch": (i32, [_P, LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, i64, _P]),
         "moe_fp8_dequant": (i32, [LP, i32, i32, _P, _P, _P, i64, _P]),
         "moe_ref_copy": (i32, [_P, _P, i64, _P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
@@ -227,6 +230,34 @@ def moe_dispatch(L: Layout, x: torch.Tensor, topk_w: torch.Tensor, topk_idx: tor
                              _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
                              _stream(stream)), "moe_dispatch")
     return D
+
+
+FUSED_MAX_TOKENS, FUSED_MAX_PAIRS = 512, 16384
+
+
+def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
+                        topk_w: torch.Tensor, mode="expert", dtype="bf16", *,
+                        out_layout: Layout | None = None, out: Dispatched | None = None,
+                        stream=None) -> tuple[Layout, Dispatched]:
+    """moe_layout + moe_dispatch in one launch, for T <= 512 (moe_layout_dispatch)."""
+    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be a contiguous int32 [T, K] tensor")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [T, H] tensor")
+    T, K = topk_idx.shape
+    if topk_w.dtype != torch.float32 or not topk_w.is_contiguous() or tuple(topk_w.shape) != (T, K):
+        raise ValueError("topk_w must be a contiguous fp32 [T, K] tensor")
+    L = out_layout if out_layout is not None else Layout.empty(T, K, E, G, device=topk_idx.device)
+    if (L.T, L.K, L.E, L.G) != (T, K, E, G):
+        raise ValueError("layout buffers were made for other sizes")
+    H = x.shape[1]
+    D = out if out is not None else alloc_dispatch(L, H, mode, dtype, x.device)
+    st = L.struct()
+    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), ctypes.byref(st), _mode(mode), _dtype(dtype), H,
+                                    _ptr(x), _ptr(topk_w), _ptr(D.recv_x), _ptr(D.recv_scale),
+                                    _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
+                                    _stream(stream)), "moe_layout_dispatch")
+    return L, D
 
 
 def moe_combine(L: Layout, y: torch.Tensor, topk_w: torch.Tensor, mode="expert", *,

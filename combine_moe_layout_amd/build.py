@@ -1,6 +1,9 @@
 """Build libmoe_ep.so (the C-ABI library of HIP kernels) in-tree for gfx950.
 
-    python -m combine_moe_layout_amd.build
+    python combine_moe_layout_amd/build.py
+
+(Run it by path, or load it with importlib by path: importing the package
+loads the library, which this script is what creates.)
 
 Each csrc/*.hip file is compiled by hipcc into an object under _build/, and the
 objects are linked into combine_moe_layout_amd/libmoe_ep.so, which the Python

@@ -131,6 +131,34 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
+int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode, int dtype, int H,
+                        const void *x, const float *topk_w, void *recv_x, float *recv_scale,
+                        float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
+                        void *stream)
+{
+    if (int rc = check_layout_ptrs(L)) return rc;
+    if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
+    if (mode != MOE_MODE_EXPERT && mode != MOE_MODE_GROUP) return MOE_ERR_BAD_MODE;
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_B128) return MOE_ERR_BAD_MODE;
+    if (H <= 0 || H % 8 != 0) return MOE_ERR_BAD_SHAPE;
+    if (dtype == MOE_DTYPE_FP8_E4M3_B128 && H % 128 != 0) return MOE_ERR_BAD_SHAPE;
+    if (L->T > MOE_FUSED_MAX_TOKENS || (int64_t)L->T * L->K > MOE_FUSED_MAX_PAIRS)
+        return MOE_ERR_BAD_SHAPE;
+    if (L->T == 0) return moe_layout(topk_idx, L, nullptr, 0, stream);
+    if (!topk_idx || !x || !topk_w || !recv_x || !recv_topk_w || !recv_topk_idx)
+        return MOE_ERR_NULL_PTR;
+    if (dtype == MOE_DTYPE_FP8_E4M3_B128 && !recv_scale) return MOE_ERR_NULL_PTR;
+    if (recv_capacity < rows_bound(L->T, L->K, L->G, mode)) return MOE_ERR_CAPACITY;
+    if (!aligned4(topk_idx) || !aligned16(x) || !aligned16(recv_x) || !aligned4(topk_w) ||
+        !aligned4(recv_topk_w) || !aligned4(recv_topk_idx) || (recv_scale && !aligned4(recv_scale)))
+        return MOE_ERR_MISALIGNED;
+    hipError_t e = moe::launch_layout_dispatch(topk_idx, L->T, L->K, L->E, L->G, ptrs_of(L), mode,
+                                               dtype == MOE_DTYPE_FP8_E4M3_B128, H, x, topk_w, recv_x,
+                                               recv_scale, recv_topk_w, recv_topk_idx,
+                                               (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 int moe_combine(const moe_layout_t *L, int mode, int H, const void *y, int64_t y_rows,
                 const float *topk_w, void *out, void *stream)
 {

@@ -55,4 +55,13 @@ hipError_t launch_fp8_dequant(const void *q, const float *scale, void *y, int64_
 
 hipError_t launch_ref_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream);
 
+// Fused layout + dispatch for small batches (one workgroup per token).
+constexpr int kFusedMaxT = 512;
+constexpr int kFusedMaxPairs = 16384;   // T * K
+size_t fused_lds_bytes(int T, int K, int E, int G);
+hipError_t launch_layout_dispatch(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L,
+                                  int mode, int fp8, int H, const void *x, const float *topk_w,
+                                  void *recv_x, float *recv_scale, float *recv_w, int32_t *recv_idx,
+                                  hipStream_t stream);
+
 }  // namespace moe

@@ -37,6 +37,8 @@ extern "C" {
 #define MOE_MAX_EXPERTS 1024 /* E */
 #define MOE_MAX_GROUPS 32    /* G: a token's groups form one 32-bit mask */
 #define MOE_MAX_TOPK 32      /* K */
+#define MOE_FUSED_MAX_TOKENS 512   /* T for moe_layout_dispatch() */
+#define MOE_FUSED_MAX_PAIRS 16384  /* T * K for moe_layout_dispatch() */
 
 enum moe_error {
     MOE_OK = 0,
@@ -152,6 +154,21 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
                  const float *topk_w, const int32_t *topk_idx, void *recv_x, float *recv_scale,
                  float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
                  void *stream);
+
+/* Low-latency form for small batches: moe_layout() and moe_dispatch() in one
+ * launch. The layout arrays and the receive buffers it writes are, bit for
+ * bit, those the two calls write (layout->status included); no workspace is
+ * needed. One workgroup per token recomputes the routing it needs from the
+ * whole index array, so the cost grows as T^2: limited to
+ * T <= MOE_FUSED_MAX_TOKENS and T * K <= MOE_FUSED_MAX_PAIRS (else
+ * MOE_ERR_BAD_SHAPE). Arguments as for moe_layout() and moe_dispatch().
+ * Source: mori pull request 586, the IntraNodeLL reply in its review thread
+ * (single-pass per-token routing, one block per token, copy fused in; latency
+ * dominates at small token counts). */
+int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode, int dtype, int H,
+                        const void *x, const float *topk_w, void *recv_x, float *recv_scale,
+                        float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
+                        void *stream);
 
 /* Combine: out[t, i] = bf16_rne( acc ), where acc starts at -0 and, for
  * k = 0 .. K-1 in order with slot(t, k) >= 0,

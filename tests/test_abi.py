@@ -12,9 +12,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def moe():
-    from combine_moe_layout_amd import build
-    if build.is_stale():
-        build.build()
+    import __graft_entry__
+    b = __graft_entry__._hip_build_module()
+    if b.is_stale():
+        b.build()
     import combine_moe_layout_amd as m
     return m
 
@@ -108,6 +109,13 @@ def test_host_validation_errors(moe):
     assert d(x=M) == -3 and d(rx=M) == -3
     assert d(x=NULL) == -1
     assert d(Lp=_fake_layout(moe, T=0), x=NULL) == 0
+    # fused layout + dispatch: small batches only
+    f = lambda T=16, K=2, H=2048, cap=32: lib.moe_layout_dispatch(
+        A, ref(_fake_layout(moe, T=T, K=K, E=64, G=8)), 0, 0, H, A, A, A, NULL, A, A, cap, NULL)
+    assert f(T=513, cap=513 * 2) == -2
+    assert f(T=512, K=33) == -2                 # K > 32
+    assert f(T=16, H=12) == -2
+    assert f(T=16, cap=31) == -4
     # combine
     c = lambda mode=0, H=2048, y=A, rows=32, out=A, Lp=L: lib.moe_combine(
         ref(Lp), mode, H, y, rows, A, out, NULL)

@@ -419,3 +419,68 @@ def test_stream_ordering_on_side_stream(moe, orc):
         out = moe.moe_combine(L, D.recv_x, w_d, "group")
     s.synchronize()
     np.testing.assert_array_equal(host_u16(out), d["x"])
+
+
+# ------------------------------------------------------------------ fused layout + dispatch (small batches)
+
+FUSED_SHAPES = [  # (T, H, E, G, K)
+    (1, 8, 8, 8, 2), (16, 2048, 8, 8, 2), (256, 7168, 256, 8, 8), (512, 1024, 64, 8, 8),
+    (300, 520, 16, 4, 3), (100, 1024, 1024, 32, 32), (511, 4096, 128, 1, 8), (77, 2048, 7, 7, 1),
+    (257, 1152, 96, 4, 6),
+]
+
+
+@pytest.mark.parametrize("T,H,E,G,K", FUSED_SHAPES)
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_fused_layout_dispatch_matches_oracle(moe, orc, T, H, E, G, K, mode, dtype):
+    if dtype == "fp8" and H % 128:
+        pytest.skip("FP8 needs H % 128 == 0")
+    d = si.make_inputs(T, H, E, K, seed=7 * T + H + K)
+    idx = d["topk_idx"].copy()
+    if T > 40:
+        idx[T // 3, 0] = E + 3                 # out of range
+        if K > 1:
+            idx[T // 2, 1] = idx[T // 2, 0]    # repeat
+    idx_d = to_dev(idx)
+    x = dev_bf16(d["x"])
+    L = moe.Layout.empty(T, K, E, G)
+    D = moe.alloc_dispatch(L, H, mode, dtype)
+    if dtype == "bf16":
+        D.recv_x.view(torch.int16).fill_(int(CANARY16.astype(np.int16)))
+    else:
+        D.recv_x.fill_(0xA5)
+        D.recv_scale.fill_(-1.5)
+    D.recv_topk_w.fill_(-3.0)
+    D.recv_topk_idx.fill_(-77)
+    L, D = moe.moe_layout_dispatch(idx_d, E, G, x, to_dev(d["topk_w"]), mode, dtype, out_layout=L, out=D)
+    Lo = orc.layout(idx, E, G)
+    check_layout(L, Lo)
+    if dtype == "bf16":
+        Do = orc.dispatch_bf16(Lo, mode, d["x"], d["topk_w"], idx)
+        got = host_u16(D.recv_x)
+        np.testing.assert_array_equal(got[:Do["R"]], Do["recv_x"])
+        assert np.all(got[Do["R"]:] == CANARY16)
+        np.testing.assert_array_equal(D.recv_topk_w.cpu().numpy()[:Do["R"]].view(np.uint32),
+                                      Do["recv_w"].view(np.uint32))
+        np.testing.assert_array_equal(D.recv_topk_idx.cpu().numpy()[:Do["R"]], Do["recv_idx"])
+    else:
+        fp8_check(D, orc.dispatch_fp8(Lo, mode, d["x"], d["topk_w"], idx))
+
+
+def test_fused_layout_dispatch_equals_two_calls(moe):
+    d = workload("t256")
+    wl = d["workload"]
+    idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
+    for mode in MODES:
+        L1 = moe.moe_layout(idx_d, wl.E, wl.G)
+        D1 = moe.moe_dispatch(L1, x_d, w_d, idx_d, mode)
+        L2, D2 = moe.moe_layout_dispatch(idx_d, wl.E, wl.G, x_d, w_d, mode)
+        torch.cuda.synchronize()
+        for n in LAYOUT_ARRAYS + ("tok_group_mask",):
+            assert torch.equal(getattr(L1, n), getattr(L2, n)), n
+        R = int(L1.rows(mode).item())
+        assert torch.equal(D1.recv_x[:R].view(torch.int16), D2.recv_x[:R].view(torch.int16))
+        out1 = moe.moe_combine(L1, D1.recv_x, w_d, mode)
+        out2 = moe.moe_combine(L2, D2.recv_x, w_d, mode)
+        assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
