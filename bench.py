@@ -411,6 +411,17 @@ def workload_table(moe, names=("tiny", "t256", "t4096", "skew", "fp8"), it=30):
                          "dispatch_frac": round(bd / md / 1e3 / PEAK_HBM_GBS, 4),
                          "combine_frac": round(bc / mc / 1e3 / PEAK_HBM_GBS, 4),
                          "dispatch_payload_gbs": round(nrows * H * (1 if wl.fp8 else 2) / md / 1e3, 1)}
+        # receive-side regroup: the per-group arrays -> the per-expert layout
+        Dg, De = dv.D["group"], dv.D["expert"]
+        moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "group", dt, out=Dg)
+        rg = lambda: moe.moe_regroup(L, Dg, out=De)
+        rg()
+        mr = stats(time_calls([rg], it)[0])["median"]
+        row_b = H if wl.fp8 else 2 * H
+        meta = K * 8 + ((H // 128) * 4 if wl.fp8 else 0)
+        br = P * (row_b + meta) + T * (G + 2 * K) * 4 + R * (row_b + meta)
+        row["regroup"] = {"us": round(mr, 2), "gbs": round(br / mr / 1e3, 1),
+                          "frac": round(br / mr / 1e3 / PEAK_HBM_GBS, 4)}
         # HIP-graph replay of the per-expert step
         De = dv.D["expert"]
         ye = De.recv_x if not wl.fp8 else None

@@ -10,6 +10,7 @@ The binding names follow the C ABI:
     moe_layout(topk_idx, E, G)                          -> Layout
     moe_dispatch(L, x, topk_w, topk_idx, mode, dtype)   -> Dispatched
     moe_layout_dispatch(topk_idx, E, G, x, topk_w, mode, dtype) -> (Layout, Dispatched)
+    moe_regroup(L, Dispatched_group)                    -> Dispatched (per-expert)
     moe_combine(L, y, topk_w, mode)                     -> bf16 [T, H]
     moe_fp8_dequant(L, q, scale, mode)                  -> bf16 [capacity, H]
 If the library is missing this module raises on import; there is no fallback.
@@ -24,7 +25,7 @@ import torch
 
 __all__ = [
     "MoeError", "Layout", "Dispatched", "moe_layout", "moe_dispatch", "moe_combine",
-    "moe_layout_dispatch",
+    "moe_layout_dispatch", "moe_regroup",
     "moe_fp8_dequant", "moe_ref_copy", "recv_rows_bound", "layout_workspace_bytes",
     "library_path", "MODE_EXPERT", "MODE_GROUP", "DTYPE_BF16", "DTYPE_FP8",
     "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS",
@@ -67,6 +68,7 @@ def _load_library() -> ctypes.CDLL:
         "moe_dispatch": (i32, [LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, _P, i64, _P]),
         "moe_combine": (i32, [LP, i32, i32, _P, i64, _P, _P, _P]),
         "moe_layout_dispatch": (i32, [_P, LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, i64, _P]),
+        "moe_regroup": (i32, [LP, i32, i32, _P, _P, _P, _P, i64, _P, _P, _P, _P, i64, _P]),
         "moe_fp8_dequant": (i32, [LP, i32, i32, _P, _P, _P, i64, _P]),
         "moe_ref_copy": (i32, [_P, _P, i64, _P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
@@ -97,12 +99,12 @@ def _check(rc: int, where: str) -> None:
 
 
 def _ptr(t: torch.Tensor | None):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return s.cuda_stream
 
 
 def _mode(mode) -> int:
@@ -163,13 +165,23 @@ class Layout:
                    torch.empty(T * min(K, G), **i32), torch.zeros(1, **i32),
                    torch.empty(max(ws, 1), dtype=torch.uint8, device=device))
 
-    def struct(self) -> _LayoutT:
-        return _LayoutT(self.T, self.K, self.E, self.G, *(self._addr(n) for n in (
-            "expert_count", "expert_offset", "group_count", "group_offset", "tok_group_mask",
-            "slot_e", "slot_g", "slot_tg", "recv_src_e", "recv_src_g", "status")))
+    _FIELDS = ("expert_count", "expert_offset", "group_count", "group_offset", "tok_group_mask",
+               "slot_e", "slot_g", "slot_tg", "recv_src_e", "recv_src_g", "status")
 
-    def _addr(self, name: str) -> int:
-        return getattr(self, name).data_ptr()
+    def struct(self) -> _LayoutT:
+        """The moe_layout_t of these tensors (built once; the tensors of a Layout
+        must not be replaced after its first use)."""
+        st = self.__dict__.get("_struct")
+        if st is None:
+            st = _LayoutT(self.T, self.K, self.E, self.G,
+                          *(getattr(self, n).data_ptr() for n in self._FIELDS))
+            self.__dict__["_struct"] = st
+            self.__dict__["_struct_ref"] = ctypes.byref(st)
+        return st
+
+    def ref(self):
+        self.struct()
+        return self.__dict__["_struct_ref"]
 
     def rows(self, mode="expert") -> torch.Tensor:
         """Device scalar tensor: number of receive rows in `mode`."""
@@ -188,8 +200,7 @@ def moe_layout(topk_idx: torch.Tensor, E: int, G: int, *, out: Layout | None = N
     L = out if out is not None else Layout.empty(T, K, E, G, device=topk_idx.device)
     if (L.T, L.K, L.E, L.G) != (T, K, E, G):
         raise ValueError("layout buffers were made for other sizes")
-    st = L.struct()
-    _check(_lib.moe_layout(_ptr(topk_idx), ctypes.byref(st), _ptr(L.workspace),
+    _check(_lib.moe_layout(_ptr(topk_idx), L.ref(), _ptr(L.workspace),
                            L.workspace.numel(), _stream(stream)), "moe_layout")
     return L
 
@@ -224,8 +235,7 @@ def moe_dispatch(L: Layout, x: torch.Tensor, topk_w: torch.Tensor, topk_idx: tor
             raise ValueError("topk_w / topk_idx must be contiguous [T, K] fp32 / int32")
     H = x.shape[1]
     D = out if out is not None else alloc_dispatch(L, H, mode, dtype, x.device)
-    st = L.struct()
-    _check(_lib.moe_dispatch(ctypes.byref(st), _mode(mode), _dtype(dtype), H, _ptr(x),
+    _check(_lib.moe_dispatch(L.ref(), _mode(mode), _dtype(dtype), H, _ptr(x),
                              _ptr(topk_w), _ptr(topk_idx), _ptr(D.recv_x), _ptr(D.recv_scale),
                              _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
                              _stream(stream)), "moe_dispatch")
@@ -252,12 +262,26 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
         raise ValueError("layout buffers were made for other sizes")
     H = x.shape[1]
     D = out if out is not None else alloc_dispatch(L, H, mode, dtype, x.device)
-    st = L.struct()
-    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), ctypes.byref(st), _mode(mode), _dtype(dtype), H,
+    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), L.ref(), _mode(mode), _dtype(dtype), H,
                                     _ptr(x), _ptr(topk_w), _ptr(D.recv_x), _ptr(D.recv_scale),
                                     _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
                                     _stream(stream)), "moe_layout_dispatch")
     return L, D
+
+
+def moe_regroup(L: Layout, Dg: Dispatched, *, out: Dispatched | None = None,
+                stream=None) -> Dispatched:
+    """Per-group receive arrays -> per-expert receive arrays (moe_regroup)."""
+    fp8 = Dg.recv_scale is not None
+    H = Dg.recv_x.shape[1]
+    De = out if out is not None else alloc_dispatch(L, H, "expert", "fp8" if fp8 else "bf16",
+                                                    Dg.recv_x.device)
+    _check(_lib.moe_regroup(L.ref(), DTYPE_FP8 if fp8 else DTYPE_BF16, H, _ptr(Dg.recv_x),
+                            _ptr(Dg.recv_scale), _ptr(Dg.recv_topk_w), _ptr(Dg.recv_topk_idx),
+                            Dg.recv_x.shape[0], _ptr(De.recv_x), _ptr(De.recv_scale),
+                            _ptr(De.recv_topk_w), _ptr(De.recv_topk_idx), De.recv_x.shape[0],
+                            _stream(stream)), "moe_regroup")
+    return De
 
 
 def moe_combine(L: Layout, y: torch.Tensor, topk_w: torch.Tensor, mode="expert", *,
@@ -267,8 +291,7 @@ def moe_combine(L: Layout, y: torch.Tensor, topk_w: torch.Tensor, mode="expert",
         raise ValueError("y must be a contiguous bf16 [rows, H] tensor")
     H = y.shape[1]
     o = out if out is not None else torch.empty((L.T, H), dtype=torch.bfloat16, device=y.device)
-    st = L.struct()
-    _check(_lib.moe_combine(ctypes.byref(st), _mode(mode), H, _ptr(y), y.shape[0], _ptr(topk_w),
+    _check(_lib.moe_combine(L.ref(), _mode(mode), H, _ptr(y), y.shape[0], _ptr(topk_w),
                             _ptr(o), _stream(stream)), "moe_combine")
     return o
 
@@ -278,8 +301,7 @@ def moe_fp8_dequant(L: Layout, q: torch.Tensor, scale: torch.Tensor, mode="exper
     """Identity expert on FP8 receive rows: bf16(decode(q) * scale) (moe_fp8_dequant)."""
     cap, H = q.shape
     y = out if out is not None else torch.empty((cap, H), dtype=torch.bfloat16, device=q.device)
-    st = L.struct()
-    _check(_lib.moe_fp8_dequant(ctypes.byref(st), _mode(mode), H, _ptr(q), _ptr(scale), _ptr(y),
+    _check(_lib.moe_fp8_dequant(L.ref(), _mode(mode), H, _ptr(q), _ptr(scale), _ptr(y),
                                 cap, _stream(stream)), "moe_fp8_dequant")
     return y
 

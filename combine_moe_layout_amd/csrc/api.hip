@@ -159,6 +159,36 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
+int moe_regroup(const moe_layout_t *L, int dtype, int H, const void *recv_g, const float *recv_scale_g,
+                const float *recv_topk_w_g, const int32_t *recv_topk_idx_g, int64_t g_capacity,
+                void *recv_e, float *recv_scale_e, float *recv_topk_w_e, int32_t *recv_topk_idx_e,
+                int64_t e_capacity, void *stream)
+{
+    if (int rc = check_layout_ptrs(L)) return rc;
+    if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_B128) return MOE_ERR_BAD_MODE;
+    const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_B128;
+    if (H <= 0 || H % 8 != 0 || (fp8 && H % 128 != 0)) return MOE_ERR_BAD_SHAPE;
+    if (L->T == 0) return MOE_OK;
+    if (!recv_g || !recv_topk_w_g || !recv_topk_idx_g || !recv_e || !recv_topk_w_e ||
+        !recv_topk_idx_e)
+        return MOE_ERR_NULL_PTR;
+    if (fp8 && (!recv_scale_g || !recv_scale_e)) return MOE_ERR_NULL_PTR;
+    if (g_capacity < rows_bound(L->T, L->K, L->G, MOE_MODE_GROUP) ||
+        e_capacity < rows_bound(L->T, L->K, L->G, MOE_MODE_EXPERT))
+        return MOE_ERR_CAPACITY;
+    if (!aligned16(recv_g) || !aligned16(recv_e) || !aligned4(recv_topk_w_g) ||
+        !aligned4(recv_topk_idx_g) || !aligned4(recv_topk_w_e) || !aligned4(recv_topk_idx_e) ||
+        (fp8 && (!aligned4(recv_scale_g) || !aligned4(recv_scale_e))))
+        return MOE_ERR_MISALIGNED;
+    hipError_t e = moe::launch_regroup(recv_g, fp8 ? H : 2 * H, fp8 ? recv_scale_g : nullptr,
+                                       fp8 ? H / 128 : 0, recv_topk_w_g, recv_topk_idx_g, L->T, L->K,
+                                       L->G, L->group_offset, L->recv_src_g, L->slot_g, L->slot_e, recv_e,
+                                       fp8 ? recv_scale_e : nullptr, recv_topk_w_e, recv_topk_idx_e,
+                                       (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 int moe_combine(const moe_layout_t *L, int mode, int H, const void *y, int64_t y_rows,
                 const float *topk_w, void *out, void *stream)
 {

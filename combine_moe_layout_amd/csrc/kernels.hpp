@@ -55,6 +55,13 @@ hipError_t launch_fp8_dequant(const void *q, const float *scale, void *y, int64_
 
 hipError_t launch_ref_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream);
 
+// Receive-side regroup: per-group rows -> per-expert rows (row_bytes % 16 == 0).
+hipError_t launch_regroup(const void *in_rows, int row_bytes, const float *in_scale, int nscale,
+                          const float *in_w, const int32_t *in_idx, int T, int K, int G,
+                          const int32_t *group_offset, const int32_t *recv_src_g,
+                          const int32_t *slot_g, const int32_t *slot_e, void *out_rows,
+                          float *out_scale, float *out_w, int32_t *out_idx, hipStream_t stream);
+
 // Fused layout + dispatch for small batches (one workgroup per token).
 constexpr int kFusedMaxT = 512;
 constexpr int kFusedMaxPairs = 16384;   // T * K

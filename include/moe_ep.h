@@ -170,6 +170,22 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode
                         float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
                         void *stream);
 
+/* Receive-side regroup: the arrays of a per-group (GROUP) dispatch result ->
+ * the per-expert (EXPERT) layout, i.e. for every EXPERT row r with pair
+ * p = recv_src_e[r]:  out[r, :] = in[slot_g[p], :]  for the row data, the K
+ * weights, the K indices and (FP8) the H/128 scales. The result equals, bit for
+ * bit, moe_dispatch() in EXPERT mode of the same tokens. Each group row is read
+ * once. recv_g: [g_capacity, H] bf16 or e4m3 as `dtype`; recv_scale_*: fp32
+ * [*, H/128] (FP8 only, else NULL); recv_topk_*: [*, K]. g_capacity and
+ * e_capacity must reach the GROUP and EXPERT bounds of moe_recv_rows_bound().
+ * Source: "Optimizing Distributed Inference Kernels for AMD DEVELOPER CHALLENGE
+ * 2025", section 3.1 (the receive kernel copies tokens into per-local-expert
+ * buffers). */
+int moe_regroup(const moe_layout_t *L, int dtype, int H, const void *recv_g, const float *recv_scale_g,
+                const float *recv_topk_w_g, const int32_t *recv_topk_idx_g, int64_t g_capacity,
+                void *recv_e, float *recv_scale_e, float *recv_topk_w_e, int32_t *recv_topk_idx_e,
+                int64_t e_capacity, void *stream);
+
 /* Combine: out[t, i] = bf16_rne( acc ), where acc starts at -0 and, for
  * k = 0 .. K-1 in order with slot(t, k) >= 0,
  *   acc = fmaf(topk_w[t, k], y[slot(t, k), i], acc)        (fp32)

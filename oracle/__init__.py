@@ -73,6 +73,8 @@ def _load():
         lib.oracle_f32_to_bf16_n.restype = None
         lib.oracle_f32_to_e4m3_n.argtypes = [i64, P, P]
         lib.oracle_f32_to_e4m3_n.restype = None
+        lib.oracle_regroup_rows.argtypes = [i64, i64, P, P, P, P]
+        lib.oracle_regroup_rows.restype = None
         _lib = lib
     return _lib
 
@@ -185,6 +187,26 @@ def combine(L: dict, mode: str, y: np.ndarray, topk_w: np.ndarray) -> np.ndarray
     slot = L["slot_e"] if mode == "expert" else L["slot_g"]
     out = np.zeros((T, H), np.uint16)
     _load().oracle_combine(T, K, H, _p(slot), _p(y), _p(w), _p(out))
+    return out
+
+
+def regroup_rows(L: dict, rows_g: np.ndarray) -> np.ndarray:
+    """Per-group receive rows -> per-expert receive rows (any per-row array)."""
+    rows_g = np.ascontiguousarray(rows_g)
+    R = L["R_expert"]
+    out = np.zeros((R,) + rows_g.shape[1:], rows_g.dtype)
+    row_bytes = rows_g.dtype.itemsize * int(np.prod(rows_g.shape[1:], dtype=np.int64))
+    _load().oracle_regroup_rows(R, row_bytes, _p(L["recv_src_e"]), _p(L["slot_g"]), _p(rows_g),
+                                _p(out))
+    return out
+
+
+def regroup(L: dict, D_group: dict) -> dict:
+    """Regroup every array of a per-group dispatch result into the per-expert layout."""
+    out = {"R": L["R_expert"]}
+    for name in ("recv_x", "recv_q", "recv_scale", "recv_w", "recv_idx"):
+        if name in D_group:
+            out[name] = regroup_rows(L, D_group[name])
     return out
 
 

@@ -306,3 +306,22 @@ void oracle_f32_to_e4m3_n(int64_t n, const float *in, uint8_t *out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_e4m3(in[i]);
 }
+
+/* ---------------------------------------------------------------- regroup */
+
+/* Receive-side regroup: rows in the per-group layout -> rows in the per-expert
+ * layout. EXPERT row r holds pair p = recv_src_e[r]; its content is the GROUP
+ * row of that pair, slot_g[p]. Rows are opaque byte strings of row_bytes bytes
+ * (a bf16 hidden row, an e4m3 row, a row of scales or of metadata), so one
+ * function serves every per-row array. Rows r >= R are not touched. */
+void oracle_regroup_rows(int64_t R, int64_t row_bytes, const int32_t *recv_src_e,
+                         const int32_t *slot_g, const void *in_rows, void *out_rows)
+{
+    const unsigned char *in = (const unsigned char *)in_rows;
+    unsigned char *out = (unsigned char *)out_rows;
+    for (int64_t r = 0; r < R; ++r) {
+        int32_t p = recv_src_e[r];
+        int32_t s = slot_g[p];
+        memcpy(out + r * row_bytes, in + (int64_t)s * row_bytes, (size_t)row_bytes);
+    }
+}

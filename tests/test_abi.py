@@ -116,6 +116,14 @@ def test_host_validation_errors(moe):
     assert f(T=512, K=33) == -2                 # K > 32
     assert f(T=16, H=12) == -2
     assert f(T=16, cap=31) == -4
+    # regroup
+    rg = lambda dt=0, H=2048, gcap=32, ecap=32, sc=NULL: lib.moe_regroup(
+        ref(L), dt, H, A, sc, A, A, gcap, A, sc, A, A, ecap, NULL)
+    assert rg(dt=2) == -7
+    assert rg(H=12) == -2
+    assert rg(dt=1, H=1000, sc=A) == -2
+    assert rg(dt=1, H=1024, sc=NULL) == -1
+    assert rg(gcap=31) == -4 and rg(ecap=31) == -4
     # combine
     c = lambda mode=0, H=2048, y=A, rows=32, out=A, Lp=L: lib.moe_combine(
         ref(Lp), mode, H, y, rows, A, out, NULL)

@@ -484,3 +484,71 @@ def test_fused_layout_dispatch_equals_two_calls(moe):
         out1 = moe.moe_combine(L1, D1.recv_x, w_d, mode)
         out2 = moe.moe_combine(L2, D2.recv_x, w_d, mode)
         assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+# ------------------------------------------------------------------ receive-side regroup
+
+REGROUP_SHAPES = [("t256", None), ("skew", None), ("fp8", None), ("tiny", None),
+                  (None, (300, 520, 16, 4, 3)), (None, (129, 1024, 64, 1, 8)), (None, (50, 16392, 64, 8, 8))]
+
+
+@pytest.mark.parametrize("name,shape", REGROUP_SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_regroup_matches_expert_dispatch(moe, orc, name, shape, dtype):
+    if name:
+        d = workload(name)
+        wl = d["workload"]
+        T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K
+        idx = d["topk_idx"]
+    else:
+        T, H, E, G, K = shape
+        d = si.make_inputs(T, H, E, K, seed=T + H)
+        idx = d["topk_idx"].copy()
+        idx[T // 2, 0] = -3                    # an invalid entry is skipped
+    if dtype == "fp8" and H % 128:
+        pytest.skip("FP8 needs H % 128 == 0")
+    idx_d, w_d, x_d = to_dev(idx), to_dev(d["topk_w"]), dev_bf16(d["x"])
+    L = moe.moe_layout(idx_d, E, G)
+    Dg = moe.moe_dispatch(L, x_d, w_d, idx_d, "group", dtype)
+    De = moe.alloc_dispatch(L, H, "expert", dtype)
+    if dtype == "bf16":
+        De.recv_x.view(torch.int16).fill_(int(CANARY16.astype(np.int16)))
+    else:
+        De.recv_x.fill_(0xA5)
+        De.recv_scale.fill_(-1.5)
+    De.recv_topk_w.fill_(-3.0)
+    De.recv_topk_idx.fill_(-77)
+    De = moe.moe_regroup(L, Dg, out=De)
+    Lo = orc.layout(idx, E, G)
+    if dtype == "bf16":
+        Do = orc.dispatch_bf16(Lo, "expert", d["x"], d["topk_w"], idx)
+        got = host_u16(De.recv_x)
+        np.testing.assert_array_equal(got[:Do["R"]], Do["recv_x"])
+        assert np.all(got[Do["R"]:] == CANARY16)
+        np.testing.assert_array_equal(De.recv_topk_idx.cpu().numpy()[:Do["R"]], Do["recv_idx"])
+        np.testing.assert_array_equal(De.recv_topk_w.cpu().numpy()[:Do["R"]].view(np.uint32),
+                                      Do["recv_w"].view(np.uint32))
+    else:
+        fp8_check(De, orc.dispatch_fp8(Lo, "expert", d["x"], d["topk_w"], idx))
+
+
+def test_regroup_of_arbitrary_rows(moe, orc):
+    """Rows that are not a dispatch result: the kernel is the oracle's gather."""
+    T, H, E, G, K = 333, 2048, 48, 6, 5
+    d = si.make_inputs(T, H, E, K, seed=4)
+    idx_d = to_dev(d["topk_idx"])
+    L = moe.moe_layout(idx_d, E, G)
+    Lo = orc.layout(d["topk_idx"], E, G)
+    Dg = moe.alloc_dispatch(L, H, "group")
+    rng = np.random.default_rng(1)
+    rows = rng.integers(0, 1 << 16, size=tuple(Dg.recv_x.shape), dtype=np.uint16)
+    wts = rng.standard_normal(tuple(Dg.recv_topk_w.shape)).astype(np.float32)
+    ids = rng.integers(-5, 99, size=tuple(Dg.recv_topk_idx.shape)).astype(np.int32)
+    Dg.recv_x.copy_(dev_bf16(rows))
+    Dg.recv_topk_w.copy_(to_dev(wts))
+    Dg.recv_topk_idx.copy_(to_dev(ids))
+    De = moe.moe_regroup(L, Dg)
+    R = Lo["R_expert"]
+    np.testing.assert_array_equal(host_u16(De.recv_x)[:R], orc.regroup_rows(Lo, rows))
+    np.testing.assert_array_equal(De.recv_topk_w.cpu().numpy()[:R], orc.regroup_rows(Lo, wts))
+    np.testing.assert_array_equal(De.recv_topk_idx.cpu().numpy()[:R], orc.regroup_rows(Lo, ids))

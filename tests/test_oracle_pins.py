@@ -511,3 +511,38 @@ def test_combine_skips_invalid_entries(orc):
     D = orc.dispatch_bf16(L, "expert", x, w, idx)
     out = bf16_to_float(orc.combine(L, "expert", D["recv_x"], w))
     np.testing.assert_array_equal(out, np.array([[1.0, 2.0], [8.0, -8.0]], np.float32))
+
+
+# ------------------------------------------------------------------ regroup (per-group rows -> per-expert rows)
+
+@pytest.mark.parametrize("name", ["tiny", "t256"])
+def test_regroup_of_group_dispatch_is_expert_dispatch(orc, name):
+    """Composition identity: dispatching per group and regrouping gives, array by
+    array, exactly the per-expert dispatch (bf16 and FP8)."""
+    d = si.make_workload(name)
+    wl = d["workload"]
+    L = orc.layout(d["topk_idx"], wl.E, wl.G)
+    Dg = orc.dispatch_bf16(L, "group", d["x"], d["topk_w"], d["topk_idx"])
+    De = orc.dispatch_bf16(L, "expert", d["x"], d["topk_w"], d["topk_idx"])
+    Rg = orc.regroup(L, Dg)
+    for n in ("recv_x", "recv_w", "recv_idx"):
+        np.testing.assert_array_equal(Rg[n], De[n][:L["R_expert"]], err_msg=n)
+    Dg8 = orc.dispatch_fp8(L, "group", d["x"], d["topk_w"], d["topk_idx"])
+    De8 = orc.dispatch_fp8(L, "expert", d["x"], d["topk_w"], d["topk_idx"])
+    Rg8 = orc.regroup(L, Dg8)
+    for n in ("recv_q", "recv_scale", "recv_w", "recv_idx"):
+        np.testing.assert_array_equal(Rg8[n], De8[n][:L["R_expert"]], err_msg=n)
+
+
+def test_regroup_rows_is_a_gather(orc):
+    """Arbitrary per-group rows: the result is numpy's gather of the rows named by
+    slot_g of each per-expert row's pair; with one group per expert it is the identity."""
+    rng = np.random.default_rng(3)
+    d = si.make_inputs(200, 8, 32, 5, seed=8)
+    L = orc.layout(d["topk_idx"], 32, 4)
+    rows = rng.integers(0, 1 << 16, size=(L["R_group"], 24), dtype=np.uint16)
+    got = orc.regroup_rows(L, rows)
+    np.testing.assert_array_equal(got, rows[L["slot_g"][L["recv_src_e"][:L["R_expert"]]]])
+    L1 = orc.layout(d["topk_idx"], 32, 32)
+    rows1 = rng.integers(0, 1 << 16, size=(L1["R_group"], 8), dtype=np.uint16)
+    np.testing.assert_array_equal(orc.regroup_rows(L1, rows1), rows1)
