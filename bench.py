@@ -422,6 +422,20 @@ def workload_table(moe, names=("tiny", "t256", "t4096", "skew", "fp8"), it=30):
         br = P * (row_b + meta) + T * (G + 2 * K) * 4 + R * (row_b + meta)
         row["regroup"] = {"us": round(mr, 2), "gbs": round(br / mr / 1e3, 1),
                           "frac": round(br / mr / 1e3 / PEAK_HBM_GBS, 4)}
+        # per-expert FP8 cast + padded transpose of the per-expert rows (bf16 workloads)
+        if not wl.fp8 and H % 64 == 0:
+            moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "expert", dt, out=De)
+            sc = torch.full((E,), 64.0, dtype=torch.float32, device="cuda")
+            am = torch.zeros(E, dtype=torch.float32, device="cuda")
+            CT = moe.moe_cast_transpose_fp8(L, De.recv_x, sc, amax=am)
+            ctf = lambda: moe.moe_cast_transpose_fp8(L, De.recv_x, sc, out=CT)
+            torch.cuda.synchronize()
+            mct = stats(time_calls([ctf], it)[0])["median"]
+            npad = int(CT.pad_offset[E].item())
+            bct = R * H * 2 + R * H + npad * H + (E + 1) * 4 * 2 + E * 8
+            row["cast_transpose"] = {"us": round(mct, 2), "gbs": round(bct / mct / 1e3, 1),
+                                     "frac": round(bct / mct / 1e3 / PEAK_HBM_GBS, 4)}
+            del CT
         # HIP-graph replay of the per-expert step
         De = dv.D["expert"]
         ye = De.recv_x if not wl.fp8 else None

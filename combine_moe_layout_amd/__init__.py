@@ -11,6 +11,7 @@ The binding names follow the C ABI:
     moe_dispatch(L, x, topk_w, topk_idx, mode, dtype)   -> Dispatched
     moe_layout_dispatch(topk_idx, E, G, x, topk_w, mode, dtype) -> (Layout, Dispatched)
     moe_regroup(L, Dispatched_group)                    -> Dispatched (per-expert)
+    moe_cast_transpose_fp8(L, x_expert, scale)          -> CastTransposed
     moe_combine(L, y, topk_w, mode)                     -> bf16 [T, H]
     moe_fp8_dequant(L, q, scale, mode)                  -> bf16 [capacity, H]
 If the library is missing this module raises on import; there is no fallback.
@@ -25,7 +26,7 @@ import torch
 
 __all__ = [
     "MoeError", "Layout", "Dispatched", "moe_layout", "moe_dispatch", "moe_combine",
-    "moe_layout_dispatch", "moe_regroup",
+    "moe_layout_dispatch", "moe_regroup", "moe_cast_transpose_fp8", "CastTransposed",
     "moe_fp8_dequant", "moe_ref_copy", "recv_rows_bound", "layout_workspace_bytes",
     "library_path", "MODE_EXPERT", "MODE_GROUP", "DTYPE_BF16", "DTYPE_FP8",
     "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS",
@@ -69,6 +70,8 @@ def _load_library() -> ctypes.CDLL:
         "moe_combine": (i32, [LP, i32, i32, _P, i64, _P, _P, _P]),
         "moe_layout_dispatch": (i32, [_P, LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, i64, _P]),
         "moe_regroup": (i32, [LP, i32, i32, _P, _P, _P, _P, i64, _P, _P, _P, _P, i64, _P]),
+        "moe_cast_transpose_t_bytes": (i64, [i32, i32, i32, i32]),
+        "moe_cast_transpose_fp8": (i32, [LP, i32, _P, i64, _P, _P, _P, i64, _P, _P, _P]),
         "moe_fp8_dequant": (i32, [LP, i32, i32, _P, _P, _P, i64, _P]),
         "moe_ref_copy": (i32, [_P, _P, i64, _P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
@@ -282,6 +285,41 @@ def moe_regroup(L: Layout, Dg: Dispatched, *, out: Dispatched | None = None,
                             _ptr(De.recv_topk_w), _ptr(De.recv_topk_idx), De.recv_x.shape[0],
                             _stream(stream)), "moe_regroup")
     return De
+
+
+@dataclasses.dataclass
+class CastTransposed:
+    c: torch.Tensor            # uint8 [rows, H]: e4m3 of x * scale[e] in the receive layout
+    t: torch.Tensor            # uint8 [bytes]: T_e = [H, n_e padded to 16] at H * pad_offset[e]
+    amax: torch.Tensor         # fp32 [E]
+    pad_offset: torch.Tensor   # int32 [E + 1]
+
+    def t_expert(self, e: int) -> torch.Tensor:
+        """T_e as a [H, padded rows] uint8 view (synchronises to read pad_offset)."""
+        po = self.pad_offset.cpu()
+        H = self.c.shape[1]
+        return self.t[H * int(po[e]):H * int(po[e + 1])].view(H, -1)
+
+
+def moe_cast_transpose_fp8(L: Layout, x: torch.Tensor, scale: torch.Tensor, *,
+                           amax: torch.Tensor | None = None, out: CastTransposed | None = None,
+                           stream=None) -> CastTransposed:
+    """Per-expert FP8 cast + padded transpose of per-expert bf16 rows (moe_cast_transpose_fp8)."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [rows, H] tensor (per-expert layout)")
+    rows, H = x.shape
+    nb = _lib.moe_cast_transpose_t_bytes(L.T, L.K, L.E, H)
+    if nb < 0:
+        raise MoeError(int(nb), "moe_cast_transpose_t_bytes")
+    if out is None:
+        out = CastTransposed(torch.empty((rows, H), dtype=torch.uint8, device=x.device),
+                             torch.empty(max(nb, 16), dtype=torch.uint8, device=x.device),
+                             amax if amax is not None else torch.zeros(L.E, dtype=torch.float32, device=x.device),
+                             torch.empty(L.E + 1, dtype=torch.int32, device=x.device))
+    _check(_lib.moe_cast_transpose_fp8(L.ref(), H, _ptr(x), rows, _ptr(scale), _ptr(out.c), _ptr(out.t),
+                                       out.t.numel(), _ptr(out.amax), _ptr(out.pad_offset),
+                                       _stream(stream)), "moe_cast_transpose_fp8")
+    return out
 
 
 def moe_combine(L: Layout, y: torch.Tensor, topk_w: torch.Tensor, mode="expert", *,

@@ -189,6 +189,30 @@ int moe_regroup(const moe_layout_t *L, int dtype, int H, const void *recv_g, con
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
+int64_t moe_cast_transpose_t_bytes(int T, int K, int E, int H)
+{
+    if (T < 0 || K < 1 || E < 1 || E > MOE_MAX_EXPERTS || H <= 0 || H % 64 != 0) return MOE_ERR_BAD_SHAPE;
+    return moe::cast_transpose_t_bound((int64_t)T * K, E, H);
+}
+
+int moe_cast_transpose_fp8(const moe_layout_t *L, int H, const void *x, int64_t x_rows,
+                           const float *scale, void *c_out, void *t_out, int64_t t_bytes, float *amax,
+                           int32_t *pad_offset, void *stream)
+{
+    if (int rc = check_layout_ptrs(L)) return rc;
+    if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
+    if (H <= 0 || H % 64 != 0) return MOE_ERR_BAD_SHAPE;
+    if (!x || !scale || !c_out || !t_out || !amax || !pad_offset) return MOE_ERR_NULL_PTR;
+    const int64_t bound = (int64_t)L->T * L->K;
+    if (x_rows < bound || t_bytes < moe::cast_transpose_t_bound(bound, L->E, H)) return MOE_ERR_CAPACITY;
+    if (!aligned16(x) || !aligned16(c_out) || !aligned16(t_out) || !aligned4(scale) || !aligned4(amax) ||
+        !aligned4(pad_offset))
+        return MOE_ERR_MISALIGNED;
+    hipError_t e = moe::launch_cast_transpose(x, bound, H, L->E, L->expert_offset, scale, c_out, t_out,
+                                              amax, pad_offset, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
 int moe_combine(const moe_layout_t *L, int mode, int H, const void *y, int64_t y_rows,
                 const float *topk_w, void *out, void *stream)
 {

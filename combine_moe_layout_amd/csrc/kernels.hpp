@@ -62,6 +62,12 @@ hipError_t launch_regroup(const void *in_rows, int row_bytes, const float *in_sc
                           const int32_t *slot_g, const int32_t *slot_e, void *out_rows,
                           float *out_scale, float *out_w, int32_t *out_idx, hipStream_t stream);
 
+// Per-expert FP8 cast + padded transpose.
+int64_t cast_transpose_t_bound(int64_t rows, int E, int H);
+hipError_t launch_cast_transpose(const void *x, int64_t rows_bound, int H, int E,
+                                 const int32_t *expert_offset, const float *scale, void *c_out,
+                                 void *t_out, float *amax, int32_t *pad_offset, hipStream_t stream);
+
 // Fused layout + dispatch for small batches (one workgroup per token).
 constexpr int kFusedMaxT = 512;
 constexpr int kFusedMaxPairs = 16384;   // T * K

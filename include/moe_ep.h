@@ -186,6 +186,28 @@ int moe_regroup(const moe_layout_t *L, int dtype, int H, const void *recv_g, con
                 void *recv_e, float *recv_scale_e, float *recv_topk_w_e, int32_t *recv_topk_idx_e,
                 int64_t e_capacity, void *stream);
 
+/* Per-expert FP8 cast + transpose of per-expert (EXPERT layout) bf16 rows x,
+ * the inputs of an FP8 expert GEMM and of its transposed (weight-gradient)
+ * GEMM. For each expert e, rows [o, o + n) with o = expert_offset[e],
+ * n = expert_count[e], and its scale s = scale[e]:
+ *   c_out[r, i]   = e4m3fn_rne_satfinite(x[r, i] * s)            (fp32 multiply)
+ *   T_e[i, j]     = c_out[o + j, i] for j < n, 0 for n <= j < np, np = n rounded up to 16
+ *   amax[e]       = max(amax[e], max |x[r, i]| over the expert's rows)
+ * T_e is a row-major [H, np] byte matrix at t_out + H * pad_offset[e], where the
+ * call writes pad_offset[e] = sum of np over experts before e (pad_offset[E] =
+ * total). amax is max-accumulated: it must hold non-negative values (zero it
+ * for a fresh maximum). x: bf16 [x_rows, H], x_rows >= T*K; c_out: uint8
+ * [x_rows, H]; t_out: at least moe_cast_transpose_t_bytes() bytes; H % 64 == 0.
+ * Rows of c_out beyond expert_offset[E] are not written.
+ * Source: "Optimized rocm specific multicast transpose kernel"
+ * (ROCm/TransformerEngine pull request 586), Change Summary: both outputs from
+ * one read with amax fused in, packed FP8 conversion, all experts in one launch,
+ * row counts padded to 16. */
+int64_t moe_cast_transpose_t_bytes(int T, int K, int E, int H);
+int moe_cast_transpose_fp8(const moe_layout_t *L, int H, const void *x, int64_t x_rows,
+                           const float *scale, void *c_out, void *t_out, int64_t t_bytes, float *amax,
+                           int32_t *pad_offset, void *stream);
+
 /* Combine: out[t, i] = bf16_rne( acc ), where acc starts at -0 and, for
  * k = 0 .. K-1 in order with slot(t, k) >= 0,
  *   acc = fmaf(topk_w[t, k], y[slot(t, k), i], acc)        (fp32)

@@ -75,6 +75,8 @@ def _load():
         lib.oracle_f32_to_e4m3_n.restype = None
         lib.oracle_regroup_rows.argtypes = [i64, i64, P, P, P, P]
         lib.oracle_regroup_rows.restype = None
+        lib.oracle_cast_transpose_fp8.argtypes = [i32, i32, P, P, P, P, P, P, P]
+        lib.oracle_cast_transpose_fp8.restype = None
         _lib = lib
     return _lib
 
@@ -208,6 +210,25 @@ def regroup(L: dict, D_group: dict) -> dict:
         if name in D_group:
             out[name] = regroup_rows(L, D_group[name])
     return out
+
+
+def cast_transpose_fp8(expert_offset: np.ndarray, x: np.ndarray, scale: np.ndarray,
+                       amax_in: np.ndarray | None = None) -> dict:
+    """Per-expert FP8 cast + padded transpose of per-expert rows x (bf16 bits [R, H])."""
+    off = _c(expert_offset, np.int32)
+    E = off.shape[0] - 1
+    x = _c(x, np.uint16)
+    H = x.shape[1]
+    R = int(off[E])
+    counts = np.diff(off)
+    tot = int(((counts + 15) // 16 * 16).sum())
+    c = np.zeros((max(R, x.shape[0]), H), np.uint8)
+    t = np.zeros(tot * H, np.uint8)
+    amax = np.zeros(E, np.float32) if amax_in is None else _c(amax_in, np.float32).copy()
+    po = np.zeros(E + 1, np.int32)
+    _load().oracle_cast_transpose_fp8(E, H, _p(off), _p(x), _p(_c(scale, np.float32)), _p(c), _p(t),
+                                      _p(amax), _p(po))
+    return {"c": c[:R], "t": t, "amax": amax, "pad_offset": po}
 
 
 # scalar codecs, exposed for exhaustive tests

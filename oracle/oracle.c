@@ -325,3 +325,38 @@ void oracle_regroup_rows(int64_t R, int64_t row_bytes, const int32_t *recv_src_e
         memcpy(out + r * row_bytes, in + (int64_t)s * row_bytes, (size_t)row_bytes);
     }
 }
+
+/* ---------------------------------------------------------------- per-expert FP8 cast + transpose */
+
+/* For each expert e with rows [o, o + n) of the per-expert layout (o =
+ * expert_offset[e], n = expert_offset[e+1] - o) and its scale s = scale[e]:
+ *   C[r, i]           = e4m3fn_rne_satfinite(x[r, i] * s)        (fp32 multiply)
+ *   T_e[i, j]         = C[o + j, i] for j < n, 0 for n <= j < np, np = n rounded up to 16
+ *   amax[e]           = max(amax[e], max |x[r, i]| over the expert's rows)
+ * T_e is a row-major [H, np] byte matrix stored at t_out + H * po[e], with
+ * po[e] = sum over e' < e of np(e'); pad_offset[e] = po[e], pad_offset[E] = total. */
+void oracle_cast_transpose_fp8(int E, int H, const int32_t *expert_offset, const uint16_t *x,
+                               const float *scale, uint8_t *c_out, uint8_t *t_out, float *amax,
+                               int32_t *pad_offset)
+{
+    int64_t po = 0;
+    for (int e = 0; e < E; ++e) {
+        int64_t o = expert_offset[e], n = expert_offset[e + 1] - o;
+        int64_t np = (n + 15) / 16 * 16;
+        pad_offset[e] = (int32_t)po;
+        float a = amax[e];
+        for (int64_t r = o; r < o + n; ++r)
+            for (int i = 0; i < H; ++i) {
+                float v = oracle_bf16_to_f32(x[r * H + i]);
+                if (fabsf(v) > a) a = fabsf(v);
+                uint8_t q = oracle_f32_to_e4m3(v * scale[e]);
+                c_out[r * H + i] = q;
+                t_out[(int64_t)H * po + (int64_t)i * np + (r - o)] = q;
+            }
+        for (int i = 0; i < H; ++i)
+            for (int64_t j = n; j < np; ++j) t_out[(int64_t)H * po + (int64_t)i * np + j] = 0;
+        amax[e] = a;
+        po += np;
+    }
+    pad_offset[E] = (int32_t)po;
+}

@@ -552,3 +552,37 @@ def test_regroup_of_arbitrary_rows(moe, orc):
     np.testing.assert_array_equal(host_u16(De.recv_x)[:R], orc.regroup_rows(Lo, rows))
     np.testing.assert_array_equal(De.recv_topk_w.cpu().numpy()[:R], orc.regroup_rows(Lo, wts))
     np.testing.assert_array_equal(De.recv_topk_idx.cpu().numpy()[:R], orc.regroup_rows(Lo, ids))
+
+
+# ------------------------------------------------------------------ per-expert FP8 cast + transpose
+
+CT_CASES = [("t256", None), ("t4096", None), ("skew", None), ("tiny", None),
+            (None, (300, 640, 16, 4, 3)), (None, (1000, 64, 1024, 32, 1)), (None, (37, 1024, 8, 1, 8))]
+
+
+@pytest.mark.parametrize("name,shape", CT_CASES)
+def test_cast_transpose_matches_oracle(moe, orc, name, shape):
+    if name:
+        d = workload(name)
+        wl = d["workload"]
+        T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K
+    else:
+        T, H, E, G, K = shape
+        d = si.make_inputs(T, H, E, K, seed=3 * T + H)
+    idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
+    L = moe.moe_layout(idx_d, E, G)
+    D = moe.moe_dispatch(L, x_d, w_d, idx_d, "expert")
+    rng = np.random.default_rng(T + E)
+    scale = rng.uniform(0.25, 300.0, E).astype(np.float32)     # large scales saturate
+    amax0 = (rng.random(E) * 3).astype(np.float32)              # accumulates into these
+    CT = moe.moe_cast_transpose_fp8(L, D.recv_x, to_dev(scale), amax=to_dev(amax0))
+    torch.cuda.synchronize()
+    Lo = orc.layout(d["topk_idx"], E, G)
+    De = orc.dispatch_bf16(Lo, "expert", d["x"], d["topk_w"], d["topk_idx"])
+    ref = orc.cast_transpose_fp8(Lo["expert_offset"], De["recv_x"], scale, amax_in=amax0)
+    np.testing.assert_array_equal(CT.pad_offset.cpu().numpy(), ref["pad_offset"])
+    R = Lo["R_expert"]
+    np.testing.assert_array_equal(CT.c[:R].cpu().numpy(), ref["c"])
+    nt = H * int(ref["pad_offset"][-1])
+    np.testing.assert_array_equal(CT.t[:nt].cpu().numpy(), ref["t"])
+    np.testing.assert_array_equal(CT.amax.cpu().numpy().view(np.uint32), ref["amax"].view(np.uint32))

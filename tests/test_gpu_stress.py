@@ -1,6 +1,8 @@
 """Random-shape stress: 200 rounds, each a random routing problem run through every
-call of the library and compared with the oracle (bit-exact; combine to the same
-bar as the parity tests). Shapes stay small so a round takes milliseconds."""
+call of the library (layout, dispatch or the fused small-batch call, dequant,
+regroup, per-expert cast + transpose, combine) and compared with the oracle
+(bit-exact; combine to the same bar as the parity tests). Shapes stay small so a
+round takes milliseconds."""
 import numpy as np
 import pytest
 import torch
@@ -96,6 +98,16 @@ def test_random_rounds(libs):
             ref = orc.regroup(Lo, {"recv_x": Do.get("recv_x", Do.get("recv_q"))})
             got = De.recv_x[:Re].cpu().numpy() if fp8 else _bits(De.recv_x)[:Re]
             assert np.array_equal(got, ref["recv_x"]), case
+        if mode == "expert" and not fp8 and H % 64 == 0:   # per-expert FP8 cast + transpose
+            scale = rng.uniform(0.25, 300.0, E).astype(np.float32)
+            CT = moe.moe_cast_transpose_fp8(L, D.recv_x, torch.from_numpy(scale).cuda())
+            ref = orc.cast_transpose_fp8(Lo["expert_offset"], Do["recv_x"], scale)
+            assert np.array_equal(CT.pad_offset.cpu().numpy(), ref["pad_offset"]), case
+            assert np.array_equal(CT.c[:R].cpu().numpy(), ref["c"]), case
+            nt = H * int(ref["pad_offset"][-1])
+            assert np.array_equal(CT.t[:nt].cpu().numpy(), ref["t"]), case
+            assert np.array_equal(CT.amax.cpu().numpy().view(np.uint32),
+                                  ref["amax"].view(np.uint32)), case
         # combine with random non-identity weights
         w2 = (rng.standard_normal((T, K)) * 1.5).astype(np.float32)
         out = moe.moe_combine(L, y, torch.from_numpy(w2).cuda(), mode)

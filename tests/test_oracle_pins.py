@@ -546,3 +546,45 @@ def test_regroup_rows_is_a_gather(orc):
     L1 = orc.layout(d["topk_idx"], 32, 32)
     rows1 = rng.integers(0, 1 << 16, size=(L1["R_group"], 8), dtype=np.uint16)
     np.testing.assert_array_equal(orc.regroup_rows(L1, rows1), rows1)
+
+
+# ------------------------------------------------------------------ per-expert FP8 cast + transpose
+
+def test_cast_transpose_against_library_routes(orc):
+    """C is torch's e4m3fn cast of x*scale (where it does not saturate), each T_e is
+    numpy's transpose of the expert's C rows followed by zero padding to 16 columns,
+    and amax is numpy's max |x| per expert."""
+    rng = np.random.default_rng(11)
+    T, H, E, G, K = 150, 256, 12, 4, 3
+    d = si.make_inputs(T, H, E, K, seed=12)
+    L = orc.layout(d["topk_idx"], E, G)
+    De = orc.dispatch_bf16(L, "expert", d["x"], d["topk_w"], d["topk_idx"])
+    scale = rng.uniform(0.5, 40.0, E).astype(np.float32)
+    out = orc.cast_transpose_fp8(L["expert_offset"], De["recv_x"], scale)
+    xf = bf16_to_float(De["recv_x"])
+    off = L["expert_offset"]
+    for e in range(E):
+        rows = slice(off[e], off[e + 1])
+        n = off[e + 1] - off[e]
+        prod = (xf[rows] * scale[e]).astype(np.float32)
+        ok = np.abs(prod) <= 448
+        ref = torch.from_numpy(np.clip(prod, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(out["c"][rows][ok], ref[ok])
+        assert np.all(out["c"][rows][~ok] & 0x7F == 0x7E)          # saturated to +-448
+        npad = (n + 15) // 16 * 16
+        assert out["pad_offset"][e + 1] - out["pad_offset"][e] == npad
+        te = out["t"][H * out["pad_offset"][e]:H * out["pad_offset"][e + 1]].reshape(H, npad)
+        np.testing.assert_array_equal(te[:, :n], out["c"][rows].T)
+        assert np.all(te[:, n:] == 0)
+        assert out["amax"][e] == (np.abs(xf[rows]).max() if n else 0.0)
+
+
+def test_cast_transpose_amax_accumulates_and_scale_one_is_exact(orc):
+    off = np.array([0, 3, 3, 5], np.int32)                    # an expert with no rows
+    vals = np.array([1.0, -0.5, 448.0, 2.0 ** -9, 0.0, 96.0, -240.0, 1.125], np.float32)
+    x = bf16_bits_of(np.resize(vals, (5, 16)))
+    out = orc.cast_transpose_fp8(off, x, np.ones(3, np.float32), amax_in=np.array([1000, 7, 0], np.float32))
+    codes = np.array([orc.f32_to_e4m3(float(v)) for v in np.resize(vals, (5, 16)).ravel()], np.uint8)
+    np.testing.assert_array_equal(out["c"].ravel(), codes)
+    np.testing.assert_array_equal(out["amax"], np.array([1000, 7, 448], np.float32))
+    assert list(out["pad_offset"]) == [0, 16, 16, 32]
