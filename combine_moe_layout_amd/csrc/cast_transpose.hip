@@ -7,18 +7,22 @@
 // fused into the conversion, packed e4m3 conversions, 128-bit loads, all
 // experts in one launch, edge tiles predicated per row with rows padded to 16.
 //
-// Design. A workgroup (256 threads) owns a 128-row tile of one expert (tiles
-// never straddle experts, so T_e's rows are contiguous within a tile) and
-// walks 512 columns in tiles of kCtCols. For each (4 consecutive rows x 8
-// columns) item a thread loads four 16-byte chunks, converts them, stores
-// four 8-byte runs of C, and packs each column's 4 bytes into one 32-bit word
-// written to an LDS tile [kCtCols columns][32 words + 1] (the pad spreads the
-// writes over the banks).
-// After a barrier each thread reads 16 rows of a column (4 words) and stores
-// them as one 16-byte run of T_e; padding rows come from zero inputs. The
-// workgroup finds its expert from a scan of per-expert tile counts over all
-// experts (E <= 1024) and a binary search. Bound by HBM: 2 bytes read and 2
-// written per element.
+// Design. A workgroup (256 threads) owns a tile of up to 128 rows of one
+// expert (tiles never straddle experts, so T_e's rows are contiguous within a
+// tile) and the 512 columns of one column group. Threads work on items of 4
+// consecutive rows x 8 columns (four 16-byte loads); the tile's padded row
+// count picks the shape of a pass: Q row quads (4..32, the power of two that
+// covers the rows) by 256/Q column chunks, so a tile of 16 rows covers its 512
+// columns in one pass and a full tile takes eight passes of 64 columns. Each
+// thread converts its item, stores four 8-byte runs of C, and packs each
+// column's 4 bytes into one 32-bit word of an LDS tile [columns][Q + 1 words]
+// (column c also shifted by c/8 words, which spreads a wave's writes over the
+// banks). After a barrier each thread reads 16 rows of a column (4 words) and
+// stores them as one 16-byte run of T_e; padding rows come from zero inputs.
+// The loads of pass k+1 are issued before pass k is converted, and the LDS
+// tile is double-buffered, so one barrier per pass suffices. The workgroup
+// finds its expert from a scan of per-expert tile counts over all experts
+// (E <= 1024). Bound by HBM: 2 bytes read and 2 written per element.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,15 +31,14 @@ namespace moe {
 namespace {
 
 constexpr int kCtBS = 256;
-constexpr int kCtRows = 128;
-constexpr int kCtCols = 64;              // H is a multiple of 64
-constexpr int kCtChunks = kCtCols / 8;   // 16-byte input chunks per tile row
-constexpr int kCtItems = (kCtRows / 4) * kCtChunks / kCtBS;   // (row quad, chunk) items per thread
-constexpr int kCtRuns = kCtCols * (kCtRows / 16) / kCtBS;     // 16-row runs of T per thread
-constexpr int kCtColTiles = 512 / kCtCols;                     // column tiles per workgroup
+constexpr int kCtRows = 128;        // rows per tile
+constexpr int kCtGroupCols = 512;   // columns per workgroup
 constexpr int kCtWaves = kCtBS / kWave;
-constexpr int kCtStride = kCtRows / 4 + 1;   // LDS words per column (+1 pad)
-constexpr int kMaxE = 1024;
+constexpr int kMaxE = 1024;                          // the library's expert limit
+constexpr int kCtEpt = (kMaxE + kCtBS - 1) / kCtBS;   // experts per thread in the scan
+// LDS words of one tile buffer: max over Q in {4, 8, 16, 32} of
+// (2048 / Q) columns x (Q + 1) words, plus the c/8 shift
+constexpr int kCtLdsWords = 512 * 5 + 64;
 
 template <bool HI>
 __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
@@ -45,27 +48,36 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
-// Exclusive scan over the 256 threads; *total gets the sum.
-__device__ __forceinline__ int ct_scan(int v, int *s, int *total)
+// Exclusive scan of two values over the 256 threads, with both totals.
+__device__ __forceinline__ void ct_scan2(int va, int vb, int *s, int &ea, int &eb, int &ta, int &tb)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    int x = v;
+    int xa = va, xb = vb;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
+        const int ya = __shfl_up(xa, o), yb = __shfl_up(xb, o);
+        if (lane >= o) {
+            xa += ya;
+            xb += yb;
+        }
+    }
+    if (lane == kWave - 1) {
+        s[wave] = xa;
+        s[kCtWaves + wave] = xb;
     }
     __syncthreads();
-    if (lane == kWave - 1) s[wave] = x;
-    __syncthreads();
-    int base = 0, all = 0;
+    int ba = 0, bb = 0;
+    ta = 0;
+    tb = 0;
 #pragma unroll
     for (int w = 0; w < kCtWaves; ++w) {
-        base += w < wave ? s[w] : 0;
-        all += s[w];
+        ba += w < wave ? s[w] : 0;
+        bb += w < wave ? s[kCtWaves + w] : 0;
+        ta += s[w];
+        tb += s[kCtWaves + w];
     }
-    *total = all;
-    return base + x - v;
+    ea = ba + xa - va;
+    eb = bb + xb - vb;
 }
 
 __global__ __launch_bounds__(kCtBS) void cast_transpose_kernel(
@@ -73,127 +85,138 @@ __global__ __launch_bounds__(kCtBS) void cast_transpose_kernel(
     const float *__restrict__ scale, uint8_t *__restrict__ c_out, uint8_t *__restrict__ t_out,
     float *__restrict__ amax, int32_t *__restrict__ pad_offset)
 {
-    __shared__ int s_tiles[kMaxE + 1];   // exclusive prefix of row tiles per expert
-    __shared__ int s_pads[kMaxE + 1];    // exclusive prefix of padded row counts
-    __shared__ int s_red[kCtWaves];
-    __shared__ int s_e;
-    __shared__ uint32_t s_t[kCtCols * kCtStride];
+    __shared__ int s_red[2 * kCtWaves];
+    __shared__ int s_info[5];   // expert, its first tile, its padded-row prefix, row offset, rows
+    __shared__ uint32_t s_t[2][kCtLdsWords];
     __shared__ float s_amax[kCtWaves];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    // 1-D grid, column group fastest: the workgroups in flight read whole rows
+    // of a compact window of tiles rather than one column slice of every row
+    const int ncg = (H + kCtGroupCols - 1) / kCtGroupCols;
+    const int tile = blockIdx.x / ncg, cg = blockIdx.x % ncg;
 
     // Per-expert tile counts and padded row counts; thread owns experts
     // tid*ept .. tid*ept+ept-1 (contiguous, so one scan gives the prefixes).
-    const int ept = (E + kCtBS - 1) / kCtBS;   // <= 4
-    int nt[4], np[4], lt = 0, lp = 0;
+    const int ept = (E + kCtBS - 1) / kCtBS;
+    int lo[kCtEpt], nn[kCtEpt], lt = 0, lp = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kCtEpt; ++j) {
         const int e = tid * ept + j;
-        const int n = (j < ept && e < E) ? expert_offset[e + 1] - expert_offset[e] : 0;
-        nt[j] = (n + kCtRows - 1) / kCtRows;
-        np[j] = (n + 15) / 16 * 16;
-        lt += nt[j];
-        lp += np[j];
-    }
-    int tot_t, tot_p;
-    int rt = ct_scan(lt, s_red, &tot_t);
-    int rp = ct_scan(lp, s_red, &tot_p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = tid * ept + j;
+        lo[j] = 0;
+        nn[j] = 0;
         if (j < ept && e < E) {
-            s_tiles[e] = rt;
-            s_pads[e] = rp;
+            lo[j] = expert_offset[e];
+            nn[j] = expert_offset[e + 1] - lo[j];
         }
-        rt += nt[j];
-        rp += np[j];
+        lt += (nn[j] + kCtRows - 1) / kCtRows;
+        lp += (nn[j] + 15) / 16 * 16;
     }
-    if (tid == 0) {
-        s_tiles[E] = tot_t;
-        s_pads[E] = tot_p;
+    int rt, rp, tot_t, tot_p;
+    ct_scan2(lt, lp, s_red, rt, rp, tot_t, tot_p);
+    const bool first = blockIdx.x == 0;
+#pragma unroll
+    for (int j = 0; j < kCtEpt; ++j) {
+        const int e = tid * ept + j;
+        const int nt = (nn[j] + kCtRows - 1) / kCtRows;
+        if (j < ept && e < E) {
+            if (first) pad_offset[e] = rp;
+            if (rt <= tile && tile < rt + nt) {   // exactly one thread owns the tile
+                s_info[0] = e;
+                s_info[1] = rt;
+                s_info[2] = rp;
+                s_info[3] = lo[j];
+                s_info[4] = nn[j];
+            }
+        }
+        rt += nt;
+        rp += (nn[j] + 15) / 16 * 16;
     }
-    __syncthreads();
-    if (blockIdx.x == 0 && blockIdx.y == 0)
-        for (int e = tid; e <= E; e += kCtBS) pad_offset[e] = s_pads[e];
-
-    const int tile = blockIdx.x;
+    if (first && tid == 0) pad_offset[E] = tot_p;
     if (tile >= tot_t) return;   // uniform: the grid covers the tile bound
-    if (tid == 0) {              // the expert whose tiles contain `tile`
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_tiles[mid] <= tile) lo = mid;
-            else hi = mid - 1;
-        }
-        s_e = lo;
-    }
     __syncthreads();
-    const int e = s_e;
-    const int o = expert_offset[e], n = expert_offset[e + 1] - o;
-    const int npad = s_pads[e + 1] - s_pads[e];
-    const int r0 = (tile - s_tiles[e]) * kCtRows;          // first row of the tile within the expert
-    const int nrows = n - r0 < kCtRows ? n - r0 : kCtRows;   // valid rows
+
+    const int e = s_info[0], o = s_info[3], n = s_info[4];
+    const int npad = (n + 15) / 16 * 16;
+    const int r0 = (tile - s_info[1]) * kCtRows;                   // first row of the tile
+    const int nrows = n - r0 < kCtRows ? n - r0 : kCtRows;         // valid rows
     const int prows = npad - r0 < kCtRows ? npad - r0 : kCtRows;   // rows of T to write (x16)
     const float s = scale[e];
     const int hv = H / 8;   // 16-byte chunks per row
-    uint8_t *te = t_out + (size_t)H * s_pads[e];
+    uint8_t *te = t_out + (size_t)H * s_info[2];
+    const u32x4 *xt = x + (size_t)(o + r0) * hv;
+    uint8_t *ct_rows = c_out + (size_t)(o + r0) * H;
 
-    // item -> (row quad q, chunk cc): 4 rows 4q..4q+3, columns 8cc..8cc+7
+    // pass shape: Q = 2^lq row quads, C = 2^lc column chunks, W = 8C columns
+    const int nq = prows / 4;
+    const int lq = nq <= 4 ? 2 : nq <= 8 ? 3 : nq <= 16 ? 4 : 5;
+    const int lc = 8 - lq, lr = lq - 2;   // run blocks of 16 rows per column: 2^lr
+    const int Q = 1 << lq, W = 8 << lc;
+    const int q = tid >> lc, cc = tid & ((1 << lc) - 1);
+    const int gcol = cg * kCtGroupCols;
+    const int ncols = H - gcol < kCtGroupCols ? H - gcol : kCtGroupCols;
+    const int passes = (ncols + W - 1) / W;
+
+    auto load = [&](u32x4(&v)[4], int k) {
+        const int ch = ((gcol + k * W) >> 3) + cc;   // chunk index within the row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * q + i;
+            v[i] = u32x4{0, 0, 0, 0};
+            if (ch < hv && row < nrows) v[i] = __builtin_nontemporal_load(xt + (size_t)row * hv + ch);
+        }
+    };
+
     float a = 0.f;
-    for (int ct = 0; ct < kCtColTiles; ++ct) {
-        const int c0 = (blockIdx.y * kCtColTiles + ct) * kCtCols;
-        if (c0 >= H) break;   // uniform
+    u32x4 cur[4], nxt[4];
+    load(cur, 0);
+    for (int k = 0; k < passes; ++k) {
+        if (k + 1 < passes) load(nxt, k + 1);
+        uint32_t *buf = s_t[k & 1];
+        const int c0 = gcol + k * W;
+        const int ch = (c0 >> 3) + cc;
+        uint32_t b[4][2];
 #pragma unroll
-        for (int it = 0; it < kCtItems; ++it) {
-            const int item = it * kCtBS + tid;
-            const int q = item / kCtChunks, cc = item % kCtChunks;
-            uint32_t b[4][2];
+        for (int i = 0; i < 4; ++i) {
+            float f[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 4 * q + i;
-                u32x4 v = {0, 0, 0, 0};
-                if (row < nrows)
-                    v = __builtin_nontemporal_load(x + (size_t)(o + r0 + row) * hv + c0 / 8 + cc);
-                float f[8];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    f[2 * m] = bf16_lo(v[m]);
-                    f[2 * m + 1] = bf16_hi(v[m]);
-                }
-#pragma unroll
-                for (int m = 0; m < 8; ++m) a = fmaxf(a, fabsf(f[m]));
-                int p0 = cvt_pk_e4m3<false>(clamp448(f[0] * s), clamp448(f[1] * s), 0);
-                p0 = cvt_pk_e4m3<true>(clamp448(f[2] * s), clamp448(f[3] * s), p0);
-                int p1 = cvt_pk_e4m3<false>(clamp448(f[4] * s), clamp448(f[5] * s), 0);
-                p1 = cvt_pk_e4m3<true>(clamp448(f[6] * s), clamp448(f[7] * s), p1);
-                b[i][0] = (uint32_t)p0;
-                b[i][1] = (uint32_t)p1;
-                if (row < nrows) {
-                    u32x2 *dst = reinterpret_cast<u32x2 *>(c_out + (size_t)(o + r0 + row) * H + c0 + 8 * cc);
-                    *dst = u32x2{(uint32_t)p0, (uint32_t)p1};
-                }
+            for (int m = 0; m < 4; ++m) {
+                f[2 * m] = bf16_lo(cur[i][m]);
+                f[2 * m + 1] = bf16_hi(cur[i][m]);
             }
-            // column c = 8cc + m: byte m of the row's 8; 4 rows -> one word
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int w = m >> 2, sh = (m & 3) * 8;
-                const uint32_t word = ((b[0][w] >> sh) & 0xFFu) | (((b[1][w] >> sh) & 0xFFu) << 8) |
-                                      (((b[2][w] >> sh) & 0xFFu) << 16) | (((b[3][w] >> sh) & 0xFFu) << 24);
-                s_t[(8 * cc + m) * kCtStride + q] = word;
-            }
+            for (int m = 0; m < 8; ++m) a = fmaxf(a, fabsf(f[m]));
+            int p0 = cvt_pk_e4m3<false>(clamp448(f[0] * s), clamp448(f[1] * s), 0);
+            p0 = cvt_pk_e4m3<true>(clamp448(f[2] * s), clamp448(f[3] * s), p0);
+            int p1 = cvt_pk_e4m3<false>(clamp448(f[4] * s), clamp448(f[5] * s), 0);
+            p1 = cvt_pk_e4m3<true>(clamp448(f[6] * s), clamp448(f[7] * s), p1);
+            b[i][0] = (uint32_t)p0;
+            b[i][1] = (uint32_t)p1;
+            const int row = 4 * q + i;
+            if (ch < hv && row < nrows)
+                *reinterpret_cast<u32x2 *>(ct_rows + (size_t)row * H + 8 * ch) = u32x2{(uint32_t)p0, (uint32_t)p1};
+        }
+        // column 8cc + m holds byte m of each row's 8; 4 rows -> one word
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int w = m >> 2, sh = (m & 3) * 8;
+            const uint32_t word = ((b[0][w] >> sh) & 0xFFu) | (((b[1][w] >> sh) & 0xFFu) << 8) |
+                                  (((b[2][w] >> sh) & 0xFFu) << 16) | (((b[3][w] >> sh) & 0xFFu) << 24);
+            buf[(8 * cc + m) * (Q + 1) + cc + q] = word;
         }
         __syncthreads();
-        // T: kCtCols columns x 8 runs of 16 rows
+        // T: W columns x 2^lr runs of 16 rows = 512 runs, two per thread
 #pragma unroll
-        for (int u = 0; u < kCtRuns; ++u) {
+        for (int u = 0; u < 2; ++u) {
             const int p = u * kCtBS + tid;
-            const int col = p >> 3, rb = p & 7;
-            if (rb * 16 < prows) {
-                const uint32_t *src = s_t + col * kCtStride + rb * 4;
+            const int col = p >> lr, rb = p & ((1 << lr) - 1);
+            if (c0 + col < H && rb * 16 < prows) {
+                const uint32_t *src = buf + col * (Q + 1) + (col >> 3) + rb * 4;
                 const u32x4 run = u32x4{src[0], src[1], src[2], src[3]};
                 store16<false>(reinterpret_cast<u32x4 *>(te + (size_t)(c0 + col) * npad + r0 + rb * 16), run);
             }
         }
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
     }
     // amax: workgroup max, one atomic per workgroup (max of non-negative
     // floats = max of their bit patterns as unsigned integers)
@@ -221,8 +244,9 @@ hipError_t launch_cast_transpose(const void *x, int64_t rows_bound, int H, int E
                                  void *t_out, float *amax, int32_t *pad_offset, hipStream_t stream)
 {
     const int64_t tiles = (rows_bound + kCtRows - 1) / kCtRows + E;   // >= sum of ceil(n_e / 128)
-    const int colgroups = (H + kCtCols * kCtColTiles - 1) / (kCtCols * kCtColTiles);
-    hipLaunchKernelGGL(cast_transpose_kernel, dim3((unsigned)tiles, colgroups), dim3(kCtBS), 0, stream,
+    const int colgroups = (H + kCtGroupCols - 1) / kCtGroupCols;
+    if (tiles * colgroups > INT32_MAX) return hipErrorInvalidValue;   // the 1-D grid's limit
+    hipLaunchKernelGGL(cast_transpose_kernel, dim3((unsigned)(tiles * colgroups)), dim3(kCtBS), 0, stream,
                        (const u32x4 *)x, H, E, expert_offset, scale, (uint8_t *)c_out,
                        (uint8_t *)t_out, amax, pad_offset);
     return hipGetLastError();
