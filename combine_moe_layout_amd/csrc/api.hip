@@ -47,9 +47,7 @@ int check_layout_ptrs(const moe_layout_t *L)
 
 size_t layout_ws_bytes(int T, int E, int G)
 {
-    const size_t tiles = (size_t)moe::layout_tiles(T);
-    const size_t b = 4 * ((size_t)E + G + 1) * tiles;
-    return (b + 255) & ~(size_t)255;
+    return (moe::layout_ws_bytes_for(T, E, G) + 255) & ~(size_t)255;
 }
 
 int64_t rows_bound(int T, int K, int G, int mode)

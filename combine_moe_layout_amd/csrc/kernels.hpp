@@ -13,6 +13,18 @@ namespace moe {
 constexpr int kLayoutTile = 256;
 
 inline int layout_tiles(int T) { return (T + kLayoutTile - 1) / kLayoutTile; }
+// Layout workspace: the count table [tiles][E + G + 1] int32 (padded to a
+// multiple of 64 words), then the per-tile LDS words [tiles][E][4] as 32-bit
+// halves (used for top-k <= 8).
+inline size_t layout_table_words(int tiles, int E, int G)
+{
+    return ((size_t)tiles * (E + G + 1) + 63) & ~(size_t)63;
+}
+inline size_t layout_ws_bytes_for(int T, int E, int G)
+{
+    const int tiles = layout_tiles(T);
+    return 4 * (layout_table_words(tiles, E, G) + (size_t)tiles * E * 4 * 2);
+}
 
 struct LayoutPtrs {
     int32_t *expert_count, *expert_offset, *group_count, *group_offset;

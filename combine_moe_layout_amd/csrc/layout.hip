@@ -28,7 +28,10 @@
 // of the totals + prefix over earlier tiles, rebuilds its LDS words and writes
 // the slots and receive-source lists. Tile 0 also writes the counts, offsets
 // and status. Global loads are issued ahead of their first use, so each kernel
-// costs about one memory round trip plus its LDS work.
+// costs about one memory round trip plus its LDS work; the stores are shaped
+// so that a wave's store touches few cache lines (a token's slot row as one
+// or two 16-byte stores, the tile's expert receive list as per-expert runs
+// staged in LDS), since scattered 4-byte stores cost one line each.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -49,14 +52,25 @@ __device__ __forceinline__ int group_of(int x, uint32_t magic)
 }
 
 // A token's K expert indices, loaded into registers at kernel entry so the
-// loads overlap the LDS initialisation. Entries k >= K are -1.
+// loads overlap other work. The loads are unconditional, from clamped in-range
+// addresses (T >= 1), so they issue back to back with no branches; mask_row
+// then sets entries k >= K, and every entry of a lane past the last token, to
+// -1. (Masking next to the load lets the compiler turn each load into a
+// branch with a wait of its own.)
 template <int KMAX>
 __device__ __forceinline__ void load_row(const int32_t *__restrict__ idx, int t, int T, int K,
                                          int (&e)[KMAX])
 {
-    const int32_t *row = idx + (size_t)t * K;
+    const int32_t *row = idx + (size_t)(t < T ? t : T - 1) * K;
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) e[k] = (t < T && k < K) ? row[k] : -1;
+    for (int k = 0; k < KMAX; ++k) e[k] = row[k < K ? k : K - 1];
+}
+
+template <int KMAX>
+__device__ __forceinline__ void mask_row(int t, int T, int K, int (&e)[KMAX])
+{
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) e[k] = (t < T && k < K) ? e[k] : -1;
 }
 
 // What inserting one token found: k positions out of range, k positions that
@@ -68,9 +82,14 @@ struct Inserted {
 };
 
 // Insert a token's valid experts into the LDS words. A token is handled by one
-// lane, in k order, so "earlier k" is well defined. (Results are returned by
-// value: with reference out-parameters the compiler merged the updates into
-// a dynamically indexed private array, i.e. scratch memory.)
+// lane, in k order, so "earlier k" is well defined: an entry repeats iff its
+// expert equals an earlier in-range entry of the same token (that entry, or
+// the first of its repeats, set the lane's bit). For top-k <= 8 the repeats
+// are found by comparing registers, so the LDS ORs return nothing and do not
+// wait; for larger k the returned old word tells (the lane's own bit already
+// set). (Results are returned by value: with reference out-parameters the
+// compiler merged the updates into a dynamically indexed private array, i.e.
+// scratch memory.)
 template <int KMAX>
 __device__ __forceinline__ Inserted insert_token(const int (&e)[KMAX], bool live, int K, int E,
                                                  uint32_t gmagic,
@@ -83,9 +102,45 @@ __device__ __forceinline__ Inserted insert_token(const int (&e)[KMAX], bool live
         const int x = e[k];
         const bool in = live && k < K && (unsigned)x < (unsigned)E;
         oor |= (live && k < K && !in) ? 1u << k : 0u;
+        if constexpr (KMAX <= 8) {
+            bool rep = false;
+#pragma unroll
+            for (int j = 0; j < k; ++j) rep = rep || e[j] == x;
+            if (in) {
+                dup |= rep ? 1u << k : 0u;
+                if (!rep) {
+                    atomicOr(&emask[x * kWaves + wave], bit);
+                    gm |= 1u << group_of(x, gmagic);
+                }
+            }
+        } else {
+            if (in) {
+                const unsigned long long old = atomicOr(&emask[x * kWaves + wave], bit);
+                const bool rep = (old & bit) != 0;
+                dup |= rep ? 1u << k : 0u;
+                gm |= rep ? 0u : 1u << group_of(x, gmagic);
+            }
+        }
+    }
+    return Inserted{oor, dup, gm};
+}
+
+// The same classification as insert_token without touching LDS (top-k <= 8),
+// for a tile whose words were already built.
+template <int KMAX>
+__device__ __forceinline__ Inserted classify_token(const int (&e)[KMAX], bool live, int K, int E,
+                                                   uint32_t gmagic)
+{
+    uint32_t oor = 0, dup = 0, gm = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int x = e[k];
+        const bool in = live && k < K && (unsigned)x < (unsigned)E;
+        oor |= (live && k < K && !in) ? 1u << k : 0u;
+        bool rep = false;
+#pragma unroll
+        for (int j = 0; j < k; ++j) rep = rep || e[j] == x;
         if (in) {
-            const unsigned long long old = atomicOr(&emask[x * kWaves + wave], bit);
-            const bool rep = (old & bit) != 0;
             dup |= rep ? 1u << k : 0u;
             gm |= rep ? 0u : 1u << group_of(x, gmagic);
         }
@@ -94,11 +149,13 @@ __device__ __forceinline__ Inserted insert_token(const int (&e)[KMAX], bool live
 }
 
 // Count kernel: one tile per workgroup. Writes row `tile` of the tile-major
-// count table: E expert counts, G group counts, then the tile's error bits.
+// count table: E expert counts, G group counts, then the tile's error bits;
+// for top-k <= 8 also the tile's E x 4 words (as 32-bit halves), which the
+// place kernel loads instead of rebuilding them.
 template <int KMAX, bool EXACT>
 __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic,
-    uint32_t *__restrict__ tok_group_mask, int32_t *__restrict__ table)
+    uint32_t *__restrict__ tok_group_mask, int32_t *__restrict__ table, uint32_t *__restrict__ words)
 {
     extern __shared__ unsigned long long emask[];   // [E][kWaves]
     __shared__ int gcnt[kMaxG][kWaves];
@@ -112,6 +169,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     for (int i = tid; i < E * kWaves; i += kLayoutTile) emask[i] = 0ull;
     if (tid == 0) s_err = 0;
     __syncthreads();
+    mask_row<KMAX>(t, T, K, e);
 
     const Inserted ins = insert_token<KMAX>(e, t < T, K, E, gmagic, emask, wave, lane);
     const uint32_t gm = ins.gm;
@@ -131,6 +189,14 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     }
     if (tid < G) row[E + tid] = gcnt[tid][0] + gcnt[tid][1] + gcnt[tid][2] + gcnt[tid][3];
     if (tid == 0) row[E + G] = s_err;
+    if constexpr (KMAX <= 8) {
+        uint32_t *wt = words + (size_t)tile * E * kWaves * 2;
+        for (int i = tid; i < E * kWaves; i += kLayoutTile) {
+            const unsigned long long w = emask[i];
+            wt[2 * i] = (uint32_t)w;
+            wt[2 * i + 1] = (uint32_t)(w >> 32);
+        }
+    }
 }
 
 // Exclusive prefix sum over the 256 threads of the workgroup; *total gets the sum.
@@ -158,19 +224,40 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave_tot, int 
 }
 
 // Sum of table column `col` over tiles, and over the tiles before `tile`.
-// Loads are issued eight tiles at a time, so a column costs ceil(tiles / 8)
-// memory round trips.
+// The first kBatch tiles' entries are loaded by the caller (together with its
+// other loads, so they share one memory round trip); later tiles are loaded
+// kBatch at a time here.
+constexpr int kBatch = 16;
+
+// Loads of a column's first kBatch entries, unconditional and from clamped
+// in-range addresses (`col` < rows, ntiles >= 1); the caller masks the sums,
+// not the loads, so that the compiler keeps them out of lane-dependent
+// branches (a predicated load costs a branch and a wait of its own).
+__device__ __forceinline__ void column_first(const int32_t *__restrict__ table, int rows, int col,
+                                             int ntiles, int (&c)[kBatch])
+{
+    const int32_t *colp = table + col;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) c[u] = colp[(size_t)(u < ntiles ? u : ntiles - 1) * rows];
+}
+
 __device__ __forceinline__ void column_sums(const int32_t *__restrict__ table, int rows, int col,
-                                            int ntiles, int tile, int &tot, int &pre)
+                                            int ntiles, int tile, const int (&first)[kBatch],
+                                            int &tot, int &pre)
 {
     tot = 0;
     pre = 0;
-    for (int b0 = 0; b0 < ntiles; b0 += 8) {
-        int c[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) c[u] = (b0 + u < ntiles) ? table[(size_t)(b0 + u) * rows + col] : 0;
+    for (int u = 0; u < kBatch; ++u) {
+        tot += u < ntiles ? first[u] : 0;
+        pre += u < tile ? first[u] : 0;
+    }
+    for (int b0 = kBatch; b0 < ntiles; b0 += 16) {
+        int c[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) c[u] = (b0 + u < ntiles) ? table[(size_t)(b0 + u) * rows + col] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
             tot += c[u];
             pre += (b0 + u < tile) ? c[u] : 0;
         }
@@ -186,10 +273,18 @@ __device__ __forceinline__ void column_sums(const int32_t *__restrict__ table, i
 template <int KMAX, bool EXACT>
 __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic,
-    int ntiles, const int32_t *__restrict__ table, LayoutPtrs L)
+    int ntiles, const int32_t *__restrict__ table, const uint32_t *__restrict__ words, LayoutPtrs L,
+    int vec)
 {
-    extern __shared__ unsigned long long emask[];   // [E][kWaves], then int off_e[E][kWaves]
+    // For top-k <= 8 the tile's receive-list entries are staged in LDS in slot
+    // order and written out as contiguous runs (one run per expert) instead of
+    // one scattered 4-byte store per pair.
+    constexpr bool kStage = KMAX <= 8;
+    extern __shared__ unsigned long long emask[];   // [E][kWaves], int off_e[E][kWaves], int ldelta[E]
     int *off_e = reinterpret_cast<int *>(emask + E * kWaves);
+    int *ldelta = off_e + E * kWaves;   // tile-local position of expert x's pairs minus their global base
+    __shared__ int32_t s_src[kStage ? kLayoutTile * KMAX : 1];   // staged pair ids, slot order
+    __shared__ int32_t s_dst[kStage ? kLayoutTile * KMAX : 1];   // and their receive slots
     __shared__ int s_wave_tot[kWaves];
     __shared__ int base_g[kMaxG];
     __shared__ int tot_g[kMaxG];
@@ -202,9 +297,40 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     const int t = tile * kLayoutTile + tid;
     const int rows = E + G + 1;
 
+    // All global loads first (table columns, the tile's tokens, its words), so
+    // that they share one memory round trip: nothing below consumes them
+    // before the scheduling barrier.
+    int c0[kMaxEChunks][kBatch], cg0[kBatch];
+#pragma unroll
+    for (int j = 0; j < kMaxEChunks; ++j) {
+        const int x = j * kLayoutTile + tid;
+        if (j * kLayoutTile < E)   // uniform
+            column_first(table, rows, x < E ? x : E - 1, ntiles, c0[j]);
+    }
+    column_first(table, rows, E + (tid < G ? tid : G - 1), ntiles, cg0);
+    const int er_v = table[(size_t)(tid < ntiles ? tid : ntiles - 1) * rows + E + G];
     int e[KMAX];
     load_row<KMAX>(idx, t, T, K, e);
-    for (int i = tid; i < E * kWaves; i += kLayoutTile) emask[i] = 0ull;
+    // the tile's words from the count kernel (top-k <= 8)
+    constexpr int kWordsPerThread = kMaxEChunks * kWaves;
+    uint32_t wlo[kStage ? kWordsPerThread : 1], whi[kStage ? kWordsPerThread : 1];
+    if constexpr (kStage) {
+        const uint32_t *wt = words + (size_t)tile * E * kWaves * 2;
+#pragma unroll
+        for (int u = 0; u < kWordsPerThread; ++u) {
+            wlo[u] = whi[u] = 0;
+            if (u * kLayoutTile < E * kWaves) {   // uniform
+                const int i = u * kLayoutTile + tid;
+                const int ic = i < E * kWaves ? i : E * kWaves - 1;
+                wlo[u] = wt[2 * ic];
+                whi[u] = wt[2 * ic + 1];
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mask_row<KMAX>(t, T, K, e);
+    if constexpr (!kStage)
+        for (int i = tid; i < E * kWaves; i += kLayoutTile) emask[i] = 0ull;
     if (tid == 0) s_err = 0;
 
     // expert offsets: experts are owned in chunks of 256 (x = chunk * 256 + tid)
@@ -213,13 +339,32 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     for (int j = 0; j < kMaxEChunks; ++j) {
         tot[j] = pre[j] = 0;
         const int x = j * kLayoutTile + tid;
-        if (x < E) column_sums(table, rows, x, ntiles, tile, tot[j], pre[j]);
+        if (j * kLayoutTile < E) {   // uniform; lanes past E sum column E - 1 and drop it
+            column_sums(table, rows, x < E ? x : E - 1, ntiles, tile, c0[j], tot[j], pre[j]);
+            tot[j] = x < E ? tot[j] : 0;
+            pre[j] = x < E ? pre[j] : 0;
+        }
     }
-    if (tid < G) column_sums(table, rows, E + tid, ntiles, tile, tot_g[tid], base_g[tid]);
+    {
+        int tg, pg;
+        column_sums(table, rows, E + (tid < G ? tid : G - 1), ntiles, tile, cg0, tg, pg);
+        if (tid < G) {
+            tot_g[tid] = tg;
+            base_g[tid] = pg;
+        }
+    }
+    __syncthreads();   // s_err cleared
     if (tile == 0) {
-        int er = 0;
-        for (int b = tid; b < ntiles; b += kLayoutTile) er |= table[(size_t)b * rows + E + G];
+        int er = tid < ntiles ? er_v : 0;
+        for (int b = tid + kLayoutTile; b < ntiles; b += kLayoutTile) er |= table[(size_t)b * rows + E + G];
         if (er) atomicOr(&s_err, er);
+    }
+    if constexpr (kStage) {
+#pragma unroll
+        for (int u = 0; u < kWordsPerThread; ++u) {
+            const int i = u * kLayoutTile + tid;
+            if (i < E * kWaves) emask[i] = (unsigned long long)wlo[u] | ((unsigned long long)whi[u] << 32);
+        }
     }
     int carry = 0;
     int base[kMaxEChunks];
@@ -262,8 +407,10 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
         if (tile == 0 && lane == 0) *L.status = s_err;
     }
 
-    // Rebuild the tile's LDS words.
-    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, gmagic, emask, wave, lane);
+    // The tile's LDS words: loaded above (top-k <= 8), else rebuilt.
+    Inserted ins;
+    if constexpr (kStage) ins = classify_token<KMAX>(e, t < T, K, E, gmagic);
+    else ins = insert_token<KMAX>(e, t < T, K, E, gmagic, emask, wave, lane);
     const uint32_t gm = ins.gm, bad = ins.bad();
     for (int g = 0; g < G; ++g) {
         const uint64_t b = __ballot((gm >> g) & 1u);
@@ -271,17 +418,30 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     }
     __syncthreads();
 
-    // Offsets per (expert, wave) and (group, wave): base + lanes of earlier waves.
+    // Offsets per (expert, wave) and (group, wave): base + lanes of earlier
+    // waves. With staging, also each expert's first position in the tile's
+    // slot-ordered pair list (an exclusive scan over experts of the tile's counts).
+    int npairs = 0;
 #pragma unroll
     for (int j = 0; j < kMaxEChunks; ++j) {
-        const int x = j * kLayoutTile + tid;
-        if (x < E) {
-            const unsigned long long *m = emask + x * kWaves;
-            int r = base[j];
+        if (j * kLayoutTile < E) {   // uniform
+            const int x = j * kLayoutTile + tid;
+            int cnt = 0;
+            if (x < E) {
+                const unsigned long long *m = emask + x * kWaves;
+                int r = base[j];
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                off_e[x * kWaves + w] = r;
-                r += __popcll(m[w]);
+                for (int w = 0; w < kWaves; ++w) {
+                    off_e[x * kWaves + w] = r;
+                    r += __popcll(m[w]);
+                }
+                cnt = r - base[j];
+            }
+            if constexpr (kStage) {
+                int all;
+                const int lex = block_exclusive_scan(cnt, s_wave_tot, &all);
+                if (x < E) ldelta[x] = npairs + lex - base[j];
+                npairs += all;
             }
         }
     }
@@ -294,32 +454,89 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
         }
     }
     __syncthreads();
-    if (t >= T) return;
 
     const uint64_t below = lanemask_lt(lane);
+    if (t < T) {
+        const size_t p0 = (size_t)t * K;
+        if constexpr (kStage) {
+            int se[KMAX], sg[KMAX];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (k < K) {
-            const size_t p = (size_t)t * K + k;
-            int se = -1, sg = -1;
-            if (!((bad >> k) & 1u)) {
-                const int x = e[k];
-                se = off_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
-                L.recv_src_e[se] = (int32_t)p;
-                const int g = group_of(x, gmagic);
-                sg = off_g[g][wave] + __popcll(gball[g][wave] & below);
+            for (int k = 0; k < KMAX; ++k) {
+                se[k] = sg[k] = -1;
+                if (k < K && !((bad >> k) & 1u)) {
+                    const int x = e[k];
+                    se[k] = off_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
+                    const int g = group_of(x, gmagic);
+                    sg[k] = off_g[g][wave] + __popcll(gball[g][wave] & below);
+                    const int li = se[k] + ldelta[x];
+                    s_src[li] = (int32_t)(p0 + k);
+                    s_dst[li] = se[k];
+                }
             }
-            L.slot_e[p] = se;
-            L.slot_g[p] = sg;
+            if (EXACT && (vec & 1)) {   // 16-byte aligned slot arrays, K in {2, 4, 8}
+                if constexpr (KMAX == 2) {
+                    *reinterpret_cast<u32x2 *>(L.slot_e + p0) = u32x2{(uint32_t)se[0], (uint32_t)se[1]};
+                    *reinterpret_cast<u32x2 *>(L.slot_g + p0) = u32x2{(uint32_t)sg[0], (uint32_t)sg[1]};
+                } else {
+#pragma unroll
+                    for (int k = 0; k < KMAX; k += 4) {
+                        *reinterpret_cast<u32x4 *>(L.slot_e + p0 + k) =
+                            u32x4{(uint32_t)se[k], (uint32_t)se[k + 1], (uint32_t)se[k + 2], (uint32_t)se[k + 3]};
+                        *reinterpret_cast<u32x4 *>(L.slot_g + p0 + k) =
+                            u32x4{(uint32_t)sg[k], (uint32_t)sg[k + 1], (uint32_t)sg[k + 2], (uint32_t)sg[k + 3]};
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < KMAX; ++k) {
+                    if (k < K) {
+                        L.slot_e[p0 + k] = se[k];
+                        L.slot_g[p0 + k] = sg[k];
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (k < K) {
+                    int se = -1, sg = -1;
+                    if (!((bad >> k) & 1u)) {
+                        const int x = e[k];
+                        se = off_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
+                        L.recv_src_e[se] = (int32_t)(p0 + k);
+                        const int g = group_of(x, gmagic);
+                        sg = off_g[g][wave] + __popcll(gball[g][wave] & below);
+                    }
+                    L.slot_e[p0 + k] = se;
+                    L.slot_g[p0 + k] = sg;
+                }
+            }
+        }
+        // slot_tg row (G entries) and the group receive lists, four groups at a time
+        int32_t *tg = L.slot_tg + (size_t)t * G;
+        for (int g0 = 0; g0 < G; g0 += 4) {
+            int s4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int g = g0 + u;
+                s4[u] = -1;
+                if (g < G && ((gm >> g) & 1u)) {
+                    s4[u] = off_g[g][wave] + __popcll(gball[g][wave] & below);
+                    L.recv_src_g[s4[u]] = t;
+                }
+            }
+            if (vec & 2) {   // G % 4 == 0 and slot_tg 16-byte aligned
+                *reinterpret_cast<u32x4 *>(tg + g0) = u32x4{(uint32_t)s4[0], (uint32_t)s4[1], (uint32_t)s4[2], (uint32_t)s4[3]};
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (g0 + u < G) tg[g0 + u] = s4[u];
+            }
         }
     }
-    for (int g = 0; g < G; ++g) {
-        int s = -1;
-        if ((gm >> g) & 1u) {
-            s = off_g[g][wave] + __popcll(gball[g][wave] & below);
-            L.recv_src_g[s] = t;
-        }
-        L.slot_tg[(size_t)t * G + g] = s;
+    if constexpr (kStage) {
+        __syncthreads();
+        for (int i = tid; i < npairs; i += kLayoutTile) L.recv_src_e[s_dst[i]] = s_src[i];
     }
 }
 
@@ -347,12 +564,17 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
         return hipGetLastError();
     }
     const int ntiles = layout_tiles(T);
+    uint32_t *words = reinterpret_cast<uint32_t *>(ws) + layout_table_words(ntiles, E, G);
     const int epg = E / G;
     const uint32_t gmagic = epg == 1 ? 0u : (uint32_t)((1ull << 32) / (unsigned)epg) + 1u;
     const size_t lds1 = (size_t)E * kWaves * sizeof(unsigned long long);
-    const size_t lds2 = lds1 + (size_t)E * kWaves * sizeof(int);
-    using CountFn = void (*)(const int32_t *, int, int, int, int, uint32_t, uint32_t *, int32_t *);
-    using PlaceFn = void (*)(const int32_t *, int, int, int, int, uint32_t, int, const int32_t *, LayoutPtrs);
+    const size_t lds2 = lds1 + (size_t)E * (kWaves + 1) * sizeof(int);
+    // vector stores of the slot rows when the arrays allow them
+    const auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    const int vec = (a16(L.slot_e) && a16(L.slot_g) ? 1 : 0) | (G % 4 == 0 && a16(L.slot_tg) ? 2 : 0);
+    using CountFn = void (*)(const int32_t *, int, int, int, int, uint32_t, uint32_t *, int32_t *, uint32_t *);
+    using PlaceFn = void (*)(const int32_t *, int, int, int, int, uint32_t, int, const int32_t *,
+                             const uint32_t *, LayoutPtrs, int);
     CountFn count;
     PlaceFn place;
     switch (K) {
@@ -364,11 +586,11 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
         else { count = layout_count_kernel<32, false>; place = layout_place_kernel<32, false>; }
     }
     hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G, gmagic,
-                       L.tok_group_mask, ws);
+                       L.tok_group_mask, ws, words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(place, dim3(ntiles), dim3(kLayoutTile), lds2, stream, idx, T, K, E, G, gmagic,
-                       ntiles, static_cast<const int32_t *>(ws), L);
+                       ntiles, static_cast<const int32_t *>(ws), words, L, vec);
     return hipGetLastError();
 }
 

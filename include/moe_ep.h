@@ -110,8 +110,10 @@ typedef struct moe_layout_t {
 } moe_layout_t;
 
 /* Bytes of device workspace moe_layout() needs for these sizes (written to
- * *bytes). The workspace holds per-tile expert and group counts and per-tile
- * error bits; its contents need no initialisation and are dead after the call.
+ * *bytes). The workspace holds per-tile expert and group counts, per-tile
+ * error bits and, for K <= 8, each tile's token-by-expert bit masks (about
+ * T * E / 8 bytes); its contents need no initialisation and are dead after
+ * the call.
  * Returns MOE_ERR_BAD_SHAPE for sizes outside the limits. */
 int moe_layout_workspace_bytes(int T, int K, int E, int G, size_t *bytes);
 

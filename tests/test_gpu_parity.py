@@ -136,6 +136,20 @@ def test_layout_reuses_buffers_without_stale_state(moe, orc):
     check_layout(L, orc.layout(a, 256, 8))                           # status cleared again
 
 
+@pytest.mark.parametrize("T,K,E,G", [(700, 8, 256, 8), (300, 4, 64, 4), (513, 2, 16, 8)])
+def test_layout_slot_arrays_4_byte_aligned(moe, orc, T, K, E, G):
+    """Slot arrays that are 4-byte but not 16-byte aligned (allowed by the ABI) take
+    the scalar store path and give the same layout."""
+    idx = si.make_inputs(T, 8, E, K, seed=T + K)["topk_idx"]
+    L = moe.Layout.empty(T, K, E, G)
+    for name, n in (("slot_e", T * K), ("slot_g", T * K), ("slot_tg", T * G)):
+        buf = torch.empty(n + 1, dtype=torch.int32, device="cuda")
+        setattr(L, name, buf[1:])
+        assert getattr(L, name).data_ptr() % 16 != 0
+    L = moe.moe_layout(to_dev(idx), E, G, out=L)
+    check_layout(L, orc.layout(idx, E, G))
+
+
 # ------------------------------------------------------------------ dispatch
 
 def dispatch_with_canary(moe, L, x, w, idx, mode, dtype="bf16"):
