@@ -183,6 +183,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain reference copy (256 MiB, 5 times): a known byte "
                          "count for scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--table", default=None, metavar="NAMES",
+                    help="only the per-workload table for these comma-separated workloads "
+                         "(e.g. t4096): every call of the library on each, timed alone, printed "
+                         "as one JSON object; for profiling one workload's kernels")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -206,6 +210,9 @@ def main():
             moe.moe_ref_copy(dst, src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy": {"bytes_read": n, "bytes_written": n, "launches": 5}}))
+        return
+    if args.table:
+        print(json.dumps({"workloads": workload_table(moe, names=tuple(args.table.split(",")))}))
         return
     d = si.make_workload(args.workload)
     wl = d["workload"]
