@@ -51,10 +51,13 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
-// Exclusive scan of two values over the 256 threads, with both totals.
-__device__ __forceinline__ void ct_scan2(int va, int vb, int *s, int &ea, int &eb, int &ta, int &tb)
+// Exclusive scan of two values over the 256 threads, with both totals, and
+// the OR of a flag over the threads (returned).
+__device__ __forceinline__ bool ct_scan2(int va, int vb, bool flag, int *s, int &ea, int &eb, int &ta,
+                                         int &tb)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const bool wflag = __any(flag);
     int xa = va, xb = vb;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -67,9 +70,10 @@ __device__ __forceinline__ void ct_scan2(int va, int vb, int *s, int &ea, int &e
     if (lane == kWave - 1) {
         s[wave] = xa;
         s[kCtWaves + wave] = xb;
+        s[2 * kCtWaves + wave] = wflag ? 1 : 0;
     }
     __syncthreads();
-    int ba = 0, bb = 0;
+    int ba = 0, bb = 0, any = 0;
     ta = 0;
     tb = 0;
 #pragma unroll
@@ -78,17 +82,19 @@ __device__ __forceinline__ void ct_scan2(int va, int vb, int *s, int &ea, int &e
         bb += w < wave ? s[kCtWaves + w] : 0;
         ta += s[w];
         tb += s[kCtWaves + w];
+        any |= s[2 * kCtWaves + w];
     }
     ea = ba + xa - va;
     eb = bb + xb - vb;
+    return any != 0;
 }
 
 __global__ __launch_bounds__(kCtBS) void cast_transpose_kernel(
-    const u32x4 *__restrict__ x, int H, int E, const int32_t *__restrict__ expert_offset,
+    const u32x4 *__restrict__ x, int H, int E, int rows_bound, const int32_t *__restrict__ expert_offset,
     const float *__restrict__ scale, uint8_t *__restrict__ c_out, uint8_t *__restrict__ t_out,
     float *__restrict__ amax, int32_t *__restrict__ pad_offset)
 {
-    __shared__ int s_red[2 * kCtWaves];
+    __shared__ int s_red[3 * kCtWaves];
     __shared__ int s_info[5];   // expert, its first tile, its padded-row prefix, row offset, rows
     __shared__ uint32_t s_t[2][kCtLdsWords];
     __shared__ float s_amax[kCtWaves];
@@ -102,20 +108,26 @@ __global__ __launch_bounds__(kCtBS) void cast_transpose_kernel(
     // tid*ept .. tid*ept+ept-1 (contiguous, so one scan gives the prefixes).
     const int ept = (E + kCtBS - 1) / kCtBS;
     int lo[kCtEpt], nn[kCtEpt], lt = 0, lp = 0;
+    bool bad = false;
 #pragma unroll
     for (int j = 0; j < kCtEpt; ++j) {
         const int e = tid * ept + j;
         lo[j] = 0;
         nn[j] = 0;
         if (j < ept && e < E) {
-            lo[j] = expert_offset[e];
-            nn[j] = expert_offset[e + 1] - lo[j];
+            // a layout's offsets rise from 0 to at most rows_bound, the rows x
+            // and C hold; any others (a layout not written for these sizes)
+            // stop the whole grid below, before any write
+            const int a = expert_offset[e], b = expert_offset[e + 1];
+            bad = bad || a < 0 || b < a || b > rows_bound;
+            lo[j] = a;
+            nn[j] = bad ? 0 : b - a;
         }
         lt += (nn[j] + kCtRows - 1) / kCtRows;
         lp += (nn[j] + 15) / 16 * 16;
     }
     int rt, rp, tot_t, tot_p;
-    ct_scan2(lt, lp, s_red, rt, rp, tot_t, tot_p);
+    if (ct_scan2(lt, lp, bad, s_red, rt, rp, tot_t, tot_p)) return;   // uniform
     const bool first = blockIdx.x == 0;
 #pragma unroll
     for (int j = 0; j < kCtEpt; ++j) {
@@ -251,7 +263,7 @@ hipError_t launch_cast_transpose(const void *x, int64_t rows_bound, int H, int E
     const int colgroups = (H + kCtGroupCols - 1) / kCtGroupCols;
     if (tiles * colgroups > INT32_MAX) return hipErrorInvalidValue;   // the 1-D grid's limit
     hipLaunchKernelGGL(cast_transpose_kernel, dim3((unsigned)(tiles * colgroups)), dim3(kCtBS), 0, stream,
-                       (const u32x4 *)x, H, E, expert_offset, scale, (uint8_t *)c_out,
+                       (const u32x4 *)x, H, E, (int)rows_bound, expert_offset, scale, (uint8_t *)c_out,
                        (uint8_t *)t_out, amax, pad_offset);
     return hipGetLastError();
 }

@@ -51,6 +51,9 @@ __global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_kernel(
     const int tid = threadIdx.x;
     const u32x4 *src = x + (size_t)t * nvec;
     const int32_t *ts = slots + (size_t)t * nslot;
+    // receive rows of a valid layout are < T * min(K, nslot) (T = the grid),
+    // which the caller's buffers hold; anything else is skipped
+    const int64_t rows = (int64_t)gridDim.x * (K < nslot ? K : nslot);
 
     for (int base = 0; base < nvec; base += kDispatchBS * ITER) {
         u32x4 v[ITER];
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_kernel(
         }
         for (int d = 0; d < nslot; ++d) {
             const int s = ts[d];
-            if (s < 0) continue;
+            if (s < 0 || s >= rows) continue;
             u32x4 *dst = recv_x + (size_t)s * nvec;
 #pragma unroll
             for (int i = 0; i < ITER; ++i) {
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_kernel(
     if (il) iv = topk_idx[(size_t)t * K + tid - K];
     for (int d = 0; d < nslot; ++d) {
         const int s = ts[d];
-        if (s < 0) continue;
+        if (s < 0 || s >= rows) continue;
         if (wl) recv_w[(size_t)s * K + tid] = wv;
         if (il) recv_idx[(size_t)s * K + tid - K] = iv;
     }
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
     const u32x4 *src = x + (size_t)t * nch * 2;
     const int32_t *ts = slots + (size_t)t * nslot;
     const int nblk = nch / 8;
+    const int64_t rows = (int64_t)gridDim.x * (K < nslot ? K : nslot);   // as in the bf16 kernel
 
     for (int j = tid; FULL ? j < nch : j - tid < nch; j += bs) {
         const bool in = FULL || j < nch;
@@ -148,7 +152,7 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
         if (in) {
             for (int d = 0; d < nslot; ++d) {
                 const int s = ts[d];
-                if (s < 0) continue;
+                if (s < 0 || s >= rows) continue;
                 store16<NT>(recv_q + (size_t)s * nch + j, q);
                 if ((tid & 7) == 0) recv_scale[(size_t)s * nblk + (j >> 3)] = scale;
             }
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
     if (il) iv = topk_idx[(size_t)t * K + tid - K];
     for (int d = 0; d < nslot; ++d) {
         const int s = ts[d];
-        if (s < 0) continue;
+        if (s < 0 || s >= rows) continue;
         if (wl) recv_w[(size_t)s * K + tid] = wv;
         if (il) recv_idx[(size_t)s * K + tid - K] = iv;
     }

@@ -28,7 +28,7 @@ constexpr int kMaxIter = 8;
 template <int ITER, bool FULL>
 __global__ __launch_bounds__(kRegroupBS) void regroup_kernel(
     const u32x4 *__restrict__ in_rows, int nvec, const float *__restrict__ in_scale, int nscale,
-    const float *__restrict__ in_w, const int32_t *__restrict__ in_idx, int K, int G,
+    const float *__restrict__ in_w, const int32_t *__restrict__ in_idx, int T, int K, int G,
     const int32_t *__restrict__ group_offset, const int32_t *__restrict__ recv_src_g,
     const int32_t *__restrict__ slot_g, const int32_t *__restrict__ slot_e,
     u32x4 *__restrict__ out_rows, float *__restrict__ out_scale, float *__restrict__ out_w,
@@ -38,6 +38,10 @@ __global__ __launch_bounds__(kRegroupBS) void regroup_kernel(
     if (s >= group_offset[G]) return;  // the grid covers the row bound; rows used: group_offset[G]
     const int tid = threadIdx.x;
     const int t = recv_src_g[s];
+    // a valid layout names a token in [0, T) and expert rows in [0, T * K);
+    // anything else (a layout not written for these sizes) is skipped
+    if (t < 0 || t >= T) return;
+    const int64_t erows = (int64_t)T * K;
     const int32_t *sg = slot_g + (size_t)t * K;
     const int32_t *se = slot_e + (size_t)t * K;
 
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(kRegroupBS) void regroup_kernel(
             if (FULL || j < nvec) v[i] = __builtin_nontemporal_load(src + j);
         }
         for (int k = 0; k < K; ++k) {
-            if (sg[k] != s) continue;
+            if (sg[k] != s || se[k] < 0 || se[k] >= erows) continue;
             u32x4 *dst = out_rows + (size_t)se[k] * nvec;
 #pragma unroll
             for (int i = 0; i < ITER; ++i) {
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(kRegroupBS) void regroup_kernel(
     if (wl) wv = in_w[(size_t)s * K + tid];
     if (il) iv = in_idx[(size_t)s * K + tid - K];
     for (int k = 0; k < K; ++k) {
-        if (sg[k] != s) continue;
+        if (sg[k] != s || se[k] < 0 || se[k] >= erows) continue;
         const int r = se[k];
         if (wl) out_w[(size_t)r * K + tid] = wv;
         if (il) out_idx[(size_t)r * K + tid - K] = iv;
@@ -96,7 +100,7 @@ hipError_t launch_regroup(const void *in_rows, int row_bytes, const float *in_sc
     int iter = (nvec + kRegroupBS - 1) / kRegroupBS;
     iter = iter < 1 ? 1 : (iter > kMaxIter ? kMaxIter : iter);
     const bool full = nvec % (kRegroupBS * iter) == 0;
-    void (*fn)(const u32x4 *, int, const float *, int, const float *, const int32_t *, int, int,
+    void (*fn)(const u32x4 *, int, const float *, int, const float *, const int32_t *, int, int, int,
                const int32_t *, const int32_t *, const int32_t *, const int32_t *, u32x4 *, float *,
                float *, int32_t *, bool);
     switch (iter) {
@@ -111,7 +115,7 @@ hipError_t launch_regroup(const void *in_rows, int row_bytes, const float *in_sc
     }
     const int64_t bound = (int64_t)T * (K < G ? K : G);   // group rows used <= bound
     hipLaunchKernelGGL(fn, dim3((unsigned)bound), dim3(kRegroupBS), 0, stream, (const u32x4 *)in_rows,
-                       nvec, in_scale, nscale, in_w, in_idx, K, G, group_offset, recv_src_g, slot_g,
+                       nvec, in_scale, nscale, in_w, in_idx, T, K, G, group_offset, recv_src_g, slot_g,
                        slot_e, (u32x4 *)out_rows, out_scale, out_w, out_idx,
                        tuning().dispatch_nt_store);
     return hipGetLastError();

@@ -149,7 +149,9 @@ int moe_layout(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t 
  * recv_scale: device fp32 [recv_capacity, H / 128] (FP8 only; NULL for BF16).
  * recv_topk_w / recv_topk_idx: device [recv_capacity, K].
  * recv_capacity >= moe_recv_rows_bound(T, K, G, mode), else MOE_ERR_CAPACITY.
- * FP8 needs H % 128 == 0. L must hold the layout of topk_idx.
+ * FP8 needs H % 128 == 0. L must hold the layout of topk_idx. As a guard
+ * against a layout not written by moe_layout() for these sizes, slots outside
+ * [0, moe_recv_rows_bound()) are skipped, so no write leaves the buffers.
  * Source: mori pull request 586, Technical Details 3 (wave-wide row copy) and
  * 4 (vectorised metadata copies); the challenge write-up, section 3.1. */
 int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *x,
@@ -180,6 +182,9 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode
  * once. recv_g: [g_capacity, H] bf16 or e4m3 as `dtype`; recv_scale_*: fp32
  * [*, H/128] (FP8 only, else NULL); recv_topk_*: [*, K]. g_capacity and
  * e_capacity must reach the GROUP and EXPERT bounds of moe_recv_rows_bound().
+ * Group rows naming a token outside [0, T), or pairs whose expert row is
+ * outside [0, T*K) (possible only for a layout not written by moe_layout()
+ * for these sizes), are skipped.
  * Source: "Optimizing Distributed Inference Kernels for AMD DEVELOPER CHALLENGE
  * 2025", section 3.1 (the receive kernel copies tokens into per-local-expert
  * buffers). */
@@ -200,7 +205,10 @@ int moe_regroup(const moe_layout_t *L, int dtype, int H, const void *recv_g, con
  * total). amax is max-accumulated: it must hold non-negative values (zero it
  * for a fresh maximum). x: bf16 [x_rows, H], x_rows >= T*K; c_out: uint8
  * [x_rows, H]; t_out: at least moe_cast_transpose_t_bytes() bytes; H % 64 == 0.
- * Rows of c_out beyond expert_offset[E] are not written.
+ * Rows of c_out beyond expert_offset[E] are not written. If the layout's
+ * offsets do not satisfy 0 <= expert_offset[e] <= expert_offset[e+1] <= T*K
+ * (a layout not written by moe_layout() for these sizes), the call writes
+ * nothing.
  * Source: "Optimized rocm specific multicast transpose kernel"
  * (ROCm/TransformerEngine pull request 586), Change Summary: both outputs from
  * one read with amax fused in, packed FP8 conversion, all experts in one launch,

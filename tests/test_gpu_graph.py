@@ -1,0 +1,114 @@
+"""The whole path captured once in a HIP graph and replayed on new inputs.
+
+Every call of the library is asynchronous on the caller's stream and allocates
+nothing, so a graph captured once can be replayed with new contents in the same
+input buffers. Each replay here follows eager work (copies of the next inputs,
+a zeroing of the amax accumulator) and a synchronisation, and every replay's
+outputs are compared with the oracle on that replay's inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def libs():
+    assert torch.cuda.is_available()
+    import combine_moe_layout_amd as moe
+    import oracle
+    return moe, oracle
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _u16_to_bf16_tensor(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+# (T, H, E, G, K, fused): fused = capture moe_layout_dispatch instead of the two calls
+CASES = [(700, 1024, 64, 8, 6, False), (300, 512, 32, 4, 8, True), (2000, 2048, 256, 8, 8, False)]
+
+
+@pytest.mark.parametrize("T,H,E,G,K,fused", CASES)
+def test_graph_replays_match_oracle(libs, T, H, E, G, K, fused):
+    moe, orc = libs
+    idx_d = torch.zeros((T, K), dtype=torch.int32, device="cuda")
+    w_d = torch.zeros((T, K), dtype=torch.float32, device="cuda")
+    x_d = torch.zeros((T, H), dtype=torch.bfloat16, device="cuda")
+    scale_d = torch.zeros(E, dtype=torch.float32, device="cuda")
+    L = moe.Layout.empty(T, K, E, G)
+    De = moe.alloc_dispatch(L, H, "expert")
+    Dg = moe.alloc_dispatch(L, H, "group")
+    Dr = moe.alloc_dispatch(L, H, "expert")          # regroup of the per-group rows
+    oe = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    og = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    amax = torch.zeros(E, dtype=torch.float32, device="cuda")
+    moe.moe_layout(idx_d, E, G, out=L)          # a layout (all tokens on expert 0) before its first use
+    CT = moe.moe_cast_transpose_fp8(L, De.recv_x, scale_d, amax=amax)   # allocates its outputs
+
+    def step():
+        if fused:
+            moe.moe_layout_dispatch(idx_d, E, G, x_d, w_d, "expert", out_layout=L, out=De)
+        else:
+            moe.moe_layout(idx_d, E, G, out=L)
+            moe.moe_dispatch(L, x_d, w_d, idx_d, "expert", out=De)
+        moe.moe_dispatch(L, x_d, w_d, idx_d, "group", out=Dg)
+        moe.moe_regroup(L, Dg, out=Dr)
+        moe.moe_combine(L, De.recv_x, w_d, "expert", out=oe)
+        moe.moe_combine(L, Dg.recv_x, w_d, "group", out=og)
+        moe.moe_cast_transpose_fp8(L, De.recv_x, scale_d, out=CT)
+
+    # warm up on a side stream, then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        d = si.make_inputs(T, H, E, K, seed=500 + 10 * rep + T, routing="uniform" if rep != 1 else "zipf")
+        idx, w, x = d["topk_idx"], d["topk_w"], d["x"]
+        rng = np.random.default_rng(rep)
+        scale = rng.uniform(0.5, 100.0, E).astype(np.float32)
+        # eager work between replays: new inputs, a cleared accumulator
+        idx_d.copy_(torch.from_numpy(idx))
+        w_d.copy_(torch.from_numpy(w))
+        x_d.copy_(_u16_to_bf16_tensor(x))
+        scale_d.copy_(torch.from_numpy(scale))
+        amax.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+
+        case = f"replay {rep}: T={T} H={H} E={E} G={G} K={K} fused={fused}"
+        Lo = orc.layout(idx, E, G)
+        assert int(L.status.item()) == Lo["status"], case
+        for n in ("expert_count", "expert_offset", "group_count", "group_offset", "slot_e",
+                  "slot_g", "slot_tg"):
+            assert np.array_equal(getattr(L, n).cpu().numpy(), Lo[n]), (case, n)
+        Doe = orc.dispatch_bf16(Lo, "expert", x, w, idx)
+        Dog = orc.dispatch_bf16(Lo, "group", x, w, idx)
+        R, P = Lo["R_expert"], Lo["R_group"]
+        assert np.array_equal(_bits(De.recv_x)[:R], Doe["recv_x"]), case
+        assert np.array_equal(_bits(Dg.recv_x)[:P], Dog["recv_x"]), case
+        assert np.array_equal(De.recv_topk_idx[:R].cpu().numpy(), Doe["recv_idx"]), case
+        assert np.array_equal(_bits(Dr.recv_x)[:R], Doe["recv_x"]), case           # regroup
+        assert np.array_equal(_bits(oe), orc.combine(Lo, "expert", Doe["recv_x"], w)), case
+        assert np.array_equal(_bits(og), orc.combine(Lo, "group", Dog["recv_x"], w)), case
+        ref = orc.cast_transpose_fp8(Lo["expert_offset"], Doe["recv_x"], scale)
+        assert np.array_equal(CT.c[:R].cpu().numpy(), ref["c"]), case
+        nt = H * int(ref["pad_offset"][-1])
+        assert np.array_equal(CT.t[:nt].cpu().numpy(), ref["t"]), case
+        assert np.array_equal(CT.amax.cpu().numpy().view(np.uint32), ref["amax"].view(np.uint32)), case
+    del g
