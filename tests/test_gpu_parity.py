@@ -600,3 +600,92 @@ def test_cast_transpose_matches_oracle(moe, orc, name, shape):
     nt = H * int(ref["pad_offset"][-1])
     np.testing.assert_array_equal(CT.t[:nt].cpu().numpy(), ref["t"])
     np.testing.assert_array_equal(CT.amax.cpu().numpy().view(np.uint32), ref["amax"].view(np.uint32))
+
+
+# ------------------------------------------------------------------ guards
+# A layout not written by moe_layout() for these sizes (stale or corrupted) must
+# not lead any kernel out of the buffers the host checked. Each case below leaves
+# spare room around every buffer it corrupts an index into, so that even an
+# unguarded access would stay in allocated memory; the checks are on the values.
+
+def _padded_i32(n, pad=64):
+    """An int32 [n] view of a buffer with `pad` more entries, all -1 (no slot)."""
+    return torch.full((n + pad,), -1, dtype=torch.int32, device="cuda")[:n]
+
+
+def test_guard_dispatch_skips_slots_outside_the_bound(moe, orc):
+    T, H, E, G, K = 300, 256, 32, 4, 4
+    d = si.make_inputs(T, H, E, K, seed=71)
+    idx, w, x = d["topk_idx"], d["topk_w"], d["x"]
+    idx_d, w_d, x_d = to_dev(idx), to_dev(w), dev_bf16(x)
+    L = moe.moe_layout(idx_d, E, G)
+    torch.cuda.synchronize()
+    Lo = orc.layout(idx, E, G)
+    bound = T * K
+    L.slot_e[5 * K + 1] = bound + 3          # past the bound, inside the spare rows
+    L.slot_e[9 * K + 0] = -5
+    D = moe.alloc_dispatch(L, H, "expert", capacity=bound + 16)
+    D.recv_x.view(torch.int16).fill_(int(CANARY16.astype(np.int16)))
+    moe.moe_dispatch(L, x_d, w_d, idx_d, "expert", out=D)
+    torch.cuda.synchronize()
+    got = host_u16(D.recv_x)
+    assert np.all(got[bound:] == CANARY16)
+    Do = orc.dispatch_bf16(Lo, "expert", x, w, idx)
+    R = Lo["R_expert"]
+    skipped = [int(Lo["slot_e"][5 * K + 1]), int(Lo["slot_e"][9 * K + 0])]
+    keep = np.ones(R, bool)
+    keep[skipped] = False
+    assert np.array_equal(got[:R][keep], Do["recv_x"][keep])
+    assert np.all(got[skipped] == CANARY16)
+
+
+def test_guard_regroup_skips_tokens_outside_the_batch(moe, orc):
+    T, H, E, G, K = 300, 256, 32, 4, 4
+    d = si.make_inputs(T, H, E, K, seed=72)
+    idx, w, x = d["topk_idx"], d["topk_w"], d["x"]
+    idx_d, w_d, x_d = to_dev(idx), to_dev(w), dev_bf16(x)
+    L = moe.Layout.empty(T, K, E, G)
+    L.slot_g, L.slot_e = _padded_i32(T * K), _padded_i32(T * K)   # room past token T - 1
+    moe.moe_layout(idx_d, E, G, out=L)
+    Dg = moe.moe_dispatch(L, x_d, w_d, idx_d, "group")
+    torch.cuda.synchronize()
+    Lo = orc.layout(idx, E, G)
+    L.recv_src_g[3] = T                      # group row 3 names a token past the batch
+    De = moe.alloc_dispatch(L, H, "expert")
+    De.recv_x.view(torch.int16).fill_(int(CANARY16.astype(np.int16)))
+    moe.moe_regroup(L, Dg, out=De)
+    torch.cuda.synchronize()
+    t3 = int(Lo["recv_src_g"][3])
+    skipped = [int(Lo["slot_e"][t3 * K + k]) for k in range(K) if Lo["slot_g"][t3 * K + k] == 3]
+    assert skipped
+    Do = orc.dispatch_bf16(Lo, "expert", x, w, idx)
+    R = Lo["R_expert"]
+    got = host_u16(De.recv_x)
+    keep = np.ones(R, bool)
+    keep[skipped] = False
+    assert np.array_equal(got[:R][keep], Do["recv_x"][keep])
+    assert np.all(got[skipped] == CANARY16)
+
+
+def test_guard_cast_transpose_writes_nothing_for_offsets_past_the_bound(moe, orc):
+    T, H, E, G, K = 300, 256, 32, 4, 4
+    d = si.make_inputs(T, H, E, K, seed=73)
+    idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
+    L = moe.moe_layout(idx_d, E, G)
+    bound = T * K
+    D = moe.alloc_dispatch(L, H, "expert", capacity=bound + 64)    # x rows to spare
+    moe.moe_dispatch(L, x_d, w_d, idx_d, "expert", out=D)
+    torch.cuda.synchronize()
+    L.expert_offset[E] = bound + 8           # past T*K: not a layout of these sizes
+    nb = H * (bound + 15 * E)                 # moe_cast_transpose_t_bytes(T, K, E, H)
+    CT = moe.CastTransposed(torch.full((bound + 64, H), 0xA5, dtype=torch.uint8, device="cuda"),
+                            torch.full((nb + 64 * H,), 0x5A, dtype=torch.uint8, device="cuda"),
+                            torch.full((E,), 2.5, dtype=torch.float32, device="cuda"),
+                            torch.full((E + 1,), -9, dtype=torch.int32, device="cuda"))
+    scale = torch.full((E,), 16.0, dtype=torch.float32, device="cuda")
+    moe.moe_cast_transpose_fp8(L, D.recv_x, scale, out=CT)
+    torch.cuda.synchronize()
+    assert bool((CT.c == 0xA5).all())
+    assert bool((CT.t == 0x5A).all())
+    assert bool((CT.amax == 2.5).all())
+    assert bool((CT.pad_offset == -9).all())
