@@ -3,20 +3,23 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t4096]
 
 One step = one pass of the hot path over one batch of synthetic input already
-resident in HBM: moe_layout (per-expert and per-group layout), moe_dispatch
-(bf16 rows into per-expert receive buffers) and moe_combine (fp32 weighted
-top-k sum back to bf16; the experts are identities, so combine reads the
-dispatched rows in place). Default workload: 4096 tokens x 7168 hidden bf16,
-256 experts in 8 groups, top-8 uniform routing.
+resident in HBM: the routing layout (per-expert and per-group) and the dispatch
+of bf16 rows into per-expert receive buffers, as one moe_layout_dispatch call
+(for this batch: the layout's count kernel, one offsets workgroup, and a
+dispatch whose workgroups place their own tokens), then moe_combine (fp32
+weighted top-k sum back to bf16; the experts are identities, so combine reads
+the dispatched rows in place). Default workload: 4096 tokens x 7168 hidden
+bf16, 256 experts in 8 groups, top-8 uniform routing.
 
 Prints ONE JSON line. `value` = algorithmic HBM bytes of a step (reads + writes,
-each byte counted once) / wall time per step. Per-kernel times come from HIP
-events recorded around every launch in the timed region, on the stream the
+each byte counted once) / wall time per step. Per-call times come from HIP
+events recorded around every call in the timed region, on the stream the
 kernels run on. The same line carries the roofline of the dominant kernel, the
 CPU oracle timed on host cores (a bounded sample of the same workload), and
-secondary measurements (the deduplicated per-group layout, FP8 dispatch on the
-FP8 workload, a plain copy ceiling, each kernel repeated alone, cold-cache
-timings).
+secondary measurements (the same step as three calls moe_layout, moe_dispatch,
+moe_combine with per-call rates, the deduplicated per-group layout, FP8
+dispatch on the FP8 workload, a plain copy ceiling, each kernel repeated alone,
+cold-cache timings, every call on every workload).
 """
 from __future__ import annotations
 
@@ -220,20 +223,19 @@ def main():
     dv = Dev(moe, d, modes=("expert",))
     L, D, out = dv.L, dv.D["expert"], dv.out
 
-    def launches():
-        return [
-            lambda: moe.moe_layout(dv.idx, E, G, out=L),
-            lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "expert", "bf16", out=D),
-            lambda: moe.moe_combine(L, D.recv_x, dv.w, "expert", out=out),
-        ]
-
-    fns = launches()
+    # one step: routing layout + dispatch as one call (the library's form for this
+    # batch: the count kernel, one offsets workgroup, and a dispatch that places its
+    # own tokens), then the combine; the three separate calls are timed in extras
+    fns = [
+        lambda: moe.moe_layout_dispatch(dv.idx, E, G, dv.x, dv.w, "expert", "bf16", out_layout=L, out=D),
+        lambda: moe.moe_combine(L, D.recv_x, dv.w, "expert", out=out),
+    ]
     for _ in range(args.warmup):
         for f in fns:
             f()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -243,13 +245,11 @@ def main():
         e[1].record()
         fns[1]()
         e[2].record()
-        fns[2]()
-        e[3].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / args.steps * 1e3
     us = {name: [ev[s][i].elapsed_time(ev[s][i + 1]) * 1e3 for s in range(args.steps)]
-          for i, name in enumerate(("layout", "dispatch", "combine"))}
+          for i, name in enumerate(("layout_dispatch", "combine"))}
 
     assert int(L.status.item()) == 0
     R = int(L.expert_offset[E].item())
@@ -261,8 +261,9 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     avg = {k: float(np.mean(v)) for k, v in us.items()}
-    kern = {"dispatch": (d_r + d_w, avg["dispatch"]), "combine": (c_r + c_w, avg["combine"])}
-    dom = max(kern, key=lambda k: kern[k][1])
+    # the dominant kernel: combine (the layout + dispatch call is several kernels)
+    kern = {"combine": (c_r + c_w, avg["combine"])}
+    dom = "combine"
     ach = kern[dom][0] / (kern[dom][1] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom, f"{dom}_expert_bf16"),
@@ -279,12 +280,11 @@ def main():
                    "tokens": T, "hidden": H, "experts": E, "groups": G, "topk": K,
                    "routing": wl.routing, "receive_layout": "expert", "seed": wl.seed},
         "roofline": roofline,
+        "step": "moe_layout_dispatch + moe_combine (per-expert layout)",
         "kernels_us": {k: {kk: round(vv, 2) for kk, vv in stats(v).items()} for k, v in us.items()},
         "kernels_gbs": {
-            "dispatch": round((d_r + d_w) / (avg["dispatch"] * 1e-6) / 1e9, 1),
+            "layout_dispatch": round((b_layout + d_r + d_w) / (avg["layout_dispatch"] * 1e-6) / 1e9, 1),
             "combine": round((c_r + c_w) / (avg["combine"] * 1e-6) / 1e9, 1),
-            "layout_us": round(avg["layout"], 2),
-            "dispatch_payload_gbs": round(R * H * 2 / (avg["dispatch"] * 1e-6) / 1e9, 1),
             "combine_payload_gbs": round(R * H * 2 / (avg["combine"] * 1e-6) / 1e9, 1),
         },
         "bytes": {"layout": b_layout, "dispatch": d_r + d_w, "combine": c_r + c_w, "rows": R,
@@ -313,6 +313,26 @@ def extras(moe, d, dv, args):
     moe.moe_layout(dv.idx, E, G, out=L)
     P = int(L.group_offset[G].item())
     R = int(L.expert_offset[E].item())
+
+    # the same step as three separate calls (layout, dispatch, combine)
+    De = dv.D["expert"]
+    lay = lambda: moe.moe_layout(dv.idx, E, G, out=L)
+    disp = lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "expert", "bf16", out=De)
+    comb = lambda: moe.moe_combine(L, De.recv_x, dv.w, "expert", out=dv.out)
+    lay(); disp(); comb()
+    t3 = time_calls([lay, disp, comb], it)
+    bl = layout_bytes(T, K, E, G, P)
+    bd3, bc3 = sum(dispatch_bytes(T, H, K, G, R, "expert")), sum(combine_bytes(T, H, K, R))
+    step3 = [a + b + c for a, b, c in zip(*t3)]
+    m3 = [stats(v)["median"] for v in t3]
+    res["three_call_step"] = {
+        "layout_us": m3[0], "dispatch_us": m3[1], "combine_us": m3[2],
+        "step_us": stats(step3)["median"],
+        "step_gbs": round((bl + bd3 + bc3) / stats(step3)["median"] / 1e3, 1),
+        "dispatch_gbs": round(bd3 / m3[1] / 1e3, 1), "combine_gbs": round(bc3 / m3[2] / 1e3, 1),
+        "dispatch_frac": round(bd3 / m3[1] / 1e3 / PEAK_HBM_GBS, 4),
+        "combine_frac": round(bc3 / m3[2] / 1e3 / PEAK_HBM_GBS, 4),
+        "dispatch_payload_gbs": round(R * H * 2 / m3[1] / 1e3, 1)}
     Dg = moe.alloc_dispatch(L, H, "group")
     disp_g = lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "group", "bf16", out=Dg)
     comb_g = lambda: moe.moe_combine(L, Dg.recv_x, dv.w, "group", out=dv.out)
@@ -374,6 +394,23 @@ def extras(moe, d, dv, args):
         f8[mode] = {"rows": rows, "dispatch_us": stats(t8[0])["median"],
                     "dispatch_gbs": round(b8 / stats(t8[0])["median"] / 1e3, 1)}
     res["fp8_dispatch"] = f8
+
+    # the same step with layout + dispatch as one call (moe_layout_dispatch: the count
+    # kernel, one offsets workgroup, and a dispatch that places its own tokens)
+    fs = {}
+    for mode in ("expert", "group"):
+        Dm = dv.D["expert"] if mode == "expert" else moe.alloc_dispatch(L, H, "group")
+        ld = lambda: moe.moe_layout_dispatch(dv.idx, E, G, dv.x, dv.w, mode, "bf16", out_layout=L, out=Dm)
+        cb = lambda: moe.moe_combine(L, Dm.recv_x, dv.w, mode, out=dv.out)
+        ld(); cb()
+        tf = time_calls([ld, cb], it)
+        rows = R if mode == "expert" else P
+        nb = (layout_bytes(T, K, E, G, P) + sum(dispatch_bytes(T, H, K, G, rows, mode))
+              + sum(combine_bytes(T, H, K, rows)))
+        step = [a + b for a, b in zip(tf[0], tf[1])]
+        fs[mode] = {"layout_dispatch_us": stats(tf[0])["median"], "combine_us": stats(tf[1])["median"],
+                    "step_us": stats(step)["median"], "step_gbs": round(nb / stats(step)["median"] / 1e3, 1)}
+    res["fused_step"] = fs
     del dv8
     torch.cuda.synchronize()
     res["workloads"] = workload_table(moe)
@@ -463,8 +500,8 @@ def workload_table(moe, names=("tiny", "t256", "t4096", "skew", "fp8"), it=30):
             torch.cuda.synchronize()
             row["graph_step_us"] = round(stats(time_calls([g.replay], it)[0])["median"], 2)
             del g
-            if T <= moe.FUSED_MAX_TOKENS and T * K <= moe.FUSED_MAX_PAIRS:
-                # the low-latency form: layout + dispatch in one launch
+            if True:
+                # layout + dispatch as one call (one launch for T <= 512)
                 fused = lambda: moe.moe_layout_dispatch(dv.idx, E, G, dv.x, dv.w, "expert", dt,
                                                         out_layout=L, out=De)
                 fused()

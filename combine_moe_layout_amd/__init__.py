@@ -68,7 +68,7 @@ def _load_library() -> ctypes.CDLL:
         "moe_layout": (i32, [_P, LP, _P, sz, _P]),
         "moe_dispatch": (i32, [LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, _P, i64, _P]),
         "moe_combine": (i32, [LP, i32, i32, _P, i64, _P, _P, _P]),
-        "moe_layout_dispatch": (i32, [_P, LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, i64, _P]),
+        "moe_layout_dispatch": (i32, [_P, LP, _P, ctypes.c_size_t, i32, i32, i32, _P, _P, _P, _P, _P, _P, i64, _P]),
         "moe_regroup": (i32, [LP, i32, i32, _P, _P, _P, _P, i64, _P, _P, _P, _P, i64, _P]),
         "moe_cast_transpose_t_bytes": (i64, [i32, i32, i32, i32]),
         "moe_cast_transpose_fp8": (i32, [LP, i32, _P, i64, _P, _P, _P, i64, _P, _P, _P]),
@@ -252,7 +252,8 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
                         topk_w: torch.Tensor, mode="expert", dtype="bf16", *,
                         out_layout: Layout | None = None, out: Dispatched | None = None,
                         stream=None) -> tuple[Layout, Dispatched]:
-    """moe_layout + moe_dispatch in one launch, for T <= 512 (moe_layout_dispatch)."""
+    """moe_layout + moe_dispatch as one call (moe_layout_dispatch): one launch for T <= 512,
+    else the count kernel, an offsets workgroup and a dispatch that places its own tokens."""
     if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or not topk_idx.is_contiguous():
         raise ValueError("topk_idx must be a contiguous int32 [T, K] tensor")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
@@ -265,7 +266,8 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
         raise ValueError("layout buffers were made for other sizes")
     H = x.shape[1]
     D = out if out is not None else alloc_dispatch(L, H, mode, dtype, x.device)
-    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), L.ref(), _mode(mode), _dtype(dtype), H,
+    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), L.ref(), _ptr(L.workspace), L.workspace.numel(),
+                                    _mode(mode), _dtype(dtype), H,
                                     _ptr(x), _ptr(topk_w), _ptr(D.recv_x), _ptr(D.recv_scale),
                                     _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
                                     _stream(stream)), "moe_layout_dispatch")

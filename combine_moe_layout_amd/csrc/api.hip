@@ -122,17 +122,17 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
     hipError_t e;
     if (dtype == MOE_DTYPE_BF16)
         e = moe::launch_dispatch_bf16(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
-                                      recv_topk_w, recv_topk_idx, (hipStream_t)stream);
+                                      recv_topk_w, recv_topk_idx, nullptr, (hipStream_t)stream);
     else
         e = moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
-                                     recv_scale, recv_topk_w, recv_topk_idx, (hipStream_t)stream);
+                                     recv_scale, recv_topk_w, recv_topk_idx, nullptr, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
-int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode, int dtype, int H,
-                        const void *x, const float *topk_w, void *recv_x, float *recv_scale,
-                        float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
-                        void *stream)
+int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t ws_bytes,
+                        int mode, int dtype, int H, const void *x, const float *topk_w, void *recv_x,
+                        float *recv_scale, float *recv_topk_w, int32_t *recv_topk_idx,
+                        int64_t recv_capacity, void *stream)
 {
     if (int rc = check_layout_ptrs(L)) return rc;
     if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
@@ -140,9 +140,7 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode
     if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_B128) return MOE_ERR_BAD_MODE;
     if (H <= 0 || H % 8 != 0) return MOE_ERR_BAD_SHAPE;
     if (dtype == MOE_DTYPE_FP8_E4M3_B128 && H % 128 != 0) return MOE_ERR_BAD_SHAPE;
-    if (L->T > MOE_FUSED_MAX_TOKENS || (int64_t)L->T * L->K > MOE_FUSED_MAX_PAIRS)
-        return MOE_ERR_BAD_SHAPE;
-    if (L->T == 0) return moe_layout(topk_idx, L, nullptr, 0, stream);
+    if (L->T == 0) return moe_layout(topk_idx, L, ws, ws_bytes, stream);
     if (!topk_idx || !x || !topk_w || !recv_x || !recv_topk_w || !recv_topk_idx)
         return MOE_ERR_NULL_PTR;
     if (dtype == MOE_DTYPE_FP8_E4M3_B128 && !recv_scale) return MOE_ERR_NULL_PTR;
@@ -150,10 +148,54 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode
     if (!aligned4(topk_idx) || !aligned16(x) || !aligned16(recv_x) || !aligned4(topk_w) ||
         !aligned4(recv_topk_w) || !aligned4(recv_topk_idx) || (recv_scale && !aligned4(recv_scale)))
         return MOE_ERR_MISALIGNED;
-    hipError_t e = moe::launch_layout_dispatch(topk_idx, L->T, L->K, L->E, L->G, ptrs_of(L), mode,
-                                               dtype == MOE_DTYPE_FP8_E4M3_B128, H, x, topk_w, recv_x,
-                                               recv_scale, recv_topk_w, recv_topk_idx,
-                                               (hipStream_t)stream);
+    const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_B128;
+    hipError_t e;
+    if (L->T <= MOE_FUSED_MAX_TOKENS && (int64_t)L->T * L->K <= MOE_FUSED_MAX_PAIRS) {
+        // small batch: one launch, no workspace
+        e = moe::launch_layout_dispatch(topk_idx, L->T, L->K, L->E, L->G, ptrs_of(L), mode, fp8, H, x,
+                                        topk_w, recv_x, recv_scale, recv_topk_w, recv_topk_idx,
+                                        (hipStream_t)stream);
+        return e == hipSuccess ? MOE_OK : hip_fail(e);
+    }
+    if (!ws || ws_bytes < layout_ws_bytes(L->T, L->E, L->G)) return MOE_ERR_WORKSPACE;
+    if (!aligned4(ws)) return MOE_ERR_MISALIGNED;
+    const moe::LayoutPtrs P = ptrs_of(L);
+    const int nslot = mode == MOE_MODE_EXPERT ? L->K : L->G;
+    const int32_t *slots = mode == MOE_MODE_EXPERT ? L->slot_e : L->slot_tg;
+    // The placing dispatch needs the per-tile masks (K <= 8) and pays its
+    // placement latency once per round of resident workgroups: a single round
+    // for the 128-thread bf16 workgroups, several for the row-sized FP8 ones,
+    // where it measured slower than the two calls. Otherwise: the two calls.
+    if (L->K > 8 || fp8) {
+        e = moe::launch_layout(topk_idx, L->T, L->K, L->E, L->G, P, static_cast<int32_t *>(ws),
+                               (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = fp8 ? moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
+                                               recv_scale, recv_topk_w, recv_topk_idx, nullptr,
+                                               (hipStream_t)stream)
+                    : moe::launch_dispatch_bf16(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
+                                                recv_topk_w, recv_topk_idx, nullptr, (hipStream_t)stream);
+        return e == hipSuccess ? MOE_OK : hip_fail(e);
+    }
+    // count + finalize, then each dispatch workgroup places its own token
+    e = moe::launch_layout_count_finalize(topk_idx, L->T, L->K, L->E, L->G, P, static_cast<int32_t *>(ws),
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e);
+    const moe::LayoutWs w = moe::layout_ws(ws, L->T, L->E, L->G);
+    moe::PlaceArgs pa;
+    pa.idx = topk_idx;
+    pa.E = L->E;
+    pa.G = L->G;
+    pa.gmagic = moe::group_magic(L->E, L->G);
+    pa.words = w.words;
+    pa.gwords = w.gwords;
+    pa.bases = w.bases;
+    pa.L = P;
+    pa.mode = mode == MOE_MODE_EXPERT ? 0 : 1;
+    e = fp8 ? moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, nullptr, topk_w, topk_idx, recv_x, recv_scale,
+                                       recv_topk_w, recv_topk_idx, &pa, (hipStream_t)stream)
+            : moe::launch_dispatch_bf16(x, L->T, H, L->K, nslot, nullptr, topk_w, topk_idx, recv_x,
+                                        recv_topk_w, recv_topk_idx, &pa, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

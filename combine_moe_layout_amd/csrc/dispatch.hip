@@ -30,6 +30,7 @@
 // The quantisation runs once per source token, not once per destination.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "place.hpp"
 
 #include <stdlib.h>
 
@@ -40,28 +41,39 @@ namespace {
 constexpr int kDispatchBS = 128;   // threads per workgroup, bf16
 constexpr int kFp8MaxBS = 1024;    // threads per workgroup, fp8: up to one per 16-element chunk
 constexpr int kMaxIter = 8;
+constexpr int kMaxSlots = 32;      // K or G destinations per token
 
-template <int ITER, bool NT, bool NTL, bool FULL>
+// PLACE: the token's slots are not read from the layout but computed here
+// (place_token; the fused layout + dispatch), after the row's first loads
+// are issued.
+template <int ITER, bool NT, bool NTL, bool FULL, bool PLACE>
 __global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_kernel(
     const u32x4 *__restrict__ x, int nvec, int K, int nslot, const int32_t *__restrict__ slots,
     const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
-    u32x4 *__restrict__ recv_x, float *__restrict__ recv_w, int32_t *__restrict__ recv_idx)
+    u32x4 *__restrict__ recv_x, float *__restrict__ recv_w, int32_t *__restrict__ recv_idx,
+    PlaceArgs P)
 {
+    __shared__ int32_t s_dst[PLACE ? kMaxSlots : 1];
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const u32x4 *src = x + (size_t)t * nvec;
-    const int32_t *ts = slots + (size_t)t * nslot;
+    const int32_t *ts = PLACE ? s_dst : slots + (size_t)t * nslot;
     // receive rows of a valid layout are < T * min(K, nslot) (T = the grid),
     // which the caller's buffers hold; anything else is skipped
     const int64_t rows = (int64_t)gridDim.x * (K < nslot ? K : nslot);
 
-    for (int base = 0; base < nvec; base += kDispatchBS * ITER) {
-        u32x4 v[ITER];
+    u32x4 v[ITER];
+    auto load_pass = [&](int base) {
 #pragma unroll
         for (int i = 0; i < ITER; ++i) {
             const int j = base + i * kDispatchBS + tid;
             if (FULL || j < nvec) v[i] = load16<NTL>(src + j);
         }
+    };
+    load_pass(0);
+    if constexpr (PLACE) place_token(P, t, K, s_dst);
+    for (int base = 0; base < nvec; base += kDispatchBS * ITER) {
+        if (base > 0) load_pass(base);
         for (int d = 0; d < nslot; ++d) {
             const int s = ts[d];
             if (s < 0 || s >= rows) continue;
@@ -100,30 +112,27 @@ __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.
 // One 16-element chunk per lane per pass; the workgroup has as many lanes as
 // the row has chunks (rounded up to whole waves, at most kFp8MaxBS), so a
 // lane holds one chunk's state and occupancy stays high.
-template <bool NT, bool NTL, bool FULL>
+template <bool NT, bool NTL, bool FULL, bool PLACE>
 __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
     const u32x4 *__restrict__ x, int nch, int K, int nslot, const int32_t *__restrict__ slots,
     const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
     u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, float *__restrict__ recv_w,
-    int32_t *__restrict__ recv_idx)
+    int32_t *__restrict__ recv_idx, PlaceArgs P)
 {
+    __shared__ int32_t s_dst[PLACE ? kMaxSlots : 1];
     // nch = H / 16 chunks of 16 elements; a row of x is 2 * nch vectors, a
     // receive row nch vectors of 16 e4m3 bytes, and nch / 8 scales.
     const int t = blockIdx.x;
     const int tid = threadIdx.x;
     const int bs = blockDim.x;
     const u32x4 *src = x + (size_t)t * nch * 2;
-    const int32_t *ts = slots + (size_t)t * nslot;
+    const int32_t *ts = PLACE ? s_dst : slots + (size_t)t * nslot;
     const int nblk = nch / 8;
     const int64_t rows = (int64_t)gridDim.x * (K < nslot ? K : nslot);   // as in the bf16 kernel
 
-    for (int j = tid; FULL ? j < nch : j - tid < nch; j += bs) {
-        const bool in = FULL || j < nch;
-        u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-        if (in) {
-            a = load16<NTL>(src + 2 * j);
-            b = load16<NTL>(src + 2 * j + 1);
-        }
+    // A lane's chunk j: amax of each 128-block over its 8 lanes, the block's
+    // scale, and the 16 packed e4m3 codes.
+    auto quantize = [&](u32x4 a, u32x4 b, u32x4 &q, float &scale) {
         float f[16];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
         amax = fmaxf(amax, __shfl_xor(amax, 1));
         amax = fmaxf(amax, __shfl_xor(amax, 2));
         amax = fmaxf(amax, __shfl_xor(amax, 4));
-        const float scale = amax / 448.f;
+        scale = amax / 448.f;
         const float inv = amax > 0.f ? 448.f / amax : 0.f;
         int w[4];
 #pragma unroll
@@ -148,7 +157,34 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
             p = cvt_pk_e4m3<true>(clamp448(f[4 * m + 2] * inv), clamp448(f[4 * m + 3] * inv), p);
             w[m] = p;
         }
-        const u32x4 q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+        q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+    };
+
+    // The first pass is loaded and quantised before the token is placed
+    // (PLACE), so the placement overlaps it.
+    u32x4 q0;
+    float scale0;
+    {
+        u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+        if (FULL || tid < nch) {
+            a = load16<NTL>(src + 2 * tid);
+            b = load16<NTL>(src + 2 * tid + 1);
+        }
+        quantize(a, b, q0, scale0);
+    }
+    if constexpr (PLACE) place_token(P, t, K, s_dst);
+    for (int j = tid; FULL ? j < nch : j - tid < nch; j += bs) {
+        const bool in = FULL || j < nch;
+        u32x4 q = q0;
+        float scale = scale0;
+        if (j != tid) {   // later passes (rows longer than the workgroup)
+            u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+            if (in) {
+                a = load16<NTL>(src + 2 * j);
+                b = load16<NTL>(src + 2 * j + 1);
+            }
+            quantize(a, b, q, scale);
+        }
         if (in) {
             for (int d = 0; d < nslot; ++d) {
                 const int s = ts[d];
@@ -175,7 +211,11 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
 // Kernel instances by (ITER, NT store, NT load, FULL).
 template <int ITER, bool NT, bool NTL, bool FULL>
 struct Bf16Inst {
-    static constexpr auto fn = dispatch_bf16_kernel<ITER, NT, NTL, FULL>;
+    static constexpr auto fn = dispatch_bf16_kernel<ITER, NT, NTL, FULL, false>;
+};
+template <int ITER, bool NT, bool NTL, bool FULL>
+struct Bf16PlaceInst {
+    static constexpr auto fn = dispatch_bf16_kernel<ITER, NT, NTL, FULL, true>;
 };
 
 template <template <int, bool, bool, bool> class Inst, int ITER>
@@ -230,33 +270,49 @@ const Tuning &tuning()
 
 hipError_t launch_dispatch_bf16(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
                                 const float *topk_w, const int32_t *topk_idx, void *recv_x,
-                                float *recv_w, int32_t *recv_idx, hipStream_t stream)
+                                float *recv_w, int32_t *recv_idx, const PlaceArgs *place,
+                                hipStream_t stream)
 {
     const int nvec = H / 8;
     const int iter = iters_for(nvec, kDispatchBS);
     const bool full = nvec % (kDispatchBS * iter) == 0;
-    auto fn = pick<Bf16Inst>(iter, tuning().dispatch_nt_store, tuning().dispatch_nt_load, full);
+    const bool nt = tuning().dispatch_nt_store, ntl = tuning().dispatch_nt_load;
+    auto fn = place ? pick<Bf16PlaceInst>(iter, nt, ntl, full) : pick<Bf16Inst>(iter, nt, ntl, full);
     hipLaunchKernelGGL(fn, dim3(T), dim3(kDispatchBS), 0, stream, (const u32x4 *)x, nvec, K, nslot,
-                       slots, topk_w, topk_idx, (u32x4 *)recv_x, recv_w, recv_idx);
+                       slots, topk_w, topk_idx, (u32x4 *)recv_x, recv_w, recv_idx,
+                       place ? *place : PlaceArgs{});
     return hipGetLastError();
 }
+
+namespace {
+
+template <bool PLACE>
+auto pick_fp8(bool nt, bool ntl, bool full)
+{
+    if (nt) {
+        if (ntl) return full ? dispatch_fp8_kernel<true, true, true, PLACE> : dispatch_fp8_kernel<true, true, false, PLACE>;
+        return full ? dispatch_fp8_kernel<true, false, true, PLACE> : dispatch_fp8_kernel<true, false, false, PLACE>;
+    }
+    if (ntl) return full ? dispatch_fp8_kernel<false, true, true, PLACE> : dispatch_fp8_kernel<false, true, false, PLACE>;
+    return full ? dispatch_fp8_kernel<false, false, true, PLACE> : dispatch_fp8_kernel<false, false, false, PLACE>;
+}
+
+}  // namespace
 
 hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
                                const float *topk_w, const int32_t *topk_idx, void *recv_q,
                                float *recv_scale, float *recv_w, int32_t *recv_idx,
-                               hipStream_t stream)
+                               const PlaceArgs *place, hipStream_t stream)
 {
     const int nch = H / 16;
     int bs = (nch + kWave - 1) / kWave * kWave;
     if (bs > kFp8MaxBS) bs = kFp8MaxBS;
     const bool full = nch % bs == 0;
     const bool nt = tuning().dispatch_nt_store, ntl = tuning().dispatch_nt_load;
-    auto fn = nt ? (ntl ? (full ? dispatch_fp8_kernel<true, true, true> : dispatch_fp8_kernel<true, true, false>)
-                        : (full ? dispatch_fp8_kernel<true, false, true> : dispatch_fp8_kernel<true, false, false>))
-                 : (ntl ? (full ? dispatch_fp8_kernel<false, true, true> : dispatch_fp8_kernel<false, true, false>)
-                        : (full ? dispatch_fp8_kernel<false, false, true> : dispatch_fp8_kernel<false, false, false>));
+    auto fn = place ? pick_fp8<true>(nt, ntl, full) : pick_fp8<false>(nt, ntl, full);
     hipLaunchKernelGGL(fn, dim3(T), dim3(bs), 0, stream, (const u32x4 *)x, nch, K, nslot, slots,
-                       topk_w, topk_idx, (u32x4 *)recv_q, recv_scale, recv_w, recv_idx);
+                       topk_w, topk_idx, (u32x4 *)recv_q, recv_scale, recv_w, recv_idx,
+                       place ? *place : PlaceArgs{});
     return hipGetLastError();
 }
 

@@ -13,17 +13,41 @@ namespace moe {
 constexpr int kLayoutTile = 256;
 
 inline int layout_tiles(int T) { return (T + kLayoutTile - 1) / kLayoutTile; }
-// Layout workspace: the count table [tiles][E + G + 1] int32 (padded to a
-// multiple of 64 words), then the per-tile LDS words [tiles][E][4] as 32-bit
-// halves (used for top-k <= 8).
+
+// Layout workspace, in 32-bit words:
+//   table  [tiles][E + G + 1]   per-tile expert counts, group counts, error bits
+//                               (padded to a multiple of 64 words)
+//   words  [tiles][E][4][2]     per-(expert, wave) token masks of each tile, as
+//                               32-bit halves (top-k <= 8)
+//   gwords [tiles][G][4][2]     per-(group, wave) token masks (top-k <= 8)
+//   bases  [tiles][E + G]       first receive row of each tile in each expert
+//                               (group) segment: the segment's offset plus the
+//                               counts of the tiles before (fused path only)
+struct LayoutWs {
+    int32_t *table;
+    uint32_t *words, *gwords;
+    int32_t *bases;
+};
 inline size_t layout_table_words(int tiles, int E, int G)
 {
     return ((size_t)tiles * (E + G + 1) + 63) & ~(size_t)63;
 }
-inline size_t layout_ws_bytes_for(int T, int E, int G)
+inline size_t layout_ws_words(int T, int E, int G)
 {
-    const int tiles = layout_tiles(T);
-    return 4 * (layout_table_words(tiles, E, G) + (size_t)tiles * E * 4 * 2);
+    const size_t tiles = (size_t)layout_tiles(T);
+    return layout_table_words((int)tiles, E, G) + tiles * E * 8 + tiles * G * 8 + tiles * (E + G);
+}
+inline size_t layout_ws_bytes_for(int T, int E, int G) { return 4 * layout_ws_words(T, E, G); }
+inline LayoutWs layout_ws(void *ws, int T, int E, int G)
+{
+    const size_t tiles = (size_t)layout_tiles(T);
+    int32_t *base = static_cast<int32_t *>(ws);
+    LayoutWs w;
+    w.table = base;
+    w.words = reinterpret_cast<uint32_t *>(base + layout_table_words((int)tiles, E, G));
+    w.gwords = w.words + tiles * E * 8;
+    w.bases = reinterpret_cast<int32_t *>(w.gwords + tiles * G * 8);
+    return w;
 }
 
 struct LayoutPtrs {
@@ -32,10 +56,33 @@ struct LayoutPtrs {
     int32_t *slot_e, *slot_g, *slot_tg, *recv_src_e, *recv_src_g, *status;
 };
 
-// Workspace: a tile-major table [tiles][E + G + 1] of expert counts, group
-// counts and error bits per tile.
+// moe_layout: count + place kernels (ws: the layout workspace above).
 hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L,
                          int32_t *ws, hipStream_t stream);
+
+// First half of the fused layout + dispatch for T > the small-batch limit
+// and top-k <= 8: the count kernel, then one workgroup that writes the
+// counts, offsets and status and each tile's bases into the workspace. The
+// dispatch kernels then place each token themselves (PlaceArgs).
+hipError_t launch_layout_count_finalize(const int32_t *idx, int T, int K, int E, int G,
+                                        const LayoutPtrs &L, int32_t *ws, hipStream_t stream);
+
+// What a dispatch kernel needs to compute its token's slots and write the
+// token's layout entries (see place_token in place.hpp).
+struct PlaceArgs {
+    const int32_t *idx;
+    int E, G;
+    uint32_t gmagic;
+    const uint32_t *words, *gwords;
+    const int32_t *bases;
+    LayoutPtrs L;
+    int mode;   // destinations: slot_e (0) or slot_tg (1)
+};
+inline uint32_t group_magic(int E, int G)
+{
+    const int epg = E / G;
+    return epg == 1 ? 0u : (uint32_t)((1ull << 32) / (unsigned)epg) + 1u;
+}
 
 // Cache policy of the dispatch row loads and stores. Defaults are the
 // measured best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1 in the
@@ -47,14 +94,17 @@ struct Tuning {
 const Tuning &tuning();
 
 // BF16 dispatch. slots: [T, nslot] (slot_e with nslot = K, or slot_tg with nslot = G).
+// place: NULL to read the destinations from `slots`, else the token's slots
+// are computed in the kernel (fused layout + dispatch; `slots` unused).
 hipError_t launch_dispatch_bf16(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
                                 const float *topk_w, const int32_t *topk_idx, void *recv_x,
-                                float *recv_w, int32_t *recv_idx, hipStream_t stream);
+                                float *recv_w, int32_t *recv_idx, const PlaceArgs *place,
+                                hipStream_t stream);
 
 hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
                                const float *topk_w, const int32_t *topk_idx, void *recv_q,
                                float *recv_scale, float *recv_w, int32_t *recv_idx,
-                               hipStream_t stream);
+                               const PlaceArgs *place, hipStream_t stream);
 
 // Combine. slot: [T, K] (slot_e, or slot_g whose entries may repeat within a token).
 hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, const int32_t *slot,

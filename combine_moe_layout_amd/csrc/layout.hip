@@ -150,15 +150,18 @@ __device__ __forceinline__ Inserted classify_token(const int (&e)[KMAX], bool li
 
 // Count kernel: one tile per workgroup. Writes row `tile` of the tile-major
 // count table: E expert counts, G group counts, then the tile's error bits;
-// for top-k <= 8 also the tile's E x 4 words (as 32-bit halves), which the
-// place kernel loads instead of rebuilding them.
+// for top-k <= 8 also the tile's E x 4 expert words and G x 4 group words
+// (as 32-bit halves), which the place kernel, or a dispatch kernel placing
+// its own token, loads instead of rebuilding them.
 template <int KMAX, bool EXACT>
 __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic,
-    uint32_t *__restrict__ tok_group_mask, int32_t *__restrict__ table, uint32_t *__restrict__ words)
+    uint32_t *__restrict__ tok_group_mask, int32_t *__restrict__ table, uint32_t *__restrict__ words,
+    uint32_t *__restrict__ gwords)
 {
     extern __shared__ unsigned long long emask[];   // [E][kWaves]
     __shared__ int gcnt[kMaxG][kWaves];
+    __shared__ unsigned long long gball[kMaxG][kWaves];
     __shared__ int s_err;
     const int K = EXACT ? KMAX : Krt;   // a compile-time constant for the common top-k
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -177,7 +180,10 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     if (t < T) tok_group_mask[t] = gm;
     for (int g = 0; g < G; ++g) {
         const uint64_t b = __ballot((gm >> g) & 1u);
-        if (lane == 0) gcnt[g][wave] = __popcll(b);
+        if (lane == 0) {
+            gcnt[g][wave] = __popcll(b);
+            gball[g][wave] = b;
+        }
     }
     if (err) atomicOr(&s_err, err);
     __syncthreads();
@@ -195,6 +201,12 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
             const unsigned long long w = emask[i];
             wt[2 * i] = (uint32_t)w;
             wt[2 * i + 1] = (uint32_t)(w >> 32);
+        }
+        if (tid < G * kWaves) {
+            const unsigned long long w = gball[tid / kWaves][tid % kWaves];
+            uint32_t *gt = gwords + (size_t)tile * G * kWaves * 2;
+            gt[2 * tid] = (uint32_t)w;
+            gt[2 * tid + 1] = (uint32_t)(w >> 32);
         }
     }
 }
@@ -540,6 +552,120 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     }
 }
 
+constexpr int kFinBS = 1024;                  // finalize: one workgroup, a thread per expert
+constexpr int kFinWaves = kFinBS / kWave;
+
+// Exclusive prefix sum over the 1024 threads of the finalize workgroup.
+__device__ __forceinline__ int fin_scan(int v, int *s_wave_tot, int &total)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) s_wave_tot[wave] = x;
+    __syncthreads();
+    int base = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kFinWaves; ++w) {
+        const int c = s_wave_tot[w];
+        base += w < wave ? c : 0;
+        all += c;
+    }
+    total = all;
+    return base + x - v;
+}
+
+// Finalize (fused layout + dispatch): one workgroup. A column's total over the
+// tiles is an expert's (group's) count, the exclusive prefix of the totals its
+// offset, and a tile's base in the column the offset plus the counts of the
+// tiles before it. Writes the counts, offsets and status of the layout and the
+// bases [tiles][E + G] into the workspace.
+__global__ __launch_bounds__(kFinBS) void layout_finalize_kernel(
+    int ntiles, int E, int G, const int32_t *__restrict__ table, int32_t *__restrict__ bases, LayoutPtrs L)
+{
+    __shared__ int s_wave_tot[kFinWaves];
+    __shared__ int s_err;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int rows = E + G + 1, cols = E + G;
+    const int xe = tid < E ? tid : E - 1;   // this thread's expert column (clamped)
+    const int xg = tid < G ? tid : G - 1;   // and group column
+    // every first load before any use (one round trip; see column_first)
+    int ce[kBatch], cg[kBatch];
+    column_first(table, rows, xe, ntiles, ce);
+    column_first(table, rows, E + xg, ntiles, cg);
+    const int er_v = table[(size_t)(tid < ntiles ? tid : ntiles - 1) * rows + E + G];
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid == 0) s_err = 0;
+
+    int te = 0, tg = 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        te += u < ntiles ? ce[u] : 0;
+        tg += u < ntiles ? cg[u] : 0;
+    }
+    for (int b = kBatch; b < ntiles; ++b) {
+        te += table[(size_t)b * rows + xe];
+        tg += table[(size_t)b * rows + E + xg];
+    }
+    te = tid < E ? te : 0;
+    __syncthreads();   // s_err cleared
+    int er = tid < ntiles ? er_v : 0;
+    for (int b = tid + kFinBS; b < ntiles; b += kFinBS) er |= table[(size_t)b * rows + E + G];
+    if (er) atomicOr(&s_err, er);
+
+    int etot;
+    const int eoff = fin_scan(te, s_wave_tot, etot);
+    if (tid < E) {
+        L.expert_count[tid] = te;
+        L.expert_offset[tid] = eoff;
+        int r = eoff;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (u < ntiles) {
+                bases[(size_t)u * cols + tid] = r;
+                r += ce[u];
+            }
+        }
+        for (int b = kBatch; b < ntiles; ++b) {
+            bases[(size_t)b * cols + tid] = r;
+            r += table[(size_t)b * rows + tid];
+        }
+    }
+    if (tid == 0) L.expert_offset[E] = etot;
+    if (wave == 0) {   // groups: an exclusive scan over the G <= 32 totals in wave 0
+        const int gt = lane < G ? tg : 0;
+        int incl = gt;
+#pragma unroll
+        for (int o = 1; o < kMaxG; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane < G) {
+            const int goff = incl - gt;
+            L.group_count[lane] = gt;
+            L.group_offset[lane] = goff;
+            int r = goff;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (u < ntiles) {
+                    bases[(size_t)u * cols + E + lane] = r;
+                    r += cg[u];
+                }
+            }
+            for (int b = kBatch; b < ntiles; ++b) {
+                bases[(size_t)b * cols + E + lane] = r;
+                r += table[(size_t)b * rows + E + lane];
+            }
+        }
+        if (lane == G - 1) L.group_offset[G] = incl;
+    }
+    __syncthreads();   // s_err complete
+    if (tid == 0) *L.status = s_err;
+}
+
 // No tokens: every count and offset is 0 and the status is clear.
 __global__ __launch_bounds__(kLayoutTile) void layout_empty_kernel(int E, int G, LayoutPtrs L)
 {
@@ -556,27 +682,15 @@ __global__ __launch_bounds__(kLayoutTile) void layout_empty_kernel(int E, int G,
 
 }  // namespace
 
-hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L,
-                         int32_t *ws, hipStream_t stream)
+namespace {
+
+using CountFn = void (*)(const int32_t *, int, int, int, int, uint32_t, uint32_t *, int32_t *, uint32_t *,
+                         uint32_t *);
+using PlaceFn = void (*)(const int32_t *, int, int, int, int, uint32_t, int, const int32_t *,
+                         const uint32_t *, LayoutPtrs, int);
+
+void pick_layout(int K, CountFn &count, PlaceFn &place)
 {
-    if (T == 0) {
-        hipLaunchKernelGGL(layout_empty_kernel, dim3(1), dim3(kLayoutTile), 0, stream, E, G, L);
-        return hipGetLastError();
-    }
-    const int ntiles = layout_tiles(T);
-    uint32_t *words = reinterpret_cast<uint32_t *>(ws) + layout_table_words(ntiles, E, G);
-    const int epg = E / G;
-    const uint32_t gmagic = epg == 1 ? 0u : (uint32_t)((1ull << 32) / (unsigned)epg) + 1u;
-    const size_t lds1 = (size_t)E * kWaves * sizeof(unsigned long long);
-    const size_t lds2 = lds1 + (size_t)E * (kWaves + 1) * sizeof(int);
-    // vector stores of the slot rows when the arrays allow them
-    const auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-    const int vec = (a16(L.slot_e) && a16(L.slot_g) ? 1 : 0) | (G % 4 == 0 && a16(L.slot_tg) ? 2 : 0);
-    using CountFn = void (*)(const int32_t *, int, int, int, int, uint32_t, uint32_t *, int32_t *, uint32_t *);
-    using PlaceFn = void (*)(const int32_t *, int, int, int, int, uint32_t, int, const int32_t *,
-                             const uint32_t *, LayoutPtrs, int);
-    CountFn count;
-    PlaceFn place;
     switch (K) {
     case 2: count = layout_count_kernel<2, true>; place = layout_place_kernel<2, true>; break;
     case 4: count = layout_count_kernel<4, true>; place = layout_place_kernel<4, true>; break;
@@ -585,12 +699,52 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
         if (K <= 8) { count = layout_count_kernel<8, false>; place = layout_place_kernel<8, false>; }
         else { count = layout_count_kernel<32, false>; place = layout_place_kernel<32, false>; }
     }
+}
+
+}  // namespace
+
+hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L,
+                         int32_t *ws, hipStream_t stream)
+{
+    if (T == 0) {
+        hipLaunchKernelGGL(layout_empty_kernel, dim3(1), dim3(kLayoutTile), 0, stream, E, G, L);
+        return hipGetLastError();
+    }
+    const int ntiles = layout_tiles(T);
+    const LayoutWs w = layout_ws(ws, T, E, G);
+    const uint32_t gmagic = group_magic(E, G);
+    const size_t lds1 = (size_t)E * kWaves * sizeof(unsigned long long);
+    const size_t lds2 = lds1 + (size_t)E * (kWaves + 1) * sizeof(int);
+    // vector stores of the slot rows when the arrays allow them
+    const auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    const int vec = (a16(L.slot_e) && a16(L.slot_g) ? 1 : 0) | (G % 4 == 0 && a16(L.slot_tg) ? 2 : 0);
+    CountFn count;
+    PlaceFn place;
+    pick_layout(K, count, place);
     hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G, gmagic,
-                       L.tok_group_mask, ws, words);
+                       L.tok_group_mask, w.table, w.words, w.gwords);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(place, dim3(ntiles), dim3(kLayoutTile), lds2, stream, idx, T, K, E, G, gmagic,
-                       ntiles, static_cast<const int32_t *>(ws), words, L, vec);
+                       ntiles, w.table, w.words, L, vec);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_count_finalize(const int32_t *idx, int T, int K, int E, int G,
+                                        const LayoutPtrs &L, int32_t *ws, hipStream_t stream)
+{
+    const int ntiles = layout_tiles(T);
+    const LayoutWs w = layout_ws(ws, T, E, G);
+    CountFn count;
+    PlaceFn place;
+    pick_layout(K, count, place);
+    const size_t lds1 = (size_t)E * kWaves * sizeof(unsigned long long);
+    hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G,
+                       group_magic(E, G), L.tok_group_mask, w.table, w.words, w.gwords);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(layout_finalize_kernel, dim3(1), dim3(kFinBS), 0, stream, ntiles, E, G, w.table,
+                       w.bases, L);
     return hipGetLastError();
 }
 

@@ -31,14 +31,14 @@
 extern "C" {
 #endif
 
-#define MOE_EP_ABI_VERSION 1
+#define MOE_EP_ABI_VERSION 2
 
 /* Limits checked at the boundary. */
 #define MOE_MAX_EXPERTS 1024 /* E */
 #define MOE_MAX_GROUPS 32    /* G: a token's groups form one 32-bit mask */
 #define MOE_MAX_TOPK 32      /* K */
-#define MOE_FUSED_MAX_TOKENS 512   /* T for moe_layout_dispatch() */
-#define MOE_FUSED_MAX_PAIRS 16384  /* T * K for moe_layout_dispatch() */
+#define MOE_FUSED_MAX_TOKENS 512   /* T of moe_layout_dispatch()'s one-launch form */
+#define MOE_FUSED_MAX_PAIRS 16384  /* T * K of moe_layout_dispatch()'s one-launch form */
 
 enum moe_error {
     MOE_OK = 0,
@@ -159,20 +159,26 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
                  float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
                  void *stream);
 
-/* Low-latency form for small batches: moe_layout() and moe_dispatch() in one
- * launch. The layout arrays and the receive buffers it writes are, bit for
- * bit, those the two calls write (layout->status included); no workspace is
- * needed. One workgroup per token recomputes the routing it needs from the
- * whole index array, so the cost grows as T^2: limited to
- * T <= MOE_FUSED_MAX_TOKENS and T * K <= MOE_FUSED_MAX_PAIRS (else
- * MOE_ERR_BAD_SHAPE). Arguments as for moe_layout() and moe_dispatch().
+/* moe_layout() and moe_dispatch() as one call. The layout arrays and the
+ * receive buffers it writes are, bit for bit, those the two calls write
+ * (layout->status included). Arguments as for moe_layout() and moe_dispatch().
+ * Small batches (T <= MOE_FUSED_MAX_TOKENS and T * K <= MOE_FUSED_MAX_PAIRS)
+ * take one launch and need no workspace (ws may be NULL): one workgroup per
+ * token recomputes the routing it needs from the whole index array, a cost
+ * that grows as T^2. Larger batches need ws (moe_layout_workspace_bytes()):
+ * for BF16 with K <= 8 the layout's count kernel and one workgroup that
+ * computes the offsets run first, and each dispatch workgroup then computes
+ * its own token's slots from the per-tile token masks while its row loads are
+ * in flight, so the separate placement launch of moe_layout() disappears;
+ * otherwise (FP8, or K > 8) the call runs moe_layout() and moe_dispatch().
  * Source: mori pull request 586, the IntraNodeLL reply in its review thread
  * (single-pass per-token routing, one block per token, copy fused in; latency
- * dominates at small token counts). */
-int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode, int dtype, int H,
-                        const void *x, const float *topk_w, void *recv_x, float *recv_scale,
-                        float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
-                        void *stream);
+ * dominates at small token counts) and its profiling section (routing
+ * overhead is what separates dispatch from combine). */
+int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t ws_bytes,
+                        int mode, int dtype, int H, const void *x, const float *topk_w, void *recv_x,
+                        float *recv_scale, float *recv_topk_w, int32_t *recv_topk_idx,
+                        int64_t recv_capacity, void *stream);
 
 /* Receive-side regroup: the arrays of a per-group (GROUP) dispatch result ->
  * the per-expert (EXPERT) layout, i.e. for every EXPERT row r with pair

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(moe):
     lib = ctypes.CDLL(moe.library_path())
     missing = [n for n in header_functions() if not hasattr(lib, n)]
     assert not missing, missing
-    assert moe._lib.moe_abi_version() == 1
+    assert moe._lib.moe_abi_version() == 2
 
 
 def test_query_functions(moe):
@@ -109,10 +109,13 @@ def test_host_validation_errors(moe):
     assert d(x=M) == -3 and d(rx=M) == -3
     assert d(x=NULL) == -1
     assert d(Lp=_fake_layout(moe, T=0), x=NULL) == 0
-    # fused layout + dispatch: small batches only
-    f = lambda T=16, K=2, H=2048, cap=32: lib.moe_layout_dispatch(
-        A, ref(_fake_layout(moe, T=T, K=K, E=64, G=8)), 0, 0, H, A, A, A, NULL, A, A, cap, NULL)
-    assert f(T=513, cap=513 * 2) == -2
+    # fused layout + dispatch: a workspace beyond the one-launch sizes
+    f = lambda T=16, K=2, H=2048, cap=32, ws=NULL, nb=0: lib.moe_layout_dispatch(
+        A, ref(_fake_layout(moe, T=T, K=K, E=64, G=8)), ws, nb, 0, 0, H, A, A, A, NULL, A, A, cap, NULL)
+    assert f(T=513, cap=513 * 2) == -5          # no workspace
+    need = moe.layout_workspace_bytes(513, 2, 64, 8)
+    assert f(T=513, cap=513 * 2, ws=A, nb=need - 4) == -5
+    assert f(T=513, cap=513 * 2, ws=M, nb=need) == -3
     assert f(T=512, K=33) == -2                 # K > 32
     assert f(T=16, H=12) == -2
     assert f(T=16, cap=31) == -4

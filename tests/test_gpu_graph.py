@@ -32,7 +32,9 @@ def _u16_to_bf16_tensor(a):
 
 
 # (T, H, E, G, K, fused): fused = capture moe_layout_dispatch instead of the two calls
-CASES = [(700, 1024, 64, 8, 6, False), (300, 512, 32, 4, 8, True), (2000, 2048, 256, 8, 8, False)]
+# (one launch for T <= 512; count, offsets and a placing dispatch above)
+CASES = [(700, 1024, 64, 8, 6, False), (300, 512, 32, 4, 8, True), (2000, 2048, 256, 8, 8, False),
+         (2000, 2048, 256, 8, 8, True), (1500, 512, 64, 8, 6, True)]
 
 
 @pytest.mark.parametrize("T,H,E,G,K,fused", CASES)

@@ -435,12 +435,14 @@ def test_stream_ordering_on_side_stream(moe, orc):
     np.testing.assert_array_equal(host_u16(out), d["x"])
 
 
-# ------------------------------------------------------------------ fused layout + dispatch (small batches)
+# ------------------------------------------------------------------ fused layout + dispatch
 
-FUSED_SHAPES = [  # (T, H, E, G, K)
+FUSED_SHAPES = [  # (T, H, E, G, K); T <= 512: one launch; larger: count + offsets + placing dispatch
     (1, 8, 8, 8, 2), (16, 2048, 8, 8, 2), (256, 7168, 256, 8, 8), (512, 1024, 64, 8, 8),
     (300, 520, 16, 4, 3), (100, 1024, 1024, 32, 32), (511, 4096, 128, 1, 8), (77, 2048, 7, 7, 1),
     (257, 1152, 96, 4, 6),
+    (513, 1024, 64, 8, 8), (1000, 512, 32, 4, 3), (2000, 256, 16, 16, 1), (777, 384, 40, 1, 5),
+    (600, 256, 64, 8, 13), (4097, 2048, 256, 8, 8), (3000, 128, 1024, 32, 8),
 ]
 
 
@@ -482,8 +484,41 @@ def test_fused_layout_dispatch_matches_oracle(moe, orc, T, H, E, G, K, mode, dty
         fp8_check(D, orc.dispatch_fp8(Lo, mode, d["x"], d["topk_w"], idx))
 
 
-def test_fused_layout_dispatch_equals_two_calls(moe):
-    d = workload("t256")
+@pytest.mark.parametrize("name", ["t4096", "skew", "fp8"])
+@pytest.mark.parametrize("mode", MODES)
+def test_fused_layout_dispatch_full_workloads(moe, orc, name, mode):
+    d = workload(name)
+    wl = d["workload"]
+    dtype = "fp8" if wl.fp8 else "bf16"
+    idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
+    L = moe.Layout.empty(wl.T, wl.K, wl.E, wl.G)
+    D = moe.alloc_dispatch(L, wl.H, mode, dtype)
+    if dtype == "bf16":
+        D.recv_x.view(torch.int16).fill_(int(CANARY16.astype(np.int16)))
+    else:
+        D.recv_x.fill_(0xA5)
+        D.recv_scale.fill_(-1.5)
+    L, D = moe.moe_layout_dispatch(idx_d, wl.E, wl.G, x_d, w_d, mode, dtype, out_layout=L, out=D)
+    Lo = orc.layout(d["topk_idx"], wl.E, wl.G)
+    check_layout(L, Lo)
+    for n in ("recv_src_e", "tok_group_mask"):
+        R = Lo["R_expert"] if n == "recv_src_e" else wl.T
+        assert np.array_equal(getattr(L, n).cpu().numpy()[:R].view(np.int32), Lo[n][:R].view(np.int32)), n
+    P = Lo["R_group"]
+    assert np.array_equal(L.recv_src_g.cpu().numpy()[:P], Lo["recv_src_g"][:P])
+    if dtype == "bf16":
+        Do = orc.dispatch_bf16(Lo, mode, d["x"], d["topk_w"], d["topk_idx"])
+        got = host_u16(D.recv_x)
+        np.testing.assert_array_equal(got[:Do["R"]], Do["recv_x"])
+        assert np.all(got[Do["R"]:] == CANARY16)
+        np.testing.assert_array_equal(D.recv_topk_idx.cpu().numpy()[:Do["R"]], Do["recv_idx"])
+    else:
+        fp8_check(D, orc.dispatch_fp8(Lo, mode, d["x"], d["topk_w"], d["topk_idx"]))
+
+
+@pytest.mark.parametrize("name", ["t256", "t4096"])
+def test_fused_layout_dispatch_equals_two_calls(moe, name):
+    d = workload(name)
     wl = d["workload"]
     idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
     for mode in MODES:
@@ -493,6 +528,9 @@ def test_fused_layout_dispatch_equals_two_calls(moe):
         torch.cuda.synchronize()
         for n in LAYOUT_ARRAYS + ("tok_group_mask",):
             assert torch.equal(getattr(L1, n), getattr(L2, n)), n
+        Re, Pg = int(L1.expert_offset[wl.E].item()), int(L1.group_offset[wl.G].item())
+        assert torch.equal(L1.recv_src_e[:Re], L2.recv_src_e[:Re])
+        assert torch.equal(L1.recv_src_g[:Pg], L2.recv_src_g[:Pg])
         R = int(L1.rows(mode).item())
         assert torch.equal(D1.recv_x[:R].view(torch.int16), D2.recv_x[:R].view(torch.int16))
         out1 = moe.moe_combine(L1, D1.recv_x, w_d, mode)
