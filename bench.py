@@ -56,7 +56,7 @@ def combine_bytes(T, H, K, R):
 
 # Source files that define each timed kernel (plus the shared device helpers).
 KERNEL_SOURCES = {
-    "dispatch": ("dispatch.hip", "common.hpp", "kernels.hpp"),
+    "dispatch": ("dispatch.hip", "place.hpp", "common.hpp", "kernels.hpp"),
     "combine": ("combine.hip", "common.hpp", "kernels.hpp"),
     "layout": ("layout.hip", "common.hpp", "kernels.hpp"),
 }
