@@ -163,10 +163,11 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
     const int nslot = mode == MOE_MODE_EXPERT ? L->K : L->G;
     const int32_t *slots = mode == MOE_MODE_EXPERT ? L->slot_e : L->slot_tg;
     // The placing dispatch needs the per-tile masks (K <= 8) and pays its
-    // placement latency once per round of resident workgroups: a single round
-    // for the 128-thread bf16 workgroups, several for the row-sized FP8 ones,
-    // where it measured slower than the two calls. Otherwise: the two calls.
-    if (L->K > 8 || fp8) {
+    // placement latency once per round of resident workgroups: few rounds for
+    // the 128-thread bf16 and one-wave FP8 workgroups, several for the
+    // row-sized FP8 ones (H > 8192), where it measured slower than the two
+    // calls. Otherwise: the two calls.
+    if (L->K > 8 || (fp8 && !moe::fp8_wave_form(H))) {
         e = moe::launch_layout(topk_idx, L->T, L->K, L->E, L->G, P, static_cast<int32_t *>(ws),
                                (hipStream_t)stream);
         if (e == hipSuccess)

@@ -109,6 +109,37 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
+// One lane's 16-element chunk (a, b: 16 bf16): the amax of its 128-block over
+// the block's 8 lanes (8 consecutive lanes of a wave; every lane of the wave
+// must call this together), the block's scale, and the 16 packed e4m3 codes.
+__device__ __forceinline__ void quantize16(u32x4 a, u32x4 b, u32x4 &q, float &scale)
+{
+    float f[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f[2 * m] = bf16_lo(a[m]);
+        f[2 * m + 1] = bf16_hi(a[m]);
+        f[8 + 2 * m] = bf16_lo(b[m]);
+        f[8 + 2 * m + 1] = bf16_hi(b[m]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(f[m]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    scale = amax / 448.f;
+    const float inv = amax > 0.f ? 448.f / amax : 0.f;
+    int w[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        int p = cvt_pk_e4m3<false>(clamp448(f[4 * m] * inv), clamp448(f[4 * m + 1] * inv), 0);
+        p = cvt_pk_e4m3<true>(clamp448(f[4 * m + 2] * inv), clamp448(f[4 * m + 3] * inv), p);
+        w[m] = p;
+    }
+    q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+}
+
 // One 16-element chunk per lane per pass; the workgroup has as many lanes as
 // the row has chunks (rounded up to whole waves, at most kFp8MaxBS), so a
 // lane holds one chunk's state and occupancy stays high.
@@ -130,36 +161,6 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
     const int nblk = nch / 8;
     const int64_t rows = (int64_t)gridDim.x * (K < nslot ? K : nslot);   // as in the bf16 kernel
 
-    // A lane's chunk j: amax of each 128-block over its 8 lanes, the block's
-    // scale, and the 16 packed e4m3 codes.
-    auto quantize = [&](u32x4 a, u32x4 b, u32x4 &q, float &scale) {
-        float f[16];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f[2 * m] = bf16_lo(a[m]);
-            f[2 * m + 1] = bf16_hi(a[m]);
-            f[8 + 2 * m] = bf16_lo(b[m]);
-            f[8 + 2 * m + 1] = bf16_hi(b[m]);
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(f[m]));
-        // the 8 lanes of one 128-element block are lanes 8c .. 8c+7 of a wave
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        amax = fmaxf(amax, __shfl_xor(amax, 4));
-        scale = amax / 448.f;
-        const float inv = amax > 0.f ? 448.f / amax : 0.f;
-        int w[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            int p = cvt_pk_e4m3<false>(clamp448(f[4 * m] * inv), clamp448(f[4 * m + 1] * inv), 0);
-            p = cvt_pk_e4m3<true>(clamp448(f[4 * m + 2] * inv), clamp448(f[4 * m + 3] * inv), p);
-            w[m] = p;
-        }
-        q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
-    };
-
     // The first pass is loaded and quantised before the token is placed
     // (PLACE), so the placement overlaps it.
     u32x4 q0;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
             a = load16<NTL>(src + 2 * tid);
             b = load16<NTL>(src + 2 * tid + 1);
         }
-        quantize(a, b, q0, scale0);
+        quantize16(a, b, q0, scale0);
     }
     if constexpr (PLACE) place_token(P, t, K, s_dst);
     for (int j = tid; FULL ? j < nch : j - tid < nch; j += bs) {
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
                 a = load16<NTL>(src + 2 * j);
                 b = load16<NTL>(src + 2 * j + 1);
             }
-            quantize(a, b, q, scale);
+            quantize16(a, b, q, scale);
         }
         if (in) {
             for (int d = 0; d < nslot; ++d) {
@@ -205,6 +206,67 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
         if (s < 0 || s >= rows) continue;
         if (wl) recv_w[(size_t)s * K + tid] = wv;
         if (il) recv_idx[(size_t)s * K + tid - K] = iv;
+    }
+}
+
+// Small workgroups (BS = 64 or 128 lanes per token, H <= 16 * BS * 8): lane
+// l holds chunks l, l + BS, ..., l + BS (ITER - 1), so a 128-block is still
+// 8 consecutive lanes in every pass, and more workgroups are resident at once
+// than with the row-sized workgroups above.
+template <int BS, int ITER, bool NT, bool NTL, bool PLACE>
+__global__ __launch_bounds__(BS) void dispatch_fp8_wave_kernel(
+    const u32x4 *__restrict__ x, int nch, int K, int nslot, const int32_t *__restrict__ slots,
+    const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
+    u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, float *__restrict__ recv_w,
+    int32_t *__restrict__ recv_idx, PlaceArgs P)
+{
+    __shared__ int32_t s_dst[PLACE ? kMaxSlots : 1];
+    const int t = blockIdx.x;
+    const int lane = threadIdx.x;   // lane of the workgroup
+    const u32x4 *src = x + (size_t)t * nch * 2;
+    const int32_t *ts = PLACE ? s_dst : slots + (size_t)t * nslot;
+    const int nblk = nch / 8;
+    const int64_t rows = (int64_t)gridDim.x * (K < nslot ? K : nslot);   // as in the bf16 kernel
+
+    u32x4 q[ITER];
+    float sc[ITER];
+    {
+        u32x4 a[ITER], b[ITER];
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int j = lane + i * BS;
+            a[i] = b[i] = u32x4{0, 0, 0, 0};
+            if (j < nch) {
+                a[i] = load16<NTL>(src + 2 * j);
+                b[i] = load16<NTL>(src + 2 * j + 1);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) quantize16(a[i], b[i], q[i], sc[i]);
+    }
+    if constexpr (PLACE) place_token(P, t, K, s_dst);
+    for (int d = 0; d < nslot; ++d) {
+        const int s = ts[d];
+        if (s < 0 || s >= rows) continue;
+#pragma unroll
+        for (int i = 0; i < ITER; ++i) {
+            const int j = lane + i * BS;
+            if (j < nch) {
+                store16<NT>(recv_q + (size_t)s * nch + j, q[i]);
+                if ((lane & 7) == 0) recv_scale[(size_t)s * nblk + (j >> 3)] = sc[i];
+            }
+        }
+    }
+    const bool wl = lane < K, il = lane >= K && lane < 2 * K;
+    float wv = 0.f;
+    int iv = 0;
+    if (wl) wv = topk_w[(size_t)t * K + lane];
+    if (il) iv = topk_idx[(size_t)t * K + lane - K];
+    for (int d = 0; d < nslot; ++d) {
+        const int s = ts[d];
+        if (s < 0 || s >= rows) continue;
+        if (wl) recv_w[(size_t)s * K + lane] = wv;
+        if (il) recv_idx[(size_t)s * K + lane - K] = iv;
     }
 }
 
@@ -263,6 +325,7 @@ const Tuning &tuning()
         };
         env("MOE_EP_DISPATCH_NT_LOAD", r.dispatch_nt_load);
         env("MOE_EP_DISPATCH_NT_STORE", r.dispatch_nt_store);
+        if (const char *f = getenv("MOE_EP_FP8_FORM")) r.fp8_form = atoi(f);
         return r;
     }();
     return t;
@@ -299,16 +362,63 @@ auto pick_fp8(bool nt, bool ntl, bool full)
 
 }  // namespace
 
+namespace {
+
+template <int BS, bool NT, bool NTL, bool PLACE>
+auto pick_fp8_wave(int iter)
+{
+    switch (iter) {
+    case 1: return dispatch_fp8_wave_kernel<BS, 1, NT, NTL, PLACE>;
+    case 2: return dispatch_fp8_wave_kernel<BS, 2, NT, NTL, PLACE>;
+    case 3: return dispatch_fp8_wave_kernel<BS, 3, NT, NTL, PLACE>;
+    case 4: return dispatch_fp8_wave_kernel<BS, 4, NT, NTL, PLACE>;
+    case 5: return dispatch_fp8_wave_kernel<BS, 5, NT, NTL, PLACE>;
+    case 6: return dispatch_fp8_wave_kernel<BS, 6, NT, NTL, PLACE>;
+    case 7: return dispatch_fp8_wave_kernel<BS, 7, NT, NTL, PLACE>;
+    default: return dispatch_fp8_wave_kernel<BS, 8, NT, NTL, PLACE>;
+    }
+}
+
+template <int BS, bool PLACE>
+auto pick_fp8_wave_flags(int iter, bool nt, bool ntl)
+{
+    if (nt) return ntl ? pick_fp8_wave<BS, true, true, PLACE>(iter) : pick_fp8_wave<BS, true, false, PLACE>(iter);
+    return ntl ? pick_fp8_wave<BS, false, true, PLACE>(iter) : pick_fp8_wave<BS, false, false, PLACE>(iter);
+}
+
+// lanes per token of the small-workgroup FP8 form (0: the row-sized form)
+int fp8_small_bs(int H)
+{
+    const int bs = tuning().fp8_form == 1 ? kWave : (tuning().fp8_form == 2 ? 2 * kWave : 0);
+    return bs && H / 16 <= 8 * bs ? bs : 0;
+}
+
+}  // namespace
+
+bool fp8_wave_form(int H) { return fp8_small_bs(H) != 0; }
+
 hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
                                const float *topk_w, const int32_t *topk_idx, void *recv_q,
                                float *recv_scale, float *recv_w, int32_t *recv_idx,
                                const PlaceArgs *place, hipStream_t stream)
 {
     const int nch = H / 16;
+    const bool nt = tuning().dispatch_nt_store, ntl = tuning().dispatch_nt_load;
+    if (const int sbs = fp8_small_bs(H)) {
+        const int iter = (nch + sbs - 1) / sbs;
+        auto fn = sbs == kWave
+                      ? (place ? pick_fp8_wave_flags<kWave, true>(iter, nt, ntl)
+                               : pick_fp8_wave_flags<kWave, false>(iter, nt, ntl))
+                      : (place ? pick_fp8_wave_flags<2 * kWave, true>(iter, nt, ntl)
+                               : pick_fp8_wave_flags<2 * kWave, false>(iter, nt, ntl));
+        hipLaunchKernelGGL(fn, dim3(T), dim3(sbs), 0, stream, (const u32x4 *)x, nch, K, nslot, slots,
+                           topk_w, topk_idx, (u32x4 *)recv_q, recv_scale, recv_w, recv_idx,
+                           place ? *place : PlaceArgs{});
+        return hipGetLastError();
+    }
     int bs = (nch + kWave - 1) / kWave * kWave;
     if (bs > kFp8MaxBS) bs = kFp8MaxBS;
     const bool full = nch % bs == 0;
-    const bool nt = tuning().dispatch_nt_store, ntl = tuning().dispatch_nt_load;
     auto fn = place ? pick_fp8<true>(nt, ntl, full) : pick_fp8<false>(nt, ntl, full);
     hipLaunchKernelGGL(fn, dim3(T), dim3(bs), 0, stream, (const u32x4 *)x, nch, K, nslot, slots,
                        topk_w, topk_idx, (u32x4 *)recv_q, recv_scale, recv_w, recv_idx,
