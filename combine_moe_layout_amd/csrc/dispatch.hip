@@ -20,9 +20,12 @@
 // write-allocate L2 made NT stores pay; here a plain streaming store sustains
 // more write bandwidth than an NT one, while NT loads read markedly faster.
 //
-// FP8: each lane holds 16 consecutive elements (two 16-byte loads), one chunk
-// per pass, in a workgroup sized to the row; the 8 lanes of one 128-block
-// reduce amax with three xor-shuffles; every lane then
+// FP8: each lane holds chunks of 16 consecutive elements (two 16-byte loads
+// each): one wave per token with H/1024 chunks per lane for H <= 8192 (so the
+// 4096 token workgroups of a large batch are mostly resident at once), else a
+// workgroup sized to the row with one chunk per lane per pass. The 8 lanes of
+// one 128-block (8 consecutive lanes in either form) reduce amax with three
+// xor-shuffles; every lane then
 // forms scale = amax / 448 and inv = 448 / amax (IEEE fp32 divisions, as
 // compiled by default), multiplies, clamps to +-448 (which equals saturating
 // round-to-nearest-even for every finite input) and converts pairs with the

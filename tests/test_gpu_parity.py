@@ -443,6 +443,7 @@ FUSED_SHAPES = [  # (T, H, E, G, K); T <= 512: one launch; larger: count + offse
     (257, 1152, 96, 4, 6),
     (513, 1024, 64, 8, 8), (1000, 512, 32, 4, 3), (2000, 256, 16, 16, 1), (777, 384, 40, 1, 5),
     (600, 256, 64, 8, 13), (4097, 2048, 256, 8, 8), (3000, 128, 1024, 32, 8),
+    (600, 8320, 32, 8, 8),   # rows over 8192: multi-pass placing bf16 dispatch; FP8 takes the two calls
 ]
 
 
