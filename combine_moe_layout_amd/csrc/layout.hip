@@ -18,16 +18,22 @@
 // their order, so
 //   rank of (t, k) inside the tile = popcount of the expert's words of earlier
 //   waves + popcount(word of its own wave & lanes below it),
-// which is the stable token-ascending order, and a token's repeated expert is
-// seen as its own bit already set. Groups use one ballot per group per wave.
+// which is the stable token-ascending order, and a token repeats an expert
+// iff one of its earlier entries names it. Groups use one ballot per group per
+// wave, which gives the same kind of word per (group, wave).
 //
 // Kernel 1 (count): per tile, expert and group counts + error bits -> one row
-// of a tile-major table in the workspace.
-// Kernel 2 (place): every tile reads the table column-wise (tiny: (E+G+1) x
-// tiles ints, coalesced), forms global offsets = exclusive prefix over experts
-// of the totals + prefix over earlier tiles, rebuilds its LDS words and writes
-// the slots and receive-source lists. Tile 0 also writes the counts, offsets
-// and status. Global loads are issued ahead of their first use, so each kernel
+// of a tile-major table in the workspace; for top-k <= 8 also the tile's
+// expert and group words.
+// Kernel 2 (place, moe_layout): every tile reads the table column-wise (tiny:
+// (E+G+1) x tiles ints, coalesced), forms global offsets = exclusive prefix
+// over experts of the totals + prefix over earlier tiles, takes its words
+// (loaded, or rebuilt for top-k > 8) and writes the slots and receive-source
+// lists. Tile 0 also writes the counts, offsets and status.
+// Kernel 2' (finalize, the fused layout + dispatch): one workgroup computes the
+// counts, offsets and status once and a base per (tile, column), from which
+// each dispatch workgroup places its own token (place.hpp).
+// Global loads are issued ahead of their first use, so each kernel
 // costs about one memory round trip plus its LDS work; the stores are shaped
 // so that a wave's store touches few cache lines (a token's slot row as one
 // or two 16-byte stores, the tile's expert receive list as per-expert runs
