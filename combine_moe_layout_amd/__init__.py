@@ -251,9 +251,11 @@ FUSED_MAX_TOKENS, FUSED_MAX_PAIRS = 512, 16384
 def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
                         topk_w: torch.Tensor, mode="expert", dtype="bf16", *,
                         out_layout: Layout | None = None, out: Dispatched | None = None,
-                        stream=None) -> tuple[Layout, Dispatched]:
-    """moe_layout + moe_dispatch as one call (moe_layout_dispatch): one launch for T <= 512,
-    else the count kernel, an offsets workgroup and a dispatch that places its own tokens."""
+                        use_workspace: bool = True, stream=None) -> tuple[Layout, Dispatched]:
+    """moe_layout + moe_dispatch as one call (moe_layout_dispatch): one launch for the
+    smallest batches, else the count kernel, an offsets workgroup and a dispatch that
+    places its own tokens. use_workspace=False passes no workspace, which asks for the
+    one-launch form (T <= 512 and T * K <= 16384)."""
     if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or not topk_idx.is_contiguous():
         raise ValueError("topk_idx must be a contiguous int32 [T, K] tensor")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
@@ -266,7 +268,8 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
         raise ValueError("layout buffers were made for other sizes")
     H = x.shape[1]
     D = out if out is not None else alloc_dispatch(L, H, mode, dtype, x.device)
-    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), L.ref(), _ptr(L.workspace), L.workspace.numel(),
+    ws, nb = (_ptr(L.workspace), L.workspace.numel()) if use_workspace else (None, 0)
+    _check(_lib.moe_layout_dispatch(_ptr(topk_idx), L.ref(), ws, nb,
                                     _mode(mode), _dtype(dtype), H,
                                     _ptr(x), _ptr(topk_w), _ptr(D.recv_x), _ptr(D.recv_scale),
                                     _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],

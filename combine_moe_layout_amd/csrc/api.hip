@@ -13,6 +13,10 @@ namespace {
 
 thread_local char g_hip_msg[160] = "";
 
+// moe_layout_dispatch: the one-launch form is used up to this T * K * E (given
+// a workspace; without one, up to the header's limits).
+constexpr int64_t kOneLaunchWork = 1 << 17;
+
 int hip_fail(hipError_t e)
 {
     snprintf(g_hip_msg, sizeof g_hip_msg, "%s (%d)", hipGetErrorString(e), (int)e);
@@ -150,8 +154,14 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
         return MOE_ERR_MISALIGNED;
     const bool fp8 = dtype == MOE_DTYPE_FP8_E4M3_B128;
     hipError_t e;
-    if (L->T <= MOE_FUSED_MAX_TOKENS && (int64_t)L->T * L->K <= MOE_FUSED_MAX_PAIRS) {
-        // small batch: one launch, no workspace
+    // One launch for the smallest batches, where its per-token recomputation of
+    // the routing (work growing with T * K and E per workgroup) is cheaper than
+    // the three launches of the other form (measured: at E = 256, K = 8 even up
+    // to T = 64, slower from T = 128; at E <= 64 faster up to T = 512), and
+    // whenever no workspace is given.
+    const bool one_launch_fits = L->T <= MOE_FUSED_MAX_TOKENS && (int64_t)L->T * L->K <= MOE_FUSED_MAX_PAIRS;
+    const bool small = (int64_t)L->T * L->K * L->E <= kOneLaunchWork;
+    if (one_launch_fits && (small || !ws)) {
         e = moe::launch_layout_dispatch(topk_idx, L->T, L->K, L->E, L->G, ptrs_of(L), mode, fp8, H, x,
                                         topk_w, recv_x, recv_scale, recv_topk_w, recv_topk_idx,
                                         (hipStream_t)stream);

@@ -162,10 +162,11 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
 /* moe_layout() and moe_dispatch() as one call. The layout arrays and the
  * receive buffers it writes are, bit for bit, those the two calls write
  * (layout->status included). Arguments as for moe_layout() and moe_dispatch().
- * Small batches (T <= MOE_FUSED_MAX_TOKENS and T * K <= MOE_FUSED_MAX_PAIRS)
- * take one launch and need no workspace (ws may be NULL): one workgroup per
- * token recomputes the routing it needs from the whole index array, a cost
- * that grows as T^2. Larger batches need ws (moe_layout_workspace_bytes()):
+ * The smallest batches (T * K * E <= 2^17), and any batch within
+ * T <= MOE_FUSED_MAX_TOKENS and T * K <= MOE_FUSED_MAX_PAIRS when ws is NULL,
+ * take one launch and need no workspace: one workgroup per token recomputes
+ * the routing it needs from the whole index array, a cost that grows with
+ * T * K and E. Other batches need ws (moe_layout_workspace_bytes()):
  * for BF16 with K <= 8 the layout's count kernel and one workgroup that
  * computes the offsets run first, and each dispatch workgroup then computes
  * its own token's slots from the per-tile token masks while its row loads are

@@ -450,9 +450,12 @@ FUSED_SHAPES = [  # (T, H, E, G, K); T <= 512: one launch; larger: count + offse
 @pytest.mark.parametrize("T,H,E,G,K", FUSED_SHAPES)
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_fused_layout_dispatch_matches_oracle(moe, orc, T, H, E, G, K, mode, dtype):
+@pytest.mark.parametrize("use_ws", [True, False], ids=["auto", "one_launch"])
+def test_fused_layout_dispatch_matches_oracle(moe, orc, T, H, E, G, K, mode, dtype, use_ws):
     if dtype == "fp8" and H % 128:
         pytest.skip("FP8 needs H % 128 == 0")
+    if not use_ws and (T > moe.FUSED_MAX_TOKENS or T * K > moe.FUSED_MAX_PAIRS):
+        pytest.skip("the one-launch form is limited to small batches")
     d = si.make_inputs(T, H, E, K, seed=7 * T + H + K)
     idx = d["topk_idx"].copy()
     if T > 40:
@@ -470,7 +473,8 @@ def test_fused_layout_dispatch_matches_oracle(moe, orc, T, H, E, G, K, mode, dty
         D.recv_scale.fill_(-1.5)
     D.recv_topk_w.fill_(-3.0)
     D.recv_topk_idx.fill_(-77)
-    L, D = moe.moe_layout_dispatch(idx_d, E, G, x, to_dev(d["topk_w"]), mode, dtype, out_layout=L, out=D)
+    L, D = moe.moe_layout_dispatch(idx_d, E, G, x, to_dev(d["topk_w"]), mode, dtype, out_layout=L, out=D,
+                                   use_workspace=use_ws)
     Lo = orc.layout(idx, E, G)
     check_layout(L, Lo)
     if dtype == "bf16":
