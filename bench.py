@@ -187,6 +187,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain reference copy (256 MiB, 5 times): a known byte "
                          "count for scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--processes", type=int, default=3,
+                    help="also time the step in this many separate processes in all (this one "
+                         "included; run one after another) and report each value and their median "
+                         "in extra.processes; `value` stays this process's")
     ap.add_argument("--table", default=None, metavar="NAMES",
                     help="only the per-workload table for these comma-separated workloads "
                          "(e.g. t4096): every call of the library on each, timed alone, printed "
@@ -304,9 +308,28 @@ def main():
 
     if not args.no_extras:
         result["extra"] = extras(moe, d, dv, args)
+        if args.processes > 1:
+            result["extra"]["processes"] = other_processes(args, value)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(d, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def other_processes(args, value):
+    """The timed step repeated in args.processes - 1 child processes (started one after
+    another, each a fresh `python bench.py --no-extras --no-cpu-baseline`), with this
+    process's value: each value, and their median."""
+    import subprocess
+    import numpy as np
+    vals = [round(value, 1)]
+    for _ in range(args.processes - 1):
+        cmd = [sys.executable, os.path.abspath(__file__), "--steps", str(args.steps), "--warmup",
+               str(args.warmup), "--workload", args.workload, "--no-extras", "--no-cpu-baseline"]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        if r.returncode != 0:
+            raise RuntimeError(f"child bench failed ({r.returncode}): {r.stderr[-2000:]}")
+        vals.append(json.loads(r.stdout.strip().splitlines()[-1])["value"])
+    return {"values": vals, "median": round(float(np.median(vals)), 1)}
 
 
 def extras(moe, d, dv, args):
