@@ -447,6 +447,20 @@ def extras(moe, d, dv, args):
     del dv8
     torch.cuda.synchronize()
     res["workloads"] = workload_table(moe)
+
+    # rates against the plain copy of the same run (mixed read/write traffic's achievable rate)
+    cg = res["copy_ceiling"]["gbs"]
+    t3 = res["three_call_step"]
+    res["of_copy_ceiling"] = {"dispatch": round(t3["dispatch_gbs"] / cg, 3),
+                              "combine": round(t3["combine_gbs"] / cg, 3),
+                              "fused_step": round(res["fused_step"]["expert"]["step_gbs"] / cg, 3)}
+    props = torch.cuda.get_device_properties(0)
+    res["env"] = {"device": torch.cuda.get_device_name(0),
+                  "arch": getattr(props, "gcnArchName", None),
+                  "compute_units": props.multi_processor_count,
+                  "hbm_gib": round(props.total_memory / 2**30, 1),
+                  "hip": torch.version.hip, "torch": torch.__version__,
+                  "host_cores_available": len(os.sched_getaffinity(0))}
     return res
 
 
