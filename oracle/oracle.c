@@ -60,6 +60,9 @@ float oracle_bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); 
  * part (0x7FFF plus the kept lsb, which breaks ties toward even) and truncate. */
 uint16_t oracle_f32_to_bf16(float f)
 {
+    /* a NaN stays a NaN: the canonical quiet NaN (the carry of the rounding
+       below would turn some NaNs into an infinity or wrap others to zero) */
+    if (isnan(f)) return 0x7FC0;
     uint32_t u = bits_from_f32(f);
     uint32_t lsb = (u >> 16) & 1u;
     u += 0x7FFFu + lsb;
@@ -87,6 +90,7 @@ uint8_t oracle_f32_to_e4m3(float f)
     uint8_t sign = (bits_from_f32(f) >> 31) ? 0x80 : 0x00;
     double a = fabs((double)f);
     if (isnan(f)) return 0x7F;
+    if (isinf(f)) return (uint8_t)(sign | 0x7E);   /* satfinite */
     if (a == 0.0) return sign;
     if (a < ldexp(1.0, -6)) {                /* subnormal range: step 2^-9 */
         double m = nearbyint(a * 512.0);     /* may round up to 8 = min normal */

@@ -358,6 +358,23 @@ def test_bf16_encode_against_torch(orc):
     assert orc.f32_to_bf16(1.0 + 3 * 2 ** -8) == 0x3F82
 
 
+def test_bf16_encode_non_finite(orc):
+    """Infinities stay infinities, values past the largest bf16 round to them, and every
+    NaN (either sign, any payload: quiet, signalling, all ones) becomes a NaN: the
+    canonical quiet NaN 0x7FC0 here (torch also gives a NaN, 0xFFFF on this build)."""
+    special = np.array([0x7F800000, 0xFF800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000, 0x7F7F7FFF,
+                        0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001, 0x7FFFFFFF, 0xFFFFFFFF,
+                        0x7FBFFFFF, 0xFFFF8000], np.uint32).view(np.float32)
+    got = orc.f32_to_bf16_array(special)
+    ref = torch.from_numpy(special).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got[:6], ref[:6])
+    is_nan = lambda b: (b & 0x7F80) == 0x7F80 and (b & 0x7F) != 0
+    assert all(is_nan(int(b)) for b in ref[6:]) and all(is_nan(int(b)) for b in got[6:])
+    assert list(got[:2]) == [0x7F80, 0xFF80]
+    assert list(got[4:6]) == [0x7F80, 0x7F7F]            # the tie above the max rounds to inf
+    assert np.all(got[6:] == 0x7FC0)
+
+
 def test_e4m3_decode_all_codes(orc):
     for c in range(256):
         s, e, m = c >> 7, (c >> 3) & 15, c & 7
@@ -398,6 +415,12 @@ def test_e4m3_encode_against_torch_and_midpoints(orc):
     # saturation above the last midpoint (torch gives NaN there; the reading is satfinite)
     assert orc.f32_to_e4m3(1e6) == 0x7E and orc.f32_to_e4m3(-500.0) == 0xFE
     assert orc.f32_to_e4m3(-0.0) == 0x80 and orc.f32_to_e4m3(0.0) == 0
+    # infinities saturate like any value past 448; a NaN of either sign is the NaN
+    # code 0x7F (torch's cast gives the same code for a positive NaN)
+    assert orc.f32_to_e4m3(math.inf) == 0x7E and orc.f32_to_e4m3(-math.inf) == 0xFE
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], np.uint32).view(np.float32)
+    assert list(orc.f32_to_e4m3_array(nans)) == [0x7F] * 4
+    assert torch.tensor([math.nan]).to(torch.float8_e4m3fn).view(torch.uint8).item() == 0x7F
 
 
 def test_fp8_quantisation_bounds(orc):
