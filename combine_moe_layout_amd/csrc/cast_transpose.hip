@@ -49,7 +49,6 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
     return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
-__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
 // Exclusive scan of two values over the 256 threads, with both totals, and
 // the OR of a flag over the threads (returned).
@@ -199,11 +198,13 @@ __global__ __launch_bounds__(kCtBS) void cast_transpose_kernel(
                 f[2 * m + 1] = bf16_hi(cur[i][m]);
             }
 #pragma unroll
-            for (int m = 0; m < 8; ++m) a = fmaxf(a, fabsf(f[m]));
-            int p0 = cvt_pk_e4m3<false>(clamp448(f[0] * s), clamp448(f[1] * s), 0);
-            p0 = cvt_pk_e4m3<true>(clamp448(f[2] * s), clamp448(f[3] * s), p0);
-            int p1 = cvt_pk_e4m3<false>(clamp448(f[4] * s), clamp448(f[5] * s), 0);
-            p1 = cvt_pk_e4m3<true>(clamp448(f[6] * s), clamp448(f[7] * s), p1);
+            for (int m = 0; m < 8; ++m) a = amax_step(a, f[m]);
+            int p0 = cvt_pk_e4m3<false>(sat448(f[0] * s), sat448(f[1] * s), 0);
+            p0 = cvt_pk_e4m3<true>(sat448(f[2] * s), sat448(f[3] * s), p0);
+            int p1 = cvt_pk_e4m3<false>(sat448(f[4] * s), sat448(f[5] * s), 0);
+            p1 = cvt_pk_e4m3<true>(sat448(f[6] * s), sat448(f[7] * s), p1);
+            p0 = (int)e4m3_nan_canon((uint32_t)p0);
+            p1 = (int)e4m3_nan_canon((uint32_t)p1);
             b[i][0] = (uint32_t)p0;
             b[i][1] = (uint32_t)p1;
             const int row = 4 * q + i;

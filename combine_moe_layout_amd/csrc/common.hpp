@@ -35,11 +35,43 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // Round a finite float to bf16, nearest even, by adding 0x7FFF plus the kept
 // lsb and truncating.
+// fp32 -> bf16 bits, round to nearest even; a NaN becomes the canonical quiet
+// NaN 0x7FC0 (the carry of the integer rounding would turn some NaNs into an
+// infinity, or wrap them to zero).
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f)
 {
     uint32_t u = __float_as_uint(f);
     u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+    return f != f ? 0x7FC0u : u >> 16;
+}
+
+// One step of an amax: max(m, |v|), passing over a NaN v. fmaxf alone does
+// not: for a signalling NaN (a bf16 such as 0x7F81 widened by a shift stays
+// signalling) the hardware max returns a quiet NaN and m is lost. The
+// canonicalisation quietens it first, and a max with a quiet NaN returns the
+// other operand.
+__device__ __forceinline__ float amax_step(float m, float v)
+{
+    return fmaxf(m, __builtin_canonicalizef(fabsf(v)));
+}
+
+// Saturation of a scaled value to the finite e4m3 range before the packed
+// conversion (satfinite: infinities too); a NaN stays a NaN.
+__device__ __forceinline__ float sat448(float v)
+{
+    return v != v ? __builtin_nanf("") : fminf(fmaxf(v, -448.f), 448.f);
+}
+
+// The packed conversion writes a NaN as the byte 0xFF; the library's e4m3 NaN
+// code is 0x7F (S.1111.111 with the sign clear, as a cast of a positive NaN
+// gives). Clears bit 7 of every byte of w that is 0xFF and leaves the rest:
+// in t = ~w those bytes are zero, and z below has 0x80 in exactly the zero
+// bytes of t (no carry crosses a byte: each addend is at most 0x7F + 0x7F).
+__device__ __forceinline__ uint32_t e4m3_nan_canon(uint32_t w)
+{
+    const uint32_t t = ~w;
+    const uint32_t z = ~(((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t | 0x7F7F7F7Fu);
+    return w ^ z;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)

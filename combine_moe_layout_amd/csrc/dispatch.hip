@@ -27,8 +27,9 @@
 // one 128-block (8 consecutive lanes in either form) reduce amax with three
 // xor-shuffles; every lane then
 // forms scale = amax / 448 and inv = 448 / amax (IEEE fp32 divisions, as
-// compiled by default), multiplies, clamps to +-448 (which equals saturating
-// round-to-nearest-even for every finite input) and converts pairs with the
+// compiled by default), multiplies, saturates to +-448 (sat448: equal to
+// saturating round-to-nearest-even for every value; a NaN stays a NaN and
+// becomes the NaN code 0x7F) and converts pairs with the
 // packed e4m3 conversion, giving one 16-byte store per lane per destination.
 // The quantisation runs once per source token, not once per destination.
 #include "common.hpp"
@@ -110,7 +111,6 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
     return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
-__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
 // One lane's 16-element chunk (a, b: 16 bf16): the amax of its 128-block over
 // the block's 8 lanes (8 consecutive lanes of a wave; every lane of the wave
@@ -127,7 +127,7 @@ __device__ __forceinline__ void quantize16(u32x4 a, u32x4 b, u32x4 &q, float &sc
     }
     float amax = 0.f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(f[m]));
+    for (int m = 0; m < 16; ++m) amax = amax_step(amax, f[m]);
     amax = fmaxf(amax, __shfl_xor(amax, 1));
     amax = fmaxf(amax, __shfl_xor(amax, 2));
     amax = fmaxf(amax, __shfl_xor(amax, 4));
@@ -136,9 +136,9 @@ __device__ __forceinline__ void quantize16(u32x4 a, u32x4 b, u32x4 &q, float &sc
     int w[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        int p = cvt_pk_e4m3<false>(clamp448(f[4 * m] * inv), clamp448(f[4 * m + 1] * inv), 0);
-        p = cvt_pk_e4m3<true>(clamp448(f[4 * m + 2] * inv), clamp448(f[4 * m + 3] * inv), p);
-        w[m] = p;
+        int p = cvt_pk_e4m3<false>(sat448(f[4 * m] * inv), sat448(f[4 * m + 1] * inv), 0);
+        p = cvt_pk_e4m3<true>(sat448(f[4 * m + 2] * inv), sat448(f[4 * m + 3] * inv), p);
+        w[m] = (int)e4m3_nan_canon((uint32_t)p);
     }
     q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
 }

@@ -37,7 +37,6 @@ __device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
     return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
-__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.f), 448.f); }
 
 // LDS layout (ints): idx[T*K] | vmask[T] | gmask[T] | cnt[E] | off[E+1] | gcnt[G] | goff[G+1]
 //                    | rank[K] | grank[G] | dst[max(K, G)] | misc
@@ -272,7 +271,7 @@ __global__ __launch_bounds__(kFusedBS) void fused_layout_dispatch_kernel(
             }
             float amax = 0.f;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) amax = fmaxf(amax, fabsf(f[m]));
+            for (int m = 0; m < 16; ++m) amax = amax_step(amax, f[m]);
             amax = fmaxf(amax, __shfl_xor(amax, 1));
             amax = fmaxf(amax, __shfl_xor(amax, 2));
             amax = fmaxf(amax, __shfl_xor(amax, 4));
@@ -281,9 +280,9 @@ __global__ __launch_bounds__(kFusedBS) void fused_layout_dispatch_kernel(
             int w[4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                int p = cvt_pk_e4m3<false>(clamp448(f[4 * m] * inv), clamp448(f[4 * m + 1] * inv), 0);
-                p = cvt_pk_e4m3<true>(clamp448(f[4 * m + 2] * inv), clamp448(f[4 * m + 3] * inv), p);
-                w[m] = p;
+                int p = cvt_pk_e4m3<false>(sat448(f[4 * m] * inv), sat448(f[4 * m + 1] * inv), 0);
+                p = cvt_pk_e4m3<true>(sat448(f[4 * m + 2] * inv), sat448(f[4 * m + 3] * inv), p);
+                w[m] = (int)e4m3_nan_canon((uint32_t)p);
             }
             const u32x4 q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
             if (in) {

@@ -73,6 +73,12 @@ enum moe_mode { MOE_MODE_EXPERT = 0, MOE_MODE_GROUP = 1 };
  * FP8_E4M3_B128: rows are OCP e4m3fn bytes with one fp32 scale per 1x128
  * block: amax = max |x| over the block, scale = amax / 448,
  * q = e4m3fn_rne_satfinite(x * (448 / amax)) (q = 0 when amax = 0).
+ * Non-finite values (here and in every call that computes on values): the
+ * amax skips NaNs (quiet or signalling); an infinity makes amax infinite, so
+ * the block's scale is +inf and its codes are +-0 (finite x) or the NaN code
+ * (x infinite or NaN: inf * 0). A NaN encodes as 0x7F in e4m3 and 0x7FC0 in
+ * bf16; infinities saturate to +-448 in e4m3 (satfinite) and stay infinities
+ * in bf16. Combine propagates them as IEEE fp32 arithmetic does.
  * Source: "Optimized rocm specific multicast transpose kernel"
  * (ROCm/TransformerEngine pull request 586), Change Summary (fused amax,
  * packed FP8 conversion). */

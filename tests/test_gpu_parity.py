@@ -447,15 +447,25 @@ FUSED_SHAPES = [  # (T, H, E, G, K); T <= 512: one launch; larger: count + offse
 ]
 
 
-@pytest.mark.parametrize("T,H,E,G,K", FUSED_SHAPES)
+def _fused_cases():
+    # FP8 needs H % 128 == 0; the call without a workspace (one launch) takes
+    # T <= 512 and T * K <= 16384 only
+    for T, H, E, G, K in FUSED_SHAPES:
+        for dtype in ("bf16", "fp8"):
+            if dtype == "fp8" and H % 128:
+                continue
+            for use_ws in (True, False):
+                if not use_ws and (T > 512 or T * K > 16384):
+                    continue
+                yield pytest.param(T, H, E, G, K, dtype, use_ws,
+                                   id=f"{T}-{H}-{E}-{G}-{K}-{dtype}-{'auto' if use_ws else 'one_launch'}")
+
+
+@pytest.mark.parametrize("T,H,E,G,K,dtype,use_ws", list(_fused_cases()))
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-@pytest.mark.parametrize("use_ws", [True, False], ids=["auto", "one_launch"])
 def test_fused_layout_dispatch_matches_oracle(moe, orc, T, H, E, G, K, mode, dtype, use_ws):
-    if dtype == "fp8" and H % 128:
-        pytest.skip("FP8 needs H % 128 == 0")
-    if not use_ws and (T > moe.FUSED_MAX_TOKENS or T * K > moe.FUSED_MAX_PAIRS):
-        pytest.skip("the one-launch form is limited to small batches")
+    if not use_ws:
+        assert T <= moe.FUSED_MAX_TOKENS and T * K <= moe.FUSED_MAX_PAIRS
     d = si.make_inputs(T, H, E, K, seed=7 * T + H + K)
     idx = d["topk_idx"].copy()
     if T > 40:
@@ -547,10 +557,12 @@ def test_fused_layout_dispatch_equals_two_calls(moe, name):
 
 REGROUP_SHAPES = [("t256", None), ("skew", None), ("fp8", None), ("tiny", None),
                   (None, (300, 520, 16, 4, 3)), (None, (129, 1024, 64, 1, 8)), (None, (50, 16392, 64, 8, 8))]
+# FP8 needs H % 128 == 0: not for H = 520 or 16392
+REGROUP_CASES = [(n, s, dt) for n, s in REGROUP_SHAPES for dt in ("bf16", "fp8")
+                 if not (dt == "fp8" and s is not None and s[1] % 128)]
 
 
-@pytest.mark.parametrize("name,shape", REGROUP_SHAPES)
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("name,shape,dtype", REGROUP_CASES)
 def test_regroup_matches_expert_dispatch(moe, orc, name, shape, dtype):
     if name:
         d = workload(name)
@@ -562,8 +574,7 @@ def test_regroup_matches_expert_dispatch(moe, orc, name, shape, dtype):
         d = si.make_inputs(T, H, E, K, seed=T + H)
         idx = d["topk_idx"].copy()
         idx[T // 2, 0] = -3                    # an invalid entry is skipped
-    if dtype == "fp8" and H % 128:
-        pytest.skip("FP8 needs H % 128 == 0")
+    assert dtype == "bf16" or H % 128 == 0
     idx_d, w_d, x_d = to_dev(idx), to_dev(d["topk_w"]), dev_bf16(d["x"])
     L = moe.moe_layout(idx_d, E, G)
     Dg = moe.moe_dispatch(L, x_d, w_d, idx_d, "group", dtype)
@@ -732,3 +743,56 @@ def test_guard_cast_transpose_writes_nothing_for_offsets_past_the_bound(moe, orc
     assert bool((CT.t == 0x5A).all())
     assert bool((CT.amax == 2.5).all())
     assert bool((CT.pad_offset == -9).all())
+
+
+# ------------------------------------------------------------------ non-finite values
+
+def test_nonfinite_values_match_oracle(moe, orc):
+    """Infinities and NaNs (both signs, quiet and signalling payloads) in the tokens'
+    rows, including a 128-block that is all NaN and one that holds an infinity,
+    through every call that computes on the values: FP8 dispatch (both layouts) and
+    its dequantisation, combine, the cast-transpose and the one-launch fused FP8
+    dispatch. Results bit for bit as the oracle's: a NaN stays a NaN (code 0x7F, bf16
+    0x7FC0), finite values and infinities saturate at +-448 in e4m3."""
+    T, H, E, G, K = 300, 1024, 32, 4, 4
+    d = si.make_inputs(T, H, E, K, seed=91)
+    rng = np.random.default_rng(91)
+    x = d["x"].copy()
+    special = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0xFFFF], np.uint16)
+    pos = rng.choice(x.size, 400, replace=False)
+    x.flat[pos] = rng.choice(special, 400)
+    x[5, 128:256] = 0x7FC0                           # a block of NaNs
+    x[7, 0] = 0x7F80                                 # an infinity in a block of finite values
+    x[9, 512:640] = 0xFF80                           # a block of infinities
+    idx, w = d["topk_idx"], d["topk_w"]
+    idx_d, w_d, x_d = to_dev(idx), to_dev(w), dev_bf16(x)
+    L = moe.moe_layout(idx_d, E, G)
+    Lo = orc.layout(idx, E, G)
+    check_layout(L, Lo)
+    for mode in MODES:
+        D = dispatch_with_canary(moe, L, x_d, w_d, idx_d, mode, "fp8")
+        Do = orc.dispatch_fp8(Lo, mode, x, w, idx)
+        fp8_check(D, Do)
+        y = moe.moe_fp8_dequant(L, D.recv_x, D.recv_scale, mode)
+        np.testing.assert_array_equal(host_u16(y)[:Do["R"]], orc.dequant_fp8(Do["recv_q"], Do["recv_scale"]))
+    De = moe.moe_dispatch(L, x_d, w_d, idx_d, "expert")
+    Deo = orc.dispatch_bf16(Lo, "expert", x, w, idx)
+    np.testing.assert_array_equal(host_u16(De.recv_x)[:Lo["R_expert"]], Deo["recv_x"])
+    out = moe.moe_combine(L, De.recv_x, w_d, "expert")
+    got = host_u16(out)
+    np.testing.assert_array_equal(got, orc.combine(Lo, "expert", Deo["recv_x"], w))
+    assert np.any(got == 0x7FC0)                     # NaNs reached the output as NaNs
+    scale = rng.uniform(0.5, 50.0, E).astype(np.float32)
+    CT = moe.moe_cast_transpose_fp8(L, De.recv_x, to_dev(scale))
+    ref = orc.cast_transpose_fp8(Lo["expert_offset"], Deo["recv_x"], scale)
+    np.testing.assert_array_equal(CT.c[:Lo["R_expert"]].cpu().numpy(), ref["c"])
+    nt = H * int(ref["pad_offset"][-1])
+    np.testing.assert_array_equal(CT.t[:nt].cpu().numpy(), ref["t"])
+    np.testing.assert_array_equal(CT.amax.cpu().numpy().view(np.uint32), ref["amax"].view(np.uint32))
+    L2 = moe.Layout.empty(T, K, E, G)
+    D2 = moe.alloc_dispatch(L2, H, "expert", "fp8")
+    D2.recv_x.fill_(0xA5)
+    D2.recv_scale.fill_(-1.5)
+    L2, D2 = moe.moe_layout_dispatch(idx_d, E, G, x_d, w_d, "expert", "fp8", out_layout=L2, out=D2,
+                                     use_workspace=False)
+    fp8_check(D2, orc.dispatch_fp8(Lo, "expert", x, w, idx))

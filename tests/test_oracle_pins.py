@@ -444,6 +444,79 @@ def test_fp8_quantisation_bounds(orc):
             assert np.all(err[~normal] <= 2 ** -10 * float(s[b]) * (1 + 1e-6))
 
 
+def test_fp8_blocks_with_non_finite_values(orc):
+    """A NaN (quiet, signalling, either sign) is skipped by the block amax, so the
+    block's scale and every other code are those of the block with the NaNs set to
+    zero (numpy's nanmax gives the same amax) and the NaNs encode as 0x7F; an
+    infinity makes amax infinite, so scale = inf, inv = 448 / inf = 0 and every
+    finite value encodes as a zero of its sign while inf * 0 is the NaN code; a
+    block of NaNs only has amax 0, scale 0 and NaN codes."""
+    rng = np.random.default_rng(5)
+    base = bf16_bits_of((rng.standard_normal(512) * 3).astype(np.float32))
+    xf = bf16_to_float(base)
+    for payload in (0x7FC0, 0x7F81, 0xFFC0, 0xFFFF):
+        row = base.copy()
+        blk = 1
+        seg = np.abs(xf[128:256])
+        pos = 128 + rng.choice([j for j in range(128) if j != int(seg.argmax())], 9, replace=False)
+        row[pos] = payload
+        zeroed = row.copy()
+        zeroed[pos] = 0
+        q, sc = orc.quantize_row_fp8(row)
+        qz, sz = orc.quantize_row_fp8(zeroed)
+        np.testing.assert_array_equal(sc.view(np.uint32), sz.view(np.uint32))
+        amax = np.nanmax(np.abs(bf16_to_float(row)[128 * blk:128 * (blk + 1)]))
+        assert sc[blk] == np.float32(amax) / np.float32(448)
+        keep = np.ones(512, bool)
+        keep[pos] = False
+        np.testing.assert_array_equal(q[keep], qz[keep])
+        assert np.all(q[pos] == 0x7F)
+    for inf in (0x7F80, 0xFF80):
+        row = base.copy()
+        row[300] = inf
+        q, sc = orc.quantize_row_fp8(row)
+        q0, s0 = orc.quantize_row_fp8(base)
+        assert math.isinf(sc[2]) and sc[2] > 0
+        blk = slice(256, 384)
+        expect = np.where(np.signbit(xf[blk]), 0x80, 0x00).astype(np.uint8)
+        expect[300 - 256] = 0x7F
+        np.testing.assert_array_equal(q[blk], expect)
+        other = np.r_[0:256, 384:512]
+        np.testing.assert_array_equal(q[other], q0[other])
+        np.testing.assert_array_equal(np.delete(sc, 2), np.delete(s0, 2))
+    row = base.copy()
+    row[0:128] = 0x7F81
+    q, sc = orc.quantize_row_fp8(row)
+    assert sc[0] == 0.0 and np.all(q[:128] == 0x7F)
+
+
+def test_cast_transpose_non_finite_values(orc):
+    """Cast-transpose: NaNs are skipped by the expert amax (numpy's nanmax of |x|),
+    an infinity makes it infinite; a NaN encodes as 0x7F, an infinity times a finite
+    scale saturates to +-448 (0x7E / 0xFE), and the transpose carries the same codes."""
+    off = np.array([0, 4, 7], np.int32)
+    rng = np.random.default_rng(8)
+    xv = (rng.standard_normal((7, 32)) * 4).astype(np.float32)
+    x = bf16_bits_of(xv)
+    x[1, 3], x[2, 30], x[0, 0] = 0x7F81, 0xFFC0, 0x7FC0          # NaNs in expert 0
+    x[5, 7], x[6, 9] = 0xFF80, 0x7FFF                             # -inf and a NaN in expert 1
+    scale = np.array([2.0, 0.5], np.float32)
+    out = orc.cast_transpose_fp8(off, x, scale)
+    xf = bf16_to_float(x)
+    assert out["amax"][0] == np.nanmax(np.abs(xf[0:4]))
+    assert math.isinf(out["amax"][1])
+    c = out["c"]
+    assert c[1, 3] == c[2, 30] == c[0, 0] == c[6, 9] == 0x7F
+    assert c[5, 7] == 0xFE
+    fin = ~np.isnan(xf) & ~np.isinf(xf)
+    with np.errstate(invalid="ignore"):
+        prod = xf * np.repeat(scale, [4, 3])[:, None]
+    ref = np.array([orc.f32_to_e4m3(float(v)) for v in prod.ravel()], np.uint8).reshape(7, 32)
+    np.testing.assert_array_equal(c[:7][fin], ref[fin])
+    t1 = out["t"][32 * 16:32 * 32].reshape(32, 16)
+    np.testing.assert_array_equal(t1[:, :3], c[4:7].T)
+
+
 def test_dequant_identity_on_exact_codes(orc):
     # a row whose block amax is 448 has scale 1, so decode(q) * 1 recovers every
     # input that is itself an e4m3 value
