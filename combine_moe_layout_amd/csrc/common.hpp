@@ -33,18 +33,6 @@ __device__ __forceinline__ u32x4 load16(const u32x4 *p)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Round a finite float to bf16, nearest even, by adding 0x7FFF plus the kept
-// lsb and truncating.
-// fp32 -> bf16 bits, round to nearest even; a NaN becomes the canonical quiet
-// NaN 0x7FC0 (the carry of the integer rounding would turn some NaNs into an
-// infinity, or wrap them to zero).
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return f != f ? 0x7FC0u : u >> 16;
-}
-
 // One step of an amax: max(m, |v|), passing over a NaN v. fmaxf alone does
 // not: for a signalling NaN (a bf16 such as 0x7F81 widened by a shift stays
 // signalling) the hardware max returns a quiet NaN and m is lost. The
@@ -74,9 +62,16 @@ __device__ __forceinline__ uint32_t e4m3_nan_canon(uint32_t w)
     return w ^ z;
 }
 
+// Two floats -> two bf16 (lo in the low half), round to nearest even, with
+// gfx950's packed conversion: one instruction per pair. On every input that
+// is not a NaN it equals the integer rounding (bits + 0x7FFF + kept lsb,
+// truncated): infinities, overflow to infinity and subnormals included. A NaN
+// gives a quiet NaN with its sign and leading payload bits.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return bf16_rne_bits(lo) | (bf16_rne_bits(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane)

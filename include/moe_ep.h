@@ -76,9 +76,12 @@ enum moe_mode { MOE_MODE_EXPERT = 0, MOE_MODE_GROUP = 1 };
  * Non-finite values (here and in every call that computes on values): the
  * amax skips NaNs (quiet or signalling); an infinity makes amax infinite, so
  * the block's scale is +inf and its codes are +-0 (finite x) or the NaN code
- * (x infinite or NaN: inf * 0). A NaN encodes as 0x7F in e4m3 and 0x7FC0 in
- * bf16; infinities saturate to +-448 in e4m3 (satfinite) and stay infinities
- * in bf16. Combine propagates them as IEEE fp32 arithmetic does.
+ * (x infinite or NaN: inf * 0). A NaN encodes as 0x7F in e4m3; infinities
+ * saturate to +-448 in e4m3 (satfinite). Rows copied as bf16 keep every bit.
+ * A bf16 result computed from a NaN (combine, dequant) is a quiet NaN whose
+ * sign and payload are not specified (IEEE 754 leaves open which input's
+ * payload a NaN result carries); infinities there follow IEEE fp32
+ * arithmetic.
  * Source: "Optimized rocm specific multicast transpose kernel"
  * (ROCm/TransformerEngine pull request 586), Change Summary (fused amax,
  * packed FP8 conversion). */

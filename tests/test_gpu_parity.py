@@ -747,13 +747,28 @@ def test_guard_cast_transpose_writes_nothing_for_offsets_past_the_bound(moe, orc
 
 # ------------------------------------------------------------------ non-finite values
 
+def assert_bf16_equal_nan_by_class(got, want):
+    """Bit-exact where the oracle's bf16 is not a NaN; a NaN where it is. The sign and
+    payload of a NaN computed from NaN inputs are not unique (IEEE 754 leaves open
+    which input's payload propagates), so only NaN-ness is compared there."""
+    is_nan = lambda b: ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape
+    wn = is_nan(want)
+    np.testing.assert_array_equal(is_nan(got), wn)
+    np.testing.assert_array_equal(got[~wn], want[~wn])
+    return int(wn.sum())
+
+
 def test_nonfinite_values_match_oracle(moe, orc):
     """Infinities and NaNs (both signs, quiet and signalling payloads) in the tokens'
     rows, including a 128-block that is all NaN and one that holds an infinity,
     through every call that computes on the values: FP8 dispatch (both layouts) and
     its dequantisation, combine, the cast-transpose and the one-launch fused FP8
-    dispatch. Results bit for bit as the oracle's: a NaN stays a NaN (code 0x7F, bf16
-    0x7FC0), finite values and infinities saturate at +-448 in e4m3."""
+    dispatch. FP8 codes and scales bit for bit as the oracle's (a NaN is the code
+    0x7F; finite values and infinities saturate at +-448); bf16 rows copied by the
+    dispatch bit for bit; bf16 results computed from the values (combine, dequant)
+    bit for bit except that a NaN is compared as a NaN."""
     T, H, E, G, K = 300, 1024, 32, 4, 4
     d = si.make_inputs(T, H, E, K, seed=91)
     rng = np.random.default_rng(91)
@@ -774,14 +789,16 @@ def test_nonfinite_values_match_oracle(moe, orc):
         Do = orc.dispatch_fp8(Lo, mode, x, w, idx)
         fp8_check(D, Do)
         y = moe.moe_fp8_dequant(L, D.recv_x, D.recv_scale, mode)
-        np.testing.assert_array_equal(host_u16(y)[:Do["R"]], orc.dequant_fp8(Do["recv_q"], Do["recv_scale"]))
+        assert assert_bf16_equal_nan_by_class(host_u16(y)[:Do["R"]],
+                                              orc.dequant_fp8(Do["recv_q"], Do["recv_scale"])) > 0
     De = moe.moe_dispatch(L, x_d, w_d, idx_d, "expert")
     Deo = orc.dispatch_bf16(Lo, "expert", x, w, idx)
     np.testing.assert_array_equal(host_u16(De.recv_x)[:Lo["R_expert"]], Deo["recv_x"])
     out = moe.moe_combine(L, De.recv_x, w_d, "expert")
     got = host_u16(out)
-    np.testing.assert_array_equal(got, orc.combine(Lo, "expert", Deo["recv_x"], w))
-    assert np.any(got == 0x7FC0)                     # NaNs reached the output as NaNs
+    assert assert_bf16_equal_nan_by_class(got, orc.combine(Lo, "expert", Deo["recv_x"], w)) > 0
+    inf_rows = (x == 0x7F80).any(axis=1) | (x == 0xFF80).any(axis=1)
+    assert np.any((got == 0x7F80) | (got == 0xFF80)) or not inf_rows.any()
     scale = rng.uniform(0.5, 50.0, E).astype(np.float32)
     CT = moe.moe_cast_transpose_fp8(L, De.recv_x, to_dev(scale))
     ref = orc.cast_transpose_fp8(Lo["expert_offset"], Deo["recv_x"], scale)
