@@ -33,6 +33,9 @@
 // Kernel 2' (finalize, the fused layout + dispatch): one workgroup computes the
 // counts, offsets and status once and a base per (tile, column), from which
 // each dispatch workgroup places its own token (place.hpp).
+// One launch instead (moe_layout with top-k <= 8 and T * K <= 16384, where it
+// measured faster): each tile's workgroup counts all tokens itself (see
+// layout_onepass_kernel).
 // Global loads are issued ahead of their first use, so each kernel
 // costs about one memory round trip plus its LDS work; the stores are shaped
 // so that a wave's store touches few cache lines (a token's slot row as one
@@ -672,6 +675,290 @@ __global__ __launch_bounds__(kFinBS) void layout_finalize_kernel(
     if (tid == 0) *L.status = s_err;
 }
 
+// One-launch layout (top-k <= 8, batches up to a few thousand tokens): a
+// 1024-thread workgroup per tile of 256 tokens. Every workgroup counts the
+// valid entries of all T tokens itself, into LDS histograms split into the
+// tokens before its tile and the others, so it has each expert's and group's
+// total (hence the offsets) and its tile's base in every column with no
+// second launch and no exchange between workgroups. The split is uniform per
+// wave: a wave's 64 consecutive tokens lie on one side of the tile boundary (a
+// multiple of 64). Waves 0-3 then rank the tile's own tokens with the
+// per-(expert, wave) words and write its entries as the place kernel does.
+// Each workgroup reads the T*K indices once (from L2 after the first).
+constexpr int kOpBS = kFinBS;          // 1024 threads: one expert per thread (E <= 1024)
+constexpr int kOpTok = 4;              // tokens per thread per round of the count
+static_assert(kOpBS >= 1024, "one expert per thread");
+
+// Count one token's valid entries into the histogram h (expert bins) and
+// return the groups it reaches. Branch-free (this code runs once per CU from a
+// cold instruction cache, so its length is its cost): an entry that does not
+// count adds 0 to a bin chosen by the lane, so no exec-mask regions and no
+// same-address pile-up. Error bits go to er.
+template <int KMAX>
+__device__ __forceinline__ uint32_t onepass_token(const int (&e)[KMAX], bool live, int K, int E,
+                                                  uint32_t gmagic, int *h, int lane, int &er)
+{
+    uint32_t gm = 0;
+    const int spare = lane < E ? lane : 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int x = e[k];
+        const bool in = live && k < K && (unsigned)x < (unsigned)E;
+        bool rep = false;
+#pragma unroll
+        for (int q = 0; q < k; ++q) rep = rep || e[q] == x;
+        const bool v = in && !rep;
+        er |= (live && k < K && !in) ? 1 : 0;
+        er |= (in && rep) ? 2 : 0;
+        atomicAdd(&h[v ? x : spare], v ? 1 : 0);
+        gm |= v ? 1u << group_of(x, gmagic) : 0u;
+    }
+    return gm;
+}
+
+template <int KMAX, bool EXACT>
+__global__ __launch_bounds__(kOpBS) void layout_onepass_kernel(
+    const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic, LayoutPtrs L, int vec)
+{
+    static_assert(KMAX <= 8, "the tile's entries are staged for at most 8 per token");
+    // dynamic LDS: emask [E][kWaves] u64, then int hb[E], ha[E], off_e[E][kWaves], ldelta[E]
+    extern __shared__ unsigned long long emask[];
+    int *hb = reinterpret_cast<int *>(emask + E * kWaves);
+    int *ha = hb + E;
+    int *off_e = ha + E;
+    int *ldelta = off_e + E * kWaves;
+    __shared__ int32_t s_src[kLayoutTile * KMAX];   // the tile's pair ids in slot order
+    __shared__ int32_t s_dst[kLayoutTile * KMAX];   // and their receive slots
+    __shared__ int s_wave_tot[kFinWaves];
+    __shared__ int gb[kMaxG], ga[kMaxG], base_g[kMaxG];
+    __shared__ int off_g[kMaxG][kWaves];
+    __shared__ uint64_t gball[kMaxG][kWaves];
+    __shared__ int s_err;
+    const int K = EXACT ? KMAX : Krt;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int tile = blockIdx.x;
+    const int t0 = tile * kLayoutTile;
+    const bool mine = tid < kLayoutTile;   // waves 0-3 hold the tile's tokens
+    const int t = t0 + tid;
+
+    // the first round of the count and the tile's own tokens: one round trip
+    int e0[KMAX], e1[KMAX], e2[KMAX], e3[KMAX];
+    load_row<KMAX>(idx, tid, T, K, e0);
+    load_row<KMAX>(idx, kOpBS + tid, T, K, e1);
+    load_row<KMAX>(idx, 2 * kOpBS + tid, T, K, e2);
+    load_row<KMAX>(idx, 3 * kOpBS + tid, T, K, e3);
+    int eo[KMAX];
+    load_row<KMAX>(idx, t, T, K, eo);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int i = tid; i < E * kWaves; i += kOpBS) emask[i] = 0ull;
+    for (int x = tid; x < E; x += kOpBS) hb[x] = ha[x] = 0;
+    if (tid < kMaxG) gb[tid] = ga[tid] = 0;
+    if (tid == 0) s_err = 0;
+    __syncthreads();
+
+    // Tokens r0 + j * kOpBS + tid, j < kOpTok, per round; rows rotate through
+    // e0 (the loop is not unrolled, to keep the code short). Lane g < G keeps
+    // the wave's count of group g, split before / not before the tile.
+    int er = 0, accb = 0, acca = 0;
+    for (int r0 = 0;;) {
+#pragma unroll 1
+        for (int j = 0; j < kOpTok; ++j) {
+            const int ub = r0 + j * kOpBS + wave * kWave;   // the wave's first token
+            if (ub < T) {                                     // uniform
+                const int u = ub + lane;
+                const bool before = ub < t0;                  // uniform
+                const uint32_t gm = onepass_token<KMAX>(e0, u < T, K, E, gmagic, before ? hb : ha, lane, er);
+                for (int g = 0; g < G; ++g) {
+                    const int c = __popcll(__ballot((gm >> g) & 1u));
+                    const int add = lane == g ? c : 0;
+                    accb += before ? add : 0;
+                    acca += before ? 0 : add;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                e0[k] = e1[k];
+                e1[k] = e2[k];
+                e2[k] = e3[k];
+            }
+        }
+        r0 += kOpBS * kOpTok;
+        if (r0 >= T) break;
+        load_row<KMAX>(idx, r0 + tid, T, K, e0);
+        load_row<KMAX>(idx, r0 + kOpBS + tid, T, K, e1);
+        load_row<KMAX>(idx, r0 + 2 * kOpBS + tid, T, K, e2);
+        load_row<KMAX>(idx, r0 + 3 * kOpBS + tid, T, K, e3);
+    }
+    if (lane < G) {
+        atomicAdd(&gb[lane], accb);
+        atomicAdd(&ga[lane], acca);
+    }
+    if (er) atomicOr(&s_err, er);
+    // the tile's words (waves 0-3), built while the counts settle
+    // the tile's words (waves 0-3): the same classification, OR-ing 0 for an
+    // entry that does not count
+    uint32_t gm_t = 0, bad_t = 0;
+    if (mine) {   // uniform per wave
+        const bool live = t < T;
+        const unsigned long long bit = 1ull << lane;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const int x = eo[k];
+            const bool in = live && k < K && (unsigned)x < (unsigned)E;
+            bool rep = false;
+#pragma unroll
+            for (int q = 0; q < k; ++q) rep = rep || eo[q] == x;
+            const bool v = in && !rep;
+            bad_t |= (k < K && !v) ? 1u << k : 0u;
+            atomicOr(&emask[(v ? x : 0) * kWaves + wave], v ? bit : 0ull);
+            gm_t |= v ? 1u << group_of(x, gmagic) : 0u;
+        }
+        uint64_t mine_b = 0;
+        for (int g = 0; g < G; ++g) {
+            const uint64_t b = __ballot((gm_t >> g) & 1u);
+            mine_b = lane == g ? b : mine_b;
+        }
+        if (lane < G) gball[lane][wave] = mine_b;
+    }
+    __syncthreads();
+
+    // offsets: an exclusive scan over the experts (one per thread) of the totals;
+    // the tile's base in column x is x's offset plus the count before the tile
+    const int x = tid;
+    const int cb = x < E ? hb[x] : 0, ca = x < E ? ha[x] : 0;
+    int etot;
+    const int eoff = fin_scan(cb + ca, s_wave_tot, etot);
+    const int base_x = eoff + cb;
+    if (tile == 0) {
+        if (x < E) {
+            L.expert_count[x] = cb + ca;
+            L.expert_offset[x] = eoff;
+        }
+        if (x == 0) L.expert_offset[E] = etot;
+    }
+    if (wave == 0) {   // groups: an exclusive scan over the G <= 32 totals
+        const int gbv = lane < G ? gb[lane] : 0;
+        const int gt = lane < G ? gbv + ga[lane] : 0;
+        int incl = gt;
+#pragma unroll
+        for (int o = 1; o < kMaxG; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane < G) {
+            const int goff = incl - gt;
+            if (tile == 0) {
+                L.group_count[lane] = gt;
+                L.group_offset[lane] = goff;
+            }
+            base_g[lane] = goff + gbv;
+        }
+        if (tile == 0 && lane == G - 1) L.group_offset[G] = incl;
+        if (tile == 0 && lane == 0) *L.status = s_err;
+    }
+    // per (expert, wave) offsets of the tile, and each expert's first position
+    // in the tile's slot-ordered pair list
+    int cnt = 0;
+    if (x < E) {
+        const unsigned long long *m = emask + x * kWaves;
+        int r = base_x;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            off_e[x * kWaves + w] = r;
+            r += __popcll(m[w]);
+        }
+        cnt = r - base_x;
+    }
+    __syncthreads();   // s_wave_tot and base_g
+    int npairs;
+    const int lex = fin_scan(cnt, s_wave_tot, npairs);
+    if (x < E) ldelta[x] = lex - base_x;
+    if (tid < G) {
+        int r = base_g[tid];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            off_g[tid][w] = r;
+            r += __popcll(gball[tid][w]);
+        }
+    }
+    __syncthreads();
+
+    if (mine && t < T) {
+        const uint32_t gm = gm_t, bad = bad_t;
+        const uint64_t below = lanemask_lt(lane);
+        const size_t p0 = (size_t)t * K;
+        L.tok_group_mask[t] = gm;
+        int se[KMAX], sg[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            se[k] = sg[k] = -1;
+            if (k < K && !((bad >> k) & 1u)) {
+                const int xe = eo[k];
+                se[k] = off_e[xe * kWaves + wave] + __popcll(emask[xe * kWaves + wave] & below);
+                const int g = group_of(xe, gmagic);
+                sg[k] = off_g[g][wave] + __popcll(gball[g][wave] & below);
+                const int li = se[k] + ldelta[xe];
+                if ((unsigned)li < (unsigned)(kLayoutTile * KMAX)) {   // always, by construction
+                    s_src[li] = (int32_t)(p0 + k);
+                    s_dst[li] = se[k];
+                }
+            }
+        }
+        if (EXACT && (vec & 1)) {   // 16-byte aligned slot arrays, K in {2, 4, 8}
+            if constexpr (KMAX == 2) {
+                *reinterpret_cast<u32x2 *>(L.slot_e + p0) = u32x2{(uint32_t)se[0], (uint32_t)se[1]};
+                *reinterpret_cast<u32x2 *>(L.slot_g + p0) = u32x2{(uint32_t)sg[0], (uint32_t)sg[1]};
+            } else {
+#pragma unroll
+                for (int k = 0; k < KMAX; k += 4) {
+                    *reinterpret_cast<u32x4 *>(L.slot_e + p0 + k) =
+                        u32x4{(uint32_t)se[k], (uint32_t)se[k + 1], (uint32_t)se[k + 2], (uint32_t)se[k + 3]};
+                    *reinterpret_cast<u32x4 *>(L.slot_g + p0 + k) =
+                        u32x4{(uint32_t)sg[k], (uint32_t)sg[k + 1], (uint32_t)sg[k + 2], (uint32_t)sg[k + 3]};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (k < K) {
+                    L.slot_e[p0 + k] = se[k];
+                    L.slot_g[p0 + k] = sg[k];
+                }
+            }
+        }
+        // (the receive lists hold T*K and T*min(K, G) entries; the guards below
+        // hold by construction and keep a wrong count from writing past them)
+        const int64_t ng = (int64_t)T * (K < G ? K : G);
+        int32_t *tg = L.slot_tg + (size_t)t * G;
+        for (int g0 = 0; g0 < G; g0 += 4) {
+            int s4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int g = g0 + u;
+                s4[u] = -1;
+                if (g < G && ((gm >> g) & 1u)) {
+                    s4[u] = off_g[g][wave] + __popcll(gball[g][wave] & below);
+                    if (s4[u] >= 0 && s4[u] < ng) L.recv_src_g[s4[u]] = t;
+                }
+            }
+            if (vec & 2) {   // G % 4 == 0 and slot_tg 16-byte aligned
+                *reinterpret_cast<u32x4 *>(tg + g0) = u32x4{(uint32_t)s4[0], (uint32_t)s4[1], (uint32_t)s4[2], (uint32_t)s4[3]};
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (g0 + u < G) tg[g0 + u] = s4[u];
+            }
+        }
+    }
+    __syncthreads();
+    const int64_t ne = (int64_t)T * K;
+    const int np = npairs < kLayoutTile * KMAX ? npairs : kLayoutTile * KMAX;
+    for (int i = tid; i < np; i += kOpBS) {
+        const int s = s_dst[i];
+        if (s >= 0 && s < ne) L.recv_src_e[s] = s_src[i];
+    }
+}
+
 // No tokens: every count and offset is 0 and the status is clear.
 __global__ __launch_bounds__(kLayoutTile) void layout_empty_kernel(int E, int G, LayoutPtrs L)
 {
@@ -694,6 +981,7 @@ using CountFn = void (*)(const int32_t *, int, int, int, int, uint32_t, uint32_t
                          uint32_t *);
 using PlaceFn = void (*)(const int32_t *, int, int, int, int, uint32_t, int, const int32_t *,
                          const uint32_t *, LayoutPtrs, int);
+using OnepassFn = void (*)(const int32_t *, int, int, int, int, uint32_t, LayoutPtrs, int);
 
 void pick_layout(int K, CountFn &count, PlaceFn &place)
 {
@@ -724,6 +1012,15 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
     // vector stores of the slot rows when the arrays allow them
     const auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     const int vec = (a16(L.slot_e) && a16(L.slot_g) ? 1 : 0) | (G % 4 == 0 && a16(L.slot_tg) ? 2 : 0);
+    if (K <= 8 && (int64_t)T * K <= tuning().layout_onepass_max_pairs) {
+        OnepassFn onepass = K == 2 ? layout_onepass_kernel<2, true>
+                          : K == 4 ? layout_onepass_kernel<4, true>
+                          : K == 8 ? layout_onepass_kernel<8, true>
+                                   : layout_onepass_kernel<8, false>;
+        const size_t lds = (size_t)E * kWaves * sizeof(unsigned long long) + (size_t)E * (kWaves + 3) * sizeof(int);
+        hipLaunchKernelGGL(onepass, dim3(ntiles), dim3(kOpBS), lds, stream, idx, T, K, E, G, gmagic, L, vec);
+        return hipGetLastError();
+    }
     CountFn count;
     PlaceFn place;
     pick_layout(K, count, place);

@@ -100,6 +100,8 @@ EDGE_SHAPES = [
     (0, 8, 256, 8), (1, 8, 256, 8), (1, 1, 1, 1), (255, 8, 256, 8), (256, 8, 256, 8),
     (257, 8, 256, 8), (1000, 1, 7, 7), (777, 32, 64, 32), (513, 6, 1024, 32), (4097, 8, 256, 1),
     (300, 2, 8, 8), (2000, 3, 12, 4), (1025, 8, 1000, 8), (600, 16, 16, 16),
+    # either side of the one-launch layout's limit (T * K <= 16384), and rounds of its count
+    (2048, 8, 256, 8), (2049, 8, 256, 8), (4096, 4, 64, 8), (8192, 2, 8, 8), (5000, 3, 1024, 32),
 ]
 
 
