@@ -220,6 +220,97 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     }
 }
 
+// A token's slot_tg row (four groups per store where the array allows) and
+// its group receive-list entries.
+__device__ __forceinline__ void token_group_entries(int t, int T, int K, int G, int wave, uint64_t below,
+                                                    uint32_t gm, const int (*off_g)[kWaves],
+                                                    const uint64_t (*gball)[kWaves], const LayoutPtrs &L,
+                                                    int vec)
+{
+    int32_t *tg = L.slot_tg + (size_t)t * G;
+    for (int g0 = 0; g0 < G; g0 += 4) {
+        int s4[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g = g0 + u;
+            s4[u] = -1;
+            if (g < G && ((gm >> g) & 1u)) {
+                s4[u] = off_g[g][wave] + __popcll(gball[g][wave] & below);
+                L.recv_src_g[s4[u]] = t;
+            }
+        }
+        if (vec & 2) {   // G % 4 == 0 and slot_tg 16-byte aligned
+            *reinterpret_cast<u32x4 *>(tg + g0) = u32x4{(uint32_t)s4[0], (uint32_t)s4[1], (uint32_t)s4[2], (uint32_t)s4[3]};
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (g0 + u < G) tg[g0 + u] = s4[u];
+        }
+    }
+}
+
+// A token's layout entries from its tile's words and per-(column, wave)
+// offsets (top-k <= 8; lane `lane` of wave `wave` holds token t < T with
+// entries e, groups gm and non-counting entries bad): its slot_e / slot_g row,
+// its slot_tg row and its group receive-list entries; its expert
+// receive-list entries are staged in slot order (s_src, s_dst) for the caller
+// to write as runs.
+template <int KMAX, bool EXACT>
+__device__ __forceinline__ void tile_token_entries(
+    int t, int T, int K, int G, uint32_t gmagic, int wave, int lane, const int (&e)[KMAX], uint32_t gm,
+    uint32_t bad, const unsigned long long *emask, const int *off_e, const int *ldelta,
+    const int (*off_g)[kWaves], const uint64_t (*gball)[kWaves], int32_t *s_src, int32_t *s_dst,
+    const LayoutPtrs &L, int vec)
+{
+    const uint64_t below = lanemask_lt(lane);
+    const size_t p0 = (size_t)t * K;
+    int se[KMAX], sg[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        se[k] = sg[k] = -1;
+        if (k < K && !((bad >> k) & 1u)) {
+            const int x = e[k];
+            se[k] = off_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
+            const int g = group_of(x, gmagic);
+            sg[k] = off_g[g][wave] + __popcll(gball[g][wave] & below);
+            const int li = se[k] + ldelta[x];
+            s_src[li] = (int32_t)(p0 + k);
+            s_dst[li] = se[k];
+        }
+    }
+    if (EXACT && (vec & 1)) {   // 16-byte aligned slot arrays, K in {2, 4, 8}
+        if constexpr (KMAX == 2) {
+            *reinterpret_cast<u32x2 *>(L.slot_e + p0) = u32x2{(uint32_t)se[0], (uint32_t)se[1]};
+            *reinterpret_cast<u32x2 *>(L.slot_g + p0) = u32x2{(uint32_t)sg[0], (uint32_t)sg[1]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; k += 4) {
+                *reinterpret_cast<u32x4 *>(L.slot_e + p0 + k) =
+                    u32x4{(uint32_t)se[k], (uint32_t)se[k + 1], (uint32_t)se[k + 2], (uint32_t)se[k + 3]};
+                *reinterpret_cast<u32x4 *>(L.slot_g + p0 + k) =
+                    u32x4{(uint32_t)sg[k], (uint32_t)sg[k + 1], (uint32_t)sg[k + 2], (uint32_t)sg[k + 3]};
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k < K) {
+                L.slot_e[p0 + k] = se[k];
+                L.slot_g[p0 + k] = sg[k];
+            }
+        }
+    }
+    token_group_entries(t, T, K, G, wave, below, gm, off_g, gball, L, vec);
+}
+
+// The staged expert receive-list entries of a tile, written as runs by
+// threads tid, tid + nthreads, ...
+__device__ __forceinline__ void tile_write_recv_src_e(int npairs, const int32_t *s_src, const int32_t *s_dst,
+                                                      int32_t *recv_src_e, int tid, int nthreads)
+{
+    for (int i = tid; i < npairs; i += nthreads) recv_src_e[s_dst[i]] = s_src[i];
+}
+
 // Exclusive prefix sum over the 256 threads of the workgroup; *total gets the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave_tot, int *total)
 {
@@ -476,47 +567,13 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     }
     __syncthreads();
 
-    const uint64_t below = lanemask_lt(lane);
     if (t < T) {
-        const size_t p0 = (size_t)t * K;
         if constexpr (kStage) {
-            int se[KMAX], sg[KMAX];
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                se[k] = sg[k] = -1;
-                if (k < K && !((bad >> k) & 1u)) {
-                    const int x = e[k];
-                    se[k] = off_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
-                    const int g = group_of(x, gmagic);
-                    sg[k] = off_g[g][wave] + __popcll(gball[g][wave] & below);
-                    const int li = se[k] + ldelta[x];
-                    s_src[li] = (int32_t)(p0 + k);
-                    s_dst[li] = se[k];
-                }
-            }
-            if (EXACT && (vec & 1)) {   // 16-byte aligned slot arrays, K in {2, 4, 8}
-                if constexpr (KMAX == 2) {
-                    *reinterpret_cast<u32x2 *>(L.slot_e + p0) = u32x2{(uint32_t)se[0], (uint32_t)se[1]};
-                    *reinterpret_cast<u32x2 *>(L.slot_g + p0) = u32x2{(uint32_t)sg[0], (uint32_t)sg[1]};
-                } else {
-#pragma unroll
-                    for (int k = 0; k < KMAX; k += 4) {
-                        *reinterpret_cast<u32x4 *>(L.slot_e + p0 + k) =
-                            u32x4{(uint32_t)se[k], (uint32_t)se[k + 1], (uint32_t)se[k + 2], (uint32_t)se[k + 3]};
-                        *reinterpret_cast<u32x4 *>(L.slot_g + p0 + k) =
-                            u32x4{(uint32_t)sg[k], (uint32_t)sg[k + 1], (uint32_t)sg[k + 2], (uint32_t)sg[k + 3]};
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int k = 0; k < KMAX; ++k) {
-                    if (k < K) {
-                        L.slot_e[p0 + k] = se[k];
-                        L.slot_g[p0 + k] = sg[k];
-                    }
-                }
-            }
+            tile_token_entries<KMAX, EXACT>(t, T, K, G, gmagic, wave, lane, e, gm, bad, emask, off_e, ldelta,
+                                            off_g, gball, s_src, s_dst, L, vec);
         } else {
+            const uint64_t below = lanemask_lt(lane);
+            const size_t p0 = (size_t)t * K;
 #pragma unroll
             for (int k = 0; k < KMAX; ++k) {
                 if (k < K) {
@@ -532,32 +589,12 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
                     L.slot_g[p0 + k] = sg;
                 }
             }
-        }
-        // slot_tg row (G entries) and the group receive lists, four groups at a time
-        int32_t *tg = L.slot_tg + (size_t)t * G;
-        for (int g0 = 0; g0 < G; g0 += 4) {
-            int s4[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int g = g0 + u;
-                s4[u] = -1;
-                if (g < G && ((gm >> g) & 1u)) {
-                    s4[u] = off_g[g][wave] + __popcll(gball[g][wave] & below);
-                    L.recv_src_g[s4[u]] = t;
-                }
-            }
-            if (vec & 2) {   // G % 4 == 0 and slot_tg 16-byte aligned
-                *reinterpret_cast<u32x4 *>(tg + g0) = u32x4{(uint32_t)s4[0], (uint32_t)s4[1], (uint32_t)s4[2], (uint32_t)s4[3]};
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (g0 + u < G) tg[g0 + u] = s4[u];
-            }
+            token_group_entries(t, T, K, G, wave, below, gm, off_g, gball, L, vec);
         }
     }
     if constexpr (kStage) {
         __syncthreads();
-        for (int i = tid; i < npairs; i += kLayoutTile) L.recv_src_e[s_dst[i]] = s_src[i];
+        tile_write_recv_src_e(npairs, s_src, s_dst, L.recv_src_e, tid, kLayoutTile);
     }
 }
 
@@ -883,80 +920,12 @@ __global__ __launch_bounds__(kOpBS) void layout_onepass_kernel(
     }
     __syncthreads();
 
-    if (mine && t < T) {
-        const uint32_t gm = gm_t, bad = bad_t;
-        const uint64_t below = lanemask_lt(lane);
-        const size_t p0 = (size_t)t * K;
-        L.tok_group_mask[t] = gm;
-        int se[KMAX], sg[KMAX];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            se[k] = sg[k] = -1;
-            if (k < K && !((bad >> k) & 1u)) {
-                const int xe = eo[k];
-                se[k] = off_e[xe * kWaves + wave] + __popcll(emask[xe * kWaves + wave] & below);
-                const int g = group_of(xe, gmagic);
-                sg[k] = off_g[g][wave] + __popcll(gball[g][wave] & below);
-                const int li = se[k] + ldelta[xe];
-                if ((unsigned)li < (unsigned)(kLayoutTile * KMAX)) {   // always, by construction
-                    s_src[li] = (int32_t)(p0 + k);
-                    s_dst[li] = se[k];
-                }
-            }
-        }
-        if (EXACT && (vec & 1)) {   // 16-byte aligned slot arrays, K in {2, 4, 8}
-            if constexpr (KMAX == 2) {
-                *reinterpret_cast<u32x2 *>(L.slot_e + p0) = u32x2{(uint32_t)se[0], (uint32_t)se[1]};
-                *reinterpret_cast<u32x2 *>(L.slot_g + p0) = u32x2{(uint32_t)sg[0], (uint32_t)sg[1]};
-            } else {
-#pragma unroll
-                for (int k = 0; k < KMAX; k += 4) {
-                    *reinterpret_cast<u32x4 *>(L.slot_e + p0 + k) =
-                        u32x4{(uint32_t)se[k], (uint32_t)se[k + 1], (uint32_t)se[k + 2], (uint32_t)se[k + 3]};
-                    *reinterpret_cast<u32x4 *>(L.slot_g + p0 + k) =
-                        u32x4{(uint32_t)sg[k], (uint32_t)sg[k + 1], (uint32_t)sg[k + 2], (uint32_t)sg[k + 3]};
-                }
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (k < K) {
-                    L.slot_e[p0 + k] = se[k];
-                    L.slot_g[p0 + k] = sg[k];
-                }
-            }
-        }
-        // (the receive lists hold T*K and T*min(K, G) entries; the guards below
-        // hold by construction and keep a wrong count from writing past them)
-        const int64_t ng = (int64_t)T * (K < G ? K : G);
-        int32_t *tg = L.slot_tg + (size_t)t * G;
-        for (int g0 = 0; g0 < G; g0 += 4) {
-            int s4[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int g = g0 + u;
-                s4[u] = -1;
-                if (g < G && ((gm >> g) & 1u)) {
-                    s4[u] = off_g[g][wave] + __popcll(gball[g][wave] & below);
-                    if (s4[u] >= 0 && s4[u] < ng) L.recv_src_g[s4[u]] = t;
-                }
-            }
-            if (vec & 2) {   // G % 4 == 0 and slot_tg 16-byte aligned
-                *reinterpret_cast<u32x4 *>(tg + g0) = u32x4{(uint32_t)s4[0], (uint32_t)s4[1], (uint32_t)s4[2], (uint32_t)s4[3]};
-            } else {
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (g0 + u < G) tg[g0 + u] = s4[u];
-            }
-        }
-    }
+    if (mine && t < T)
+        tile_token_entries<KMAX, EXACT>(t, T, K, G, gmagic, wave, lane, eo, gm_t, bad_t, emask, off_e, ldelta,
+                                        off_g, gball, s_src, s_dst, L, vec);
+    if (mine && t < T) L.tok_group_mask[t] = gm_t;
     __syncthreads();
-    const int64_t ne = (int64_t)T * K;
-    const int np = npairs < kLayoutTile * KMAX ? npairs : kLayoutTile * KMAX;
-    for (int i = tid; i < np; i += kOpBS) {
-        const int s = s_dst[i];
-        if (s >= 0 && s < ne) L.recv_src_e[s] = s_src[i];
-    }
+    tile_write_recv_src_e(npairs, s_src, s_dst, L.recv_src_e, tid, kOpBS);
 }
 
 // No tokens: every count and offset is 0 and the status is clear.
