@@ -381,8 +381,9 @@ __device__ __forceinline__ void column_sums(const int32_t *__restrict__ table, i
 // the table, coalesced: thread x reads column x); then the tile's LDS words
 // are rebuilt exactly as the count kernel built them, and each pair's slot is
 // its expert's offset for this (tile, wave) plus its rank among the wave's
-// lanes.
-template <int KMAX, bool EXACT>
+// lanes. Experts are owned in NCH chunks of 256 (x = chunk * 256 + tid):
+// NCH = 1 for E <= 256 keeps the code and its registers to one chunk.
+template <int KMAX, bool EXACT, int NCH>
 __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic,
     int ntiles, const int32_t *__restrict__ table, const uint32_t *__restrict__ words, LayoutPtrs L,
@@ -412,9 +413,9 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     // All global loads first (table columns, the tile's tokens, its words), so
     // that they share one memory round trip: nothing below consumes them
     // before the scheduling barrier.
-    int c0[kMaxEChunks][kBatch], cg0[kBatch];
+    int c0[NCH][kBatch], cg0[kBatch];
 #pragma unroll
-    for (int j = 0; j < kMaxEChunks; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         const int x = j * kLayoutTile + tid;
         if (j * kLayoutTile < E)   // uniform
             column_first(table, rows, x < E ? x : E - 1, ntiles, c0[j]);
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     int e[KMAX];
     load_row<KMAX>(idx, t, T, K, e);
     // the tile's words from the count kernel (top-k <= 8)
-    constexpr int kWordsPerThread = kMaxEChunks * kWaves;
+    constexpr int kWordsPerThread = NCH * kWaves;
     uint32_t wlo[kStage ? kWordsPerThread : 1], whi[kStage ? kWordsPerThread : 1];
     if constexpr (kStage) {
         const uint32_t *wt = words + (size_t)tile * E * kWaves * 2;
@@ -446,9 +447,9 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     if (tid == 0) s_err = 0;
 
     // expert offsets: experts are owned in chunks of 256 (x = chunk * 256 + tid)
-    int tot[kMaxEChunks], pre[kMaxEChunks];
+    int tot[NCH], pre[NCH];
 #pragma unroll
-    for (int j = 0; j < kMaxEChunks; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         tot[j] = pre[j] = 0;
         const int x = j * kLayoutTile + tid;
         if (j * kLayoutTile < E) {   // uniform; lanes past E sum column E - 1 and drop it
@@ -479,9 +480,9 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
         }
     }
     int carry = 0;
-    int base[kMaxEChunks];
+    int base[NCH];
 #pragma unroll
-    for (int j = 0; j < kMaxEChunks; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         base[j] = 0;
         if (j * kLayoutTile < E) {   // uniform
             int all;
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     // slot-ordered pair list (an exclusive scan over experts of the tile's counts).
     int npairs = 0;
 #pragma unroll
-    for (int j = 0; j < kMaxEChunks; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         if (j * kLayoutTile < E) {   // uniform
             const int x = j * kLayoutTile + tid;
             int cnt = 0;
@@ -952,16 +953,23 @@ using PlaceFn = void (*)(const int32_t *, int, int, int, int, uint32_t, int, con
                          const uint32_t *, LayoutPtrs, int);
 using OnepassFn = void (*)(const int32_t *, int, int, int, int, uint32_t, LayoutPtrs, int);
 
-void pick_layout(int K, CountFn &count, PlaceFn &place)
+template <int NCH>
+void pick_layout_n(int K, CountFn &count, PlaceFn &place)
 {
     switch (K) {
-    case 2: count = layout_count_kernel<2, true>; place = layout_place_kernel<2, true>; break;
-    case 4: count = layout_count_kernel<4, true>; place = layout_place_kernel<4, true>; break;
-    case 8: count = layout_count_kernel<8, true>; place = layout_place_kernel<8, true>; break;
+    case 2: count = layout_count_kernel<2, true>; place = layout_place_kernel<2, true, NCH>; break;
+    case 4: count = layout_count_kernel<4, true>; place = layout_place_kernel<4, true, NCH>; break;
+    case 8: count = layout_count_kernel<8, true>; place = layout_place_kernel<8, true, NCH>; break;
     default:
-        if (K <= 8) { count = layout_count_kernel<8, false>; place = layout_place_kernel<8, false>; }
-        else { count = layout_count_kernel<32, false>; place = layout_place_kernel<32, false>; }
+        if (K <= 8) { count = layout_count_kernel<8, false>; place = layout_place_kernel<8, false, NCH>; }
+        else { count = layout_count_kernel<32, false>; place = layout_place_kernel<32, false, NCH>; }
     }
+}
+
+void pick_layout(int K, int E, CountFn &count, PlaceFn &place)
+{
+    if (E <= kLayoutTile) pick_layout_n<1>(K, count, place);
+    else pick_layout_n<kMaxEChunks>(K, count, place);
 }
 
 }  // namespace
@@ -992,7 +1000,7 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
     }
     CountFn count;
     PlaceFn place;
-    pick_layout(K, count, place);
+    pick_layout(K, E, count, place);
     hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G, gmagic,
                        L.tok_group_mask, w.table, w.words, w.gwords);
     hipError_t e = hipGetLastError();
@@ -1009,7 +1017,7 @@ hipError_t launch_layout_count_finalize(const int32_t *idx, int T, int K, int E,
     const LayoutWs w = layout_ws(ws, T, E, G);
     CountFn count;
     PlaceFn place;
-    pick_layout(K, count, place);
+    pick_layout(K, E, count, place);
     const size_t lds1 = (size_t)E * kWaves * sizeof(unsigned long long);
     hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G,
                        group_magic(E, G), L.tok_group_mask, w.table, w.words, w.gwords);
