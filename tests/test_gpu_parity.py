@@ -112,10 +112,13 @@ def test_layout_edge_shapes(moe, orc, T, K, E, G):
     check_layout(L, orc.layout(idx, E, G))
 
 
-@pytest.mark.parametrize("seed", range(6))
+# seeds 0-5: T * K <= 16384 (the one-launch layout); 6-8: larger (count + place)
+@pytest.mark.parametrize("seed", range(9))
 def test_layout_invalid_entries(moe, orc, seed):
     rng = np.random.default_rng(seed)
     T, K, E, G = int(rng.integers(200, 900)), int(rng.integers(2, 9)), 64, 8
+    if seed >= 6:
+        T, K = int(rng.integers(2100, 4000)), 8
     idx = rng.integers(0, E, size=(T, K)).astype(np.int32)           # repeats likely
     bad = rng.random((T, K)) < 0.05
     idx[bad] = rng.choice([-1, -7, E, E + 5, 1 << 30], size=int(bad.sum()))
@@ -125,11 +128,12 @@ def test_layout_invalid_entries(moe, orc, seed):
     check_layout(L, Lo)
 
 
-def test_layout_reuses_buffers_without_stale_state(moe, orc):
+@pytest.mark.parametrize("T", [1500, 2500])   # one launch; count + place
+def test_layout_reuses_buffers_without_stale_state(moe, orc, T):
     """A layout written into buffers that hold an earlier, different layout equals a
     fresh one (the stale-map hazard of cached routing)."""
-    a = si.make_inputs(1500, 8, 256, 8, seed=41)["topk_idx"]
-    b = si.make_inputs(1500, 8, 256, 8, seed=42)["topk_idx"]
+    a = si.make_inputs(T, 8, 256, 8, seed=41)["topk_idx"]
+    b = si.make_inputs(T, 8, 256, 8, seed=42)["topk_idx"]
     b[:7, 3] = 999                                                    # invalid entries in b
     L = moe.moe_layout(to_dev(a), 256, 8)
     L = moe.moe_layout(to_dev(b), 256, 8, out=L)
