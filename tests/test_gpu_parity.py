@@ -102,6 +102,8 @@ EDGE_SHAPES = [
     (300, 2, 8, 8), (2000, 3, 12, 4), (1025, 8, 1000, 8), (600, 16, 16, 16),
     # either side of the one-launch layout's limit (T * K <= 16384), and rounds of its count
     (2048, 8, 256, 8), (2049, 8, 256, 8), (4096, 4, 64, 8), (8192, 2, 8, 8), (5000, 3, 1024, 32),
+    # every token takes every expert (K = E), with G = E, G = 1 and between; above the limit too
+    (300, 32, 32, 32), (200, 8, 8, 1), (700, 16, 16, 4), (2500, 8, 8, 8),
 ]
 
 
@@ -196,6 +198,7 @@ def test_dispatch_bf16_full_workloads(moe, orc, name, mode):
 DISPATCH_EDGE = [  # (T, H, E, G, K): ragged / multi-pass hidden sizes, one group, one expert per group
     (1, 8, 8, 8, 2), (3, 520, 16, 4, 3), (129, 1024, 32, 8, 4), (40, 16392, 64, 8, 8),
     (300, 4096, 128, 1, 8), (77, 2048, 8, 8, 2), (513, 7168, 256, 8, 8), (50, 8200, 16, 16, 16),
+    (60, 1024, 16, 4, 16), (5, 8, 1, 1, 1),   # K = E: every expert of every token; one expert
 ]
 
 
@@ -358,7 +361,7 @@ def test_combine_full_workloads(moe, orc, name, mode):
 
 COMBINE_EDGE = [(1, 8, 8, 8, 2), (3, 520, 16, 4, 3), (200, 1024, 32, 8, 5), (40, 16392, 64, 8, 8),
                 (300, 4096, 128, 1, 8), (100, 2048, 64, 32, 32), (77, 7168, 256, 8, 4),
-                (90, 3072, 96, 4, 6)]
+                (90, 3072, 96, 4, 6), (64, 2048, 32, 32, 32), (33, 1024, 8, 2, 8), (5, 8, 1, 1, 1)]
 
 
 @pytest.mark.parametrize("T,H,E,G,K", COMBINE_EDGE)
