@@ -822,3 +822,55 @@ def test_nonfinite_values_match_oracle(moe, orc):
     L2, D2 = moe.moe_layout_dispatch(idx_d, E, G, x_d, w_d, "expert", "fp8", out_layout=L2, out=D2,
                                      use_workspace=False)
     fp8_check(D2, orc.dispatch_fp8(Lo, "expert", x, w, idx))
+
+
+# ------------------------------------------------------------------ FP8 over a wide dynamic range
+
+def test_fp8_wide_dynamic_range_matches_oracle(moe, orc):
+    """Rows whose 128-blocks have amax anywhere from 2^-110 to 2^120 and elements down to 40
+    binades below their block's amax (e4m3 subnormal codes, values that round to zero,
+    bf16 subnormal inputs), with exact zeros of both signs: FP8 dispatch in both layouts,
+    dequantisation and cast-transpose (scales that saturate part of each expert) all bit
+    for bit as the oracle's."""
+    T, H, E, G, K = 200, 2048, 32, 4, 4
+    d = si.make_inputs(T, H, E, K, seed=77)
+    rng = np.random.default_rng(77)
+    nb = H // 128
+    block_e = rng.uniform(-110, 120, (T, nb, 1))                      # log2 of each block's amax
+    below = rng.uniform(0, 40, (T, nb, 128))                           # binades below it
+    below[:, :, 0] = 0                                                  # one element at the amax
+    mag = np.exp2(block_e - below)
+    sign = np.where(rng.random((T, nb, 128)) < 0.5, -1.0, 1.0)
+    xf = (sign * mag).reshape(T, H).astype(np.float32)
+    xf[rng.random((T, H)) < 0.05] = 0.0
+    xf[rng.random((T, H)) < 0.02] = -0.0
+    x = torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bf = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float().numpy()
+    amax = np.abs(bf.reshape(T, nb, 128)).max(axis=2)
+    assert amax.min() > 2.0 ** -112 and np.isfinite(amax).all()        # inside the supported range
+    assert np.any((np.abs(bf) < 2.0 ** -126) & (bf != 0))                # bf16 subnormal inputs occur
+    idx, w = d["topk_idx"], d["topk_w"]
+    idx_d, w_d, x_d = to_dev(idx), to_dev(w), dev_bf16(x)
+    L = moe.moe_layout(idx_d, E, G)
+    Lo = orc.layout(idx, E, G)
+    for mode in MODES:
+        D = dispatch_with_canary(moe, L, x_d, w_d, idx_d, mode, "fp8")
+        Do = orc.dispatch_fp8(Lo, mode, x, w, idx)
+        fp8_check(D, Do)
+        y = moe.moe_fp8_dequant(L, D.recv_x, D.recv_scale, mode)
+        np.testing.assert_array_equal(host_u16(y)[:Do["R"]], orc.dequant_fp8(Do["recv_q"], Do["recv_scale"]))
+    De = moe.moe_dispatch(L, x_d, w_d, idx_d, "expert")
+    Deo = orc.dispatch_bf16(Lo, "expert", x, w, idx)
+    off = Lo["expert_offset"]
+    rows = torch.from_numpy(Deo["recv_x"].view(np.int16)).view(torch.bfloat16).float().numpy()
+    scale = np.ones(E, np.float32)
+    for e in range(E):
+        if off[e + 1] > off[e]:
+            a = float(np.abs(rows[off[e]:off[e + 1]]).max())
+            scale[e] = np.float32(448.0 / a * 2.0 ** rng.uniform(-4, 4))   # part of the rows saturate
+    CT = moe.moe_cast_transpose_fp8(L, De.recv_x, to_dev(scale))
+    ref = orc.cast_transpose_fp8(off, Deo["recv_x"], scale)
+    np.testing.assert_array_equal(CT.c[:Lo["R_expert"]].cpu().numpy(), ref["c"])
+    nt = H * int(ref["pad_offset"][-1])
+    np.testing.assert_array_equal(CT.t[:nt].cpu().numpy(), ref["t"])
+    np.testing.assert_array_equal(CT.amax.cpu().numpy().view(np.uint32), ref["amax"].view(np.uint32))
