@@ -874,3 +874,37 @@ def test_fp8_wide_dynamic_range_matches_oracle(moe, orc):
     nt = H * int(ref["pad_offset"][-1])
     np.testing.assert_array_equal(CT.t[:nt].cpu().numpy(), ref["t"])
     np.testing.assert_array_equal(CT.amax.cpu().numpy().view(np.uint32), ref["amax"].view(np.uint32))
+
+
+def test_combine_wide_dynamic_range_matches_oracle(moe, orc):
+    """Expert outputs over the whole bf16 range (subnormals included) and weights from 2^-20
+    to 2^20 of either sign: sums that overflow to infinity, that land in the bf16 subnormal
+    range and that cancel to signed zeros, with the fma chain's k order. Bit for bit as the
+    oracle's, a NaN (both infinities in one sum) compared as a NaN."""
+    T, H, E, G, K = 300, 1024, 64, 8, 8
+    d = si.make_inputs(T, H, E, K, seed=78)
+    rng = np.random.default_rng(78)
+    idx = d["topk_idx"]
+    idx_d = to_dev(idx)
+    L = moe.moe_layout(idx_d, E, G)
+    Lo = orc.layout(idx, E, G)
+    # a fifth of the tokens read only tiny rows with weights <= 1: their sums are subnormal
+    tiny = rng.random(T) < 0.2
+    wmag = np.where(tiny[:, None], np.exp2(rng.uniform(-4, 0, (T, K))), np.exp2(rng.uniform(-20, 20, (T, K))))
+    w = (np.where(rng.random((T, K)) < 0.5, -1.0, 1.0) * wmag).astype(np.float32)
+    for mode in MODES:
+        R = Lo["R_expert"] if mode == "expert" else Lo["R_group"]
+        mag = np.exp2(rng.uniform(-140, 127.9, (R, H)))
+        sl = Lo["slot_e"].reshape(T, K) if mode == "expert" else Lo["slot_tg"].reshape(T, G)
+        own = sl[tiny].ravel()                                        # rows of one token each
+        own = own[own >= 0]
+        mag[own] = np.exp2(rng.uniform(-140, -128, (own.size, H)))
+        yf = (np.where(rng.random((R, H)) < 0.5, -1.0, 1.0) * mag).astype(np.float32)
+        yf[rng.random((R, H)) < 0.05] = 0.0
+        y_u16 = torch.from_numpy(yf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        out = host_u16(moe.moe_combine(L, dev_bf16(y_u16), to_dev(w), mode))
+        ref = orc.combine(Lo, mode, y_u16, w)
+        assert_bf16_equal_nan_by_class(out, ref)
+        r = ref[(ref & 0x7FFF) <= 0x7F80]
+        assert np.any((r & 0x7FFF) == 0x7F80)                                  # infinities
+        assert np.any(((r & 0x7F80) == 0) & ((r & 0x7F) != 0))                 # subnormal results
