@@ -908,3 +908,53 @@ def test_combine_wide_dynamic_range_matches_oracle(moe, orc):
         r = ref[(ref & 0x7FFF) <= 0x7F80]
         assert np.any((r & 0x7FFF) == 0x7F80)                                  # infinities
         assert np.any(((r & 0x7F80) == 0) & ((r & 0x7F) != 0))                 # subnormal results
+
+
+# ------------------------------------------------------------------ buffers past 4 GiB
+
+def test_receive_buffers_past_4gib(moe, orc):
+    """40,000 tokens x 7168 bf16, top-8 of 256 experts: the per-expert receive buffer holds
+    320,000 rows (4.6 GB, more than 2^31 elements), so every row offset must be 64-bit. The
+    layout equals the oracle's; every receive row equals its source row (per-expert through
+    the fused call, per-group through moe_dispatch); sampled FP8 receive rows equal the
+    oracle's quantisation of their source rows; and identity experts come back bit for bit
+    through combine (weights summing to 1). x is drawn on the GPU from a seeded generator."""
+    T, H, E, G, K = 40000, 7168, 256, 8, 8
+    d = si.make_inputs(T, 8, E, K, seed=99)            # routing and weights (x drawn below)
+    idx, w = d["topk_idx"], d["topk_w"]
+    gen = torch.Generator(device="cuda").manual_seed(99)
+    x = torch.randn((T, H), generator=gen, device="cuda").to(torch.bfloat16)
+    idx_d, w_d = to_dev(idx), to_dev(w)
+    Lo = orc.layout(idx, E, G)
+
+    L, D = moe.moe_layout_dispatch(idx_d, E, G, x, w_d, "expert")
+    check_layout(L, Lo)
+    R = Lo["R_expert"]
+    assert R == T * K and R * H > 2 ** 31
+    src_e = torch.from_numpy(Lo["recv_src_e"][:R].astype(np.int64)).cuda()
+    for a in range(0, R, 32768):
+        b = min(R, a + 32768)
+        tok = src_e[a:b] // K
+        assert torch.equal(D.recv_x[a:b].view(torch.int16), x[tok].view(torch.int16)), (a, b)
+        assert torch.equal(D.recv_topk_idx[a:b], idx_d[tok]), (a, b)
+    out = moe.moe_combine(L, D.recv_x, w_d, "expert")
+    assert torch.equal(out.view(torch.int16), x.view(torch.int16))
+    del D, out
+
+    Dg = moe.moe_dispatch(L, x, w_d, idx_d, "group")
+    P = Lo["R_group"]
+    src_g = torch.from_numpy(Lo["recv_src_g"][:P].astype(np.int64)).cuda()
+    for a in range(0, P, 32768):
+        b = min(P, a + 32768)
+        assert torch.equal(Dg.recv_x[a:b].view(torch.int16), x[src_g[a:b]].view(torch.int16)), (a, b)
+    del Dg
+
+    Df = moe.moe_dispatch(L, x, w_d, idx_d, "expert", "fp8")
+    rng = np.random.default_rng(99)
+    rows = np.concatenate([rng.choice(R, 60, replace=False), [0, R - 1]])
+    for r in rows:
+        t = int(Lo["recv_src_e"][r]) // K
+        xr = x[t].view(torch.int16).cpu().numpy().view(np.uint16)
+        q, s = orc.quantize_row_fp8(xr)
+        np.testing.assert_array_equal(Df.recv_x[int(r)].cpu().numpy(), q)
+        np.testing.assert_array_equal(Df.recv_scale[int(r)].cpu().numpy().view(np.uint32), s.view(np.uint32))
