@@ -917,8 +917,11 @@ def test_receive_buffers_past_4gib(moe, orc):
     320,000 rows (4.6 GB, more than 2^31 elements), so every row offset must be 64-bit. The
     layout equals the oracle's; every receive row equals its source row (per-expert through
     the fused call, per-group through moe_dispatch); sampled FP8 receive rows equal the
-    oracle's quantisation of their source rows; and identity experts come back bit for bit
-    through combine (weights summing to 1). x is drawn on the GPU from a seeded generator."""
+    oracle's quantisation of their source rows; identity experts come back bit for bit
+    through combine (weights summing to 1); sampled cast-transpose rows equal the oracle's
+    encoding and every expert's transposed block is the transpose of its rows; the regroup
+    of the per-group rows equals the per-expert dispatch. x is drawn on the GPU from a
+    seeded generator."""
     T, H, E, G, K = 40000, 7168, 256, 8, 8
     d = si.make_inputs(T, 8, E, K, seed=99)            # routing and weights (x drawn below)
     idx, w = d["topk_idx"], d["topk_w"]
@@ -939,15 +942,39 @@ def test_receive_buffers_past_4gib(moe, orc):
         assert torch.equal(D.recv_topk_idx[a:b], idx_d[tok]), (a, b)
     out = moe.moe_combine(L, D.recv_x, w_d, "expert")
     assert torch.equal(out.view(torch.int16), x.view(torch.int16))
-    del D, out
+    del out
 
+    # cast-transpose of the per-expert rows: sampled rows of C against the oracle's encoding
+    # of x * scale, and every expert's T_e against the transpose of its C rows
+    off = Lo["expert_offset"]
+    scale = np.random.default_rng(98).uniform(4.0, 400.0, E).astype(np.float32)
+    CT = moe.moe_cast_transpose_fp8(L, D.recv_x, to_dev(scale))
+    po = CT.pad_offset.cpu().numpy()
+    erows = np.random.default_rng(97).choice(R, 40, replace=False)
+    for r in erows:
+        e = int(np.searchsorted(off, r, side="right") - 1)
+        xr = D.recv_x[int(r)].float().cpu().numpy()
+        ref = orc.f32_to_e4m3_array((xr * scale[e]).astype(np.float32))
+        np.testing.assert_array_equal(CT.c[int(r)].cpu().numpy(), ref)
+    for e in range(E):
+        n, npad = int(off[e + 1] - off[e]), int(po[e + 1] - po[e])
+        assert npad == (n + 15) // 16 * 16
+        te = CT.t[H * int(po[e]):H * int(po[e + 1])].view(H, npad)
+        assert torch.equal(te[:, :n], CT.c[int(off[e]):int(off[e + 1])].t()), e
+        assert not bool(te[:, n:].any()), e
+    del CT
+
+    # per-group dispatch, and its regroup into per-expert rows (equal to the dispatch above)
     Dg = moe.moe_dispatch(L, x, w_d, idx_d, "group")
     P = Lo["R_group"]
     src_g = torch.from_numpy(Lo["recv_src_g"][:P].astype(np.int64)).cuda()
     for a in range(0, P, 32768):
         b = min(P, a + 32768)
         assert torch.equal(Dg.recv_x[a:b].view(torch.int16), x[src_g[a:b]].view(torch.int16)), (a, b)
-    del Dg
+    Dr = moe.moe_regroup(L, Dg)
+    assert torch.equal(Dr.recv_x[:R].view(torch.int16), D.recv_x[:R].view(torch.int16))
+    assert torch.equal(Dr.recv_topk_idx[:R], D.recv_topk_idx[:R])
+    del Dg, Dr, D
 
     Df = moe.moe_dispatch(L, x, w_d, idx_d, "expert", "fp8")
     rng = np.random.default_rng(99)
