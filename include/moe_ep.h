@@ -138,7 +138,9 @@ int64_t moe_recv_rows_bound(int T, int K, int G, int mode);
  * entries get slot -1, are not counted, and set status bits.
  * Requires 1 <= K <= MOE_MAX_TOPK, K <= E <= MOE_MAX_EXPERTS,
  * 1 <= G <= MOE_MAX_GROUPS, E % G == 0, T >= 0, T * max(K, G) < 2^30.
- * ws: device workspace of at least moe_layout_workspace_bytes() bytes.
+ * ws: device workspace of at least moe_layout_workspace_bytes() bytes (for
+ * K <= 8 and T * K <= 16384 the layout runs as one launch that does not touch
+ * it; it is required in every case).
  * stream: a hipStream_t (NULL = the null stream).
  * Source: mori pull request 586, Motivation and Technical Details 1; the
  * separate routing launch is the one its profiling section proposes. */
