@@ -13,6 +13,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 import torch
+from hypothesis import given, settings, strategies as st
 
 import synth_inputs as si
 
@@ -221,6 +222,29 @@ def test_layout_brute_force_with_invalid_entries(orc):
             assert L["recv_src_e"][r] == t * K + k
         for r, (_, t) in enumerate(gkeys):
             assert L["recv_src_g"][r] == t
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.data())
+def test_layout_brute_force_hypothesis(orc, data):
+    """Hypothesis-generated tiny shapes and index arrays (out-of-range, negative and
+    repeated entries included) against the Python brute force."""
+    G = data.draw(st.sampled_from([1, 2, 4]))
+    E = G * data.draw(st.integers(1, 3))
+    K = data.draw(st.integers(1, 4))
+    T = data.draw(st.integers(0, 7))
+    flat = data.draw(st.lists(st.integers(-2, E + 1), min_size=T * K, max_size=T * K))
+    idx = np.array(flat, np.int32).reshape(T, K)
+    L = orc.layout(idx, E, G)
+    status, keys, gkeys, slot_e, slot_tg, slot_g = _brute_layout(idx.tolist(), E, G)
+    assert L["status"] == status
+    assert L["R_expert"] == len(keys) and L["R_group"] == len(gkeys)
+    for (t, k), s in slot_e.items():
+        assert L["slot_e"][t * K + k] == s and L["slot_g"][t * K + k] == slot_g[(t, k)]
+    for (t, g), s in slot_tg.items():
+        assert L["slot_tg"][t * G + g] == s
+    assert [int(v) for v in L["recv_src_e"][:len(keys)]] == [t * K + k for _, t, k in keys]
+    assert [int(v) for v in L["recv_src_g"][:len(gkeys)]] == [t for _, t in gkeys]
 
 
 @pytest.mark.parametrize("name", ["tiny", "t256", "t4096", "skew"])
