@@ -996,3 +996,90 @@ def test_receive_buffers_past_4gib(moe, orc):
         q, s = orc.quantize_row_fp8(xr)
         np.testing.assert_array_equal(Df.recv_x[int(r)].cpu().numpy(), q)
         np.testing.assert_array_equal(Df.recv_scale[int(r)].cpu().numpy().view(np.uint32), s.view(np.uint32))
+
+
+# ------------------------------------------------------------------ guard bands
+
+GUARD_BYTES = 4096
+
+
+class Guarded:
+    """Views into allocations that carry a filled band of GUARD_BYTES on each side."""
+
+    def __init__(self):
+        self.bases = []
+
+    def __call__(self, shape, dtype, fill=0):
+        n = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+        base = torch.empty(n + 2 * GUARD_BYTES, dtype=torch.uint8, device="cuda")
+        base.fill_(0xC3)
+        view = base[GUARD_BYTES:GUARD_BYTES + n].view(dtype).view(shape)
+        view.view(torch.uint8).fill_(fill)
+        self.bases.append((base, n))
+        return view
+
+    def intact(self):
+        for base, n in self.bases:
+            if not (bool((base[:GUARD_BYTES] == 0xC3).all()) and bool((base[GUARD_BYTES + n:] == 0xC3).all())):
+                return False
+        return True
+
+
+@pytest.mark.parametrize("T,H,E,G,K", [(300, 1024, 32, 4, 4), (2100, 512, 64, 8, 8), (77, 2048, 8, 8, 2)])
+def test_guard_bands_untouched_by_every_call(moe, orc, T, H, E, G, K):
+    """Every array a call writes sits between two filled 4 KiB bands: layout (one launch
+    and count + place), dispatch bf16 / FP8 in both layouts, the fused call, combine,
+    regroup, cast-transpose and dequant leave the bands as they were; results still
+    match the oracle."""
+    g = Guarded()
+    d = si.make_inputs(T, H, E, K, seed=T + H)
+    idx, w, x = d["topk_idx"], d["topk_w"], d["x"]
+    idx_d, w_d, x_d = to_dev(idx), to_dev(w), dev_bf16(x)
+    Lo = orc.layout(idx, E, G)
+    L = moe.Layout.empty(T, K, E, G)
+    for name, n in (("expert_count", E), ("expert_offset", E + 1), ("group_count", G), ("group_offset", G + 1),
+                    ("tok_group_mask", T), ("slot_e", T * K), ("slot_g", T * K), ("slot_tg", T * G),
+                    ("recv_src_e", T * K), ("recv_src_g", T * min(K, G)), ("status", 1)):
+        setattr(L, name, g((n,), torch.int32))
+    L.workspace = g((L.workspace.numel(),), torch.uint8)
+    moe.moe_layout(idx_d, E, G, out=L)
+    check_layout(L, Lo)
+
+    def recv(mode, dtype):
+        cap = moe.recv_rows_bound(T, K, G, mode)
+        fp8 = dtype == "fp8"
+        return moe.Dispatched(g((cap, H), torch.uint8 if fp8 else torch.bfloat16),
+                              g((cap, H // 128), torch.float32) if fp8 else None,
+                              g((cap, K), torch.float32), g((cap, K), torch.int32))
+
+    Ds = {}
+    for mode in MODES:
+        for dtype in ("bf16", "fp8"):
+            if dtype == "fp8" and H % 128:
+                continue
+            Ds[mode, dtype] = moe.moe_dispatch(L, x_d, w_d, idx_d, mode, dtype, out=recv(mode, dtype))
+        out = g((T, H), torch.bfloat16)
+        moe.moe_combine(L, Ds[mode, "bf16"].recv_x, w_d, mode, out=out)
+        Do = orc.dispatch_bf16(Lo, mode, x, w, idx)
+        assert_combine_equal(host_u16(out), orc.combine(Lo, mode, Do["recv_x"], w))
+    Dr = moe.moe_regroup(L, Ds["group", "bf16"], out=recv("expert", "bf16"))
+    R = Lo["R_expert"]
+    assert torch.equal(Dr.recv_x[:R].view(torch.int16), Ds["expert", "bf16"].recv_x[:R].view(torch.int16))
+    if H % 128 == 0:
+        y = g((moe.recv_rows_bound(T, K, G, "expert"), H), torch.bfloat16)
+        moe.moe_fp8_dequant(L, Ds["expert", "fp8"].recv_x, Ds["expert", "fp8"].recv_scale, "expert", out=y)
+        nb = moe._lib.moe_cast_transpose_t_bytes(T, K, E, H)
+        CT = moe.CastTransposed(g((R, H), torch.uint8), g((max(nb, 16),), torch.uint8),
+                                g((E,), torch.float32), g((E + 1,), torch.int32))
+        moe.moe_cast_transpose_fp8(L, Ds["expert", "bf16"].recv_x, to_dev(np.full(E, 3.0, np.float32)), out=CT)
+        rows_e = orc.dispatch_bf16(Lo, "expert", x, w, idx)["recv_x"]
+        ref = orc.cast_transpose_fp8(Lo["expert_offset"], rows_e, np.full(E, 3.0, np.float32))
+        np.testing.assert_array_equal(CT.c.cpu().numpy(), ref["c"][:R])
+    L2 = moe.Layout.empty(T, K, E, G)
+    for name in ("slot_e", "slot_g", "slot_tg", "recv_src_e", "recv_src_g", "tok_group_mask"):
+        setattr(L2, name, g((getattr(L2, name).numel(),), torch.int32))
+    L2.workspace = g((L2.workspace.numel(),), torch.uint8)
+    moe.moe_layout_dispatch(idx_d, E, G, x_d, w_d, "expert", out_layout=L2, out=recv("expert", "bf16"))
+    check_layout(L2, Lo)
+    torch.cuda.synchronize()
+    assert g.intact()
