@@ -459,9 +459,28 @@ def extras(moe, d, dv, args):
                   "arch": getattr(props, "gcnArchName", None),
                   "compute_units": props.multi_processor_count,
                   "hbm_gib": round(props.total_memory / 2**30, 1),
+                  **device_clocks(),
                   "hip": torch.version.hip, "torch": torch.__version__,
                   "host_cores_available": len(os.sched_getaffinity(0))}
     return res
+
+
+def device_clocks():
+    """Peak engine and memory clocks (MHz) and memory bus width (bits) of device 0, from
+    the HIP runtime (hipDeviceGetAttribute; attribute numbers of hip_runtime_api.h:
+    ClockRate 5, MemoryClockRate 60, MemoryBusWidth 59); None where unavailable."""
+    import ctypes
+    out = {"engine_clock_mhz": None, "memory_clock_mhz": None, "memory_bus_bits": None}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return out
+    for key, attr, scale in (("engine_clock_mhz", 5, 1000), ("memory_clock_mhz", 60, 1000),
+                             ("memory_bus_bits", 59, 1)):
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0:
+            out[key] = v.value // scale
+    return out
 
 
 def workload_table(moe, names=("tiny", "t256", "t4096", "skew", "fp8"), it=30):
