@@ -25,6 +25,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -63,14 +64,25 @@ KERNEL_SOURCES = {
 }
 
 
+_COMMENT = re.compile(r"/\*.*?\*/|//[^\n]*", re.S)
+
+
+def code_text(src: str) -> str:
+    """The code of a C++ source with its comments and blank space removed, so that a
+    comment edit leaves a kernel's hash (and its recorded counters) valid. The kernel
+    sources hold no string literal containing comment markers."""
+    return " ".join(_COMMENT.sub(" ", src).split())
+
+
 def source_hash(kernel: str | None = None) -> str:
-    """Hash of the sources of one kernel (or of all kernel sources)."""
+    """Hash of the code (comments and spacing aside) of the sources of one kernel, or
+    of all kernel sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "combine_moe_layout_amd", "csrc")
     files = KERNEL_SOURCES[kernel] if kernel else sorted(os.listdir(csrc))
     for fn in files:
         h.update(fn.encode())
-        h.update(open(os.path.join(csrc, fn), "rb").read())
+        h.update(code_text(open(os.path.join(csrc, fn), encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

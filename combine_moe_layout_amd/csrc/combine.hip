@@ -12,14 +12,16 @@
 // Design. One workgroup per token; each lane owns ITER 16-byte vectors (8
 // elements each) of the output row per pass and keeps their fp32
 // accumulators in registers (ITER = 1 with the workgroup sized to the row
-// where it divides evenly into waves, which measured best). For a token whose K slots are all valid (the
-// normal case) the rows are read either row by row in contiguous bursts
-// (per-expert layout) or column by column with the next column prefetched
-// (per-group layout, where rows repeat), and folded with one fmaf per element
-// and k, in k order, starting from -0. Tokens with skipped entries take a
-// general loop with the same arithmetic. Nothing here is a dense
-// contraction (K <= 32 weights per row), so there is no MFMA: the kernel is
-// bound by the HBM reads of the expert rows.
+// where it divides evenly into waves, which measured best). For a token whose
+// K slots are all valid (the normal case) the rows are read either row by row
+// in contiguous bursts (per-expert layout) or column by column with the next
+// column prefetched (per-group layout, where rows repeat), and folded with one
+// fmaf per element and k, in k order, starting from -0. Tokens with skipped
+// entries take a general loop with the same arithmetic. The sums are rounded
+// to bf16 by the packed hardware conversion (round to nearest even; see
+// pack_bf16x2). Nothing here is a dense contraction (K <= 32 weights per
+// row), so there is no MFMA: the kernel is bound by the HBM reads of the
+// expert rows.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "moe_ep.h"

@@ -25,13 +25,14 @@
 // 4096 token workgroups of a large batch are mostly resident at once), else a
 // workgroup sized to the row with one chunk per lane per pass. The 8 lanes of
 // one 128-block (8 consecutive lanes in either form) reduce amax with three
-// xor-shuffles; every lane then
-// forms scale = amax / 448 and inv = 448 / amax (IEEE fp32 divisions, as
-// compiled by default), multiplies, saturates to +-448 (sat448: equal to
-// saturating round-to-nearest-even for every value; a NaN stays a NaN and
-// becomes the NaN code 0x7F) and converts pairs with the
-// packed e4m3 conversion, giving one 16-byte store per lane per destination.
-// The quantisation runs once per source token, not once per destination.
+// xor-shuffles (NaNs are passed over: see amax_step); every lane then forms
+// scale = amax / 448 and inv = 448 / amax (correctly rounded fp32 divisions:
+// the library is built with -fhip-fp32-correctly-rounded-divide-sqrt),
+// multiplies, saturates to +-448 (sat448: equal to saturating
+// round-to-nearest-even for every value; a NaN stays a NaN) and converts pairs
+// with the packed e4m3 conversion (its NaN byte mapped to the code 0x7F),
+// giving one 16-byte store per lane per destination. The quantisation runs
+// once per source token, not once per destination.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "place.hpp"
