@@ -13,3 +13,13 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_kernel_hash_ignores_comments_but_not_code():
+    sys.path.insert(0, ROOT)
+    import bench
+    a = "int f(int x)\n{\n    return x + 1;   // one more\n}\n/* note */\n"
+    b = "int f(int x) { /* the next integer */\n  return x + 1;\n}\n"
+    c = "int f(int x) { return x + 2; }\n"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(c)
