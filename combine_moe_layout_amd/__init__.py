@@ -102,7 +102,13 @@ def _check(rc: int, where: str) -> None:
 
 
 def _ptr(t: torch.Tensor | None):
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor for the C ABI. A host tensor is refused here: its
+    address given to a kernel would be a GPU memory fault, not an error code."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("arrays passed to the library must be GPU tensors (device memory)")
+    return t.data_ptr()
 
 
 def _stream(stream):
@@ -176,8 +182,7 @@ class Layout:
         must not be replaced after its first use)."""
         st = self.__dict__.get("_struct")
         if st is None:
-            st = _LayoutT(self.T, self.K, self.E, self.G,
-                          *(getattr(self, n).data_ptr() for n in self._FIELDS))
+            st = _LayoutT(self.T, self.K, self.E, self.G, *(_ptr(getattr(self, n)) for n in self._FIELDS))
             self.__dict__["_struct"] = st
             self.__dict__["_struct_ref"] = ctypes.byref(st)
         return st
