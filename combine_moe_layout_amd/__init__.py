@@ -258,9 +258,10 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
                         out_layout: Layout | None = None, out: Dispatched | None = None,
                         use_workspace: bool = True, stream=None) -> tuple[Layout, Dispatched]:
     """moe_layout + moe_dispatch as one call (moe_layout_dispatch): one launch for the
-    smallest batches, else the count kernel, an offsets workgroup and a dispatch that
-    places its own tokens. use_workspace=False passes no workspace, which asks for the
-    one-launch form (T <= 512 and T * K <= 16384)."""
+    smallest batches, the one-launch layout and a dispatch up to T * K = 8192, else the
+    count kernel, an offsets workgroup and a dispatch that places its own tokens.
+    use_workspace=False passes no workspace, which asks for the one-launch form
+    (T <= 512 and T * K <= 16384)."""
     if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or not topk_idx.is_contiguous():
         raise ValueError("topk_idx must be a contiguous int32 [T, K] tensor")
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():

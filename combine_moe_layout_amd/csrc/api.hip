@@ -177,7 +177,10 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
     // the 128-thread bf16 and one-wave FP8 workgroups, several for the
     // row-sized FP8 ones (H > 8192), where it measured slower than the two
     // calls. Otherwise: the two calls.
-    if (L->K > 8 || (fp8 && !moe::fp8_wave_form(H))) {
+    const int64_t pairs = (int64_t)L->T * L->K;
+    const bool via_onepass = L->K <= 8 && pairs <= moe::tuning().fused_onepass_max_pairs &&
+                             pairs <= moe::tuning().layout_onepass_max_pairs;
+    if (L->K > 8 || (fp8 && !moe::fp8_wave_form(H)) || via_onepass) {
         e = moe::launch_layout(topk_idx, L->T, L->K, L->E, L->G, P, static_cast<int32_t *>(ws),
                                (hipStream_t)stream);
         if (e == hipSuccess)

@@ -331,6 +331,7 @@ const Tuning &tuning()
         env("MOE_EP_DISPATCH_NT_STORE", r.dispatch_nt_store);
         if (const char *f = getenv("MOE_EP_FP8_FORM")) r.fp8_form = atoi(f);
         if (const char *f = getenv("MOE_EP_LAYOUT_ONEPASS_MAX_PAIRS")) r.layout_onepass_max_pairs = atoi(f);
+        if (const char *f = getenv("MOE_EP_FUSED_ONEPASS_MAX_PAIRS")) r.fused_onepass_max_pairs = atoi(f);
         return r;
     }();
     return t;

@@ -87,7 +87,7 @@ inline uint32_t group_magic(int E, int G)
 // Cache policy of the dispatch row loads and stores, the FP8 dispatch's form
 // and the largest batch of the one-launch layout. Defaults are the measured
 // best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2
-// and MOE_EP_LAYOUT_ONEPASS_MAX_PAIRS=<T*K> in the environment override them
+// and MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K> in the environment override them
 // (read once per process) for A/B runs.
 struct Tuning {
     bool dispatch_nt_load = true;    // x rows are read once
@@ -95,6 +95,7 @@ struct Tuning {
     int fp8_form = 1;                // FP8 dispatch: 0 row-sized workgroups, 1 one wave
                                      // per token, 2 two waves per token (H <= 16 * BS * 8)
     int layout_onepass_max_pairs = 16384;   // moe_layout in one launch up to T * K pairs (top-k <= 8)
+    int fused_onepass_max_pairs = 8192;     // moe_layout_dispatch as that layout + a plain dispatch
 };
 const Tuning &tuning();
 // Whether the FP8 dispatch of rows of H elements runs in a small-workgroup form.

@@ -177,12 +177,15 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
  * T <= MOE_FUSED_MAX_TOKENS and T * K <= MOE_FUSED_MAX_PAIRS when ws is NULL,
  * take one launch and need no workspace: one workgroup per token recomputes
  * the routing it needs from the whole index array, a cost that grows with
- * T * K and E. Other batches need ws (moe_layout_workspace_bytes()):
- * for BF16 with K <= 8 the layout's count kernel and one workgroup that
- * computes the offsets run first, and each dispatch workgroup then computes
- * its own token's slots from the per-tile token masks while its row loads are
- * in flight, so the separate placement launch of moe_layout() disappears;
- * otherwise (FP8, or K > 8) the call runs moe_layout() and moe_dispatch().
+ * T * K and E. Other batches need ws (moe_layout_workspace_bytes()). With
+ * K <= 8 and T * K <= 8192 the call runs moe_layout() (one launch at these
+ * sizes) and the dispatch. Larger batches with K <= 8 (BF16, or FP8 with
+ * H <= 8192) run the layout's count kernel and one workgroup that computes
+ * the offsets first, and each dispatch workgroup then computes its own
+ * token's slots from the per-tile token masks while its row loads are in
+ * flight, so the separate placement launch of moe_layout() disappears;
+ * otherwise (K > 8, or FP8 with H > 8192) the call runs moe_layout() and
+ * moe_dispatch().
  * Source: mori pull request 586, the IntraNodeLL reply in its review thread
  * (single-pass per-token routing, one block per token, copy fused in; latency
  * dominates at small token counts) and its profiling section (routing
