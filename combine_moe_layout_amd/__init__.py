@@ -111,9 +111,19 @@ def _ptr(t: torch.Tensor | None):
     return t.data_ptr()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None)
+
+
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    """hipStream_t of `stream`, or of torch's current stream on the current device.
+    torch's raw-handle getter avoids building a Stream object per call (about 2.8 us
+    of host time per call on MI355X hosts); the public API is the fallback."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None and _cur_device is not None:
+        return _raw_stream(_cur_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _mode(mode) -> int:

@@ -1087,3 +1087,13 @@ def test_guard_bands_untouched_by_every_call(moe, orc, T, H, E, G, K):
     check_layout(L2, Lo)
     torch.cuda.synchronize()
     assert g.intact()
+
+
+def test_binding_stream_is_torchs_current_stream(moe):
+    """The binding's stream handle is torch's current stream, default and inside a
+    side-stream context."""
+    assert moe._stream(None) == torch.cuda.current_stream().cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert moe._stream(None) == s.cuda_stream == torch.cuda.current_stream().cuda_stream
+    assert moe._stream(s) == s.cuda_stream
