@@ -377,7 +377,8 @@ def extras(moe, d, dv, args):
         "dispatch_gbs": round(bd3 / m3[1] / 1e3, 1), "combine_gbs": round(bc3 / m3[2] / 1e3, 1),
         "dispatch_frac": round(bd3 / m3[1] / 1e3 / PEAK_HBM_GBS, 4),
         "combine_frac": round(bc3 / m3[2] / 1e3 / PEAK_HBM_GBS, 4),
-        "dispatch_payload_gbs": round(R * H * 2 / m3[1] / 1e3, 1)}
+        "dispatch_payload_gbs": round(R * H * 2 / m3[1] / 1e3, 1),
+        "combine_payload_gbs": round(R * H * 2 / m3[2] / 1e3, 1)}
     Dg = moe.alloc_dispatch(L, H, "group")
     disp_g = lambda: moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "group", "bf16", out=Dg)
     comb_g = lambda: moe.moe_combine(L, Dg.recv_x, dv.w, "group", out=dv.out)
@@ -532,7 +533,8 @@ def workload_table(moe, names=("tiny", "t256", "t4096", "skew", "fp8"), it=30):
                          "dispatch_gbs": round(bd / md / 1e3, 1), "combine_gbs": round(bc / mc / 1e3, 1),
                          "dispatch_frac": round(bd / md / 1e3 / PEAK_HBM_GBS, 4),
                          "combine_frac": round(bc / mc / 1e3 / PEAK_HBM_GBS, 4),
-                         "dispatch_payload_gbs": round(nrows * H * (1 if wl.fp8 else 2) / md / 1e3, 1)}
+                         "dispatch_payload_gbs": round(nrows * H * (1 if wl.fp8 else 2) / md / 1e3, 1),
+                         "combine_payload_gbs": round(nrows * H * 2 / mc / 1e3, 1)}
         # receive-side regroup: the per-group arrays -> the per-expert layout
         Dg, De = dv.D["group"], dv.D["expert"]
         moe.moe_dispatch(L, dv.x, dv.w, dv.idx, "group", dt, out=Dg)
