@@ -29,7 +29,7 @@ __all__ = [
     "moe_layout_dispatch", "moe_regroup", "moe_cast_transpose_fp8", "CastTransposed",
     "moe_fp8_dequant", "moe_ref_copy", "recv_rows_bound", "layout_workspace_bytes",
     "library_path", "MODE_EXPERT", "MODE_GROUP", "DTYPE_BF16", "DTYPE_FP8",
-    "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS",
+    "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS", "STATUS_SYNC_TIMEOUT",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +38,7 @@ _LIB_PATH = os.environ.get("MOE_EP_LIB") or os.path.join(_PKG, "libmoe_ep.so")
 
 MODE_EXPERT, MODE_GROUP = 0, 1
 DTYPE_BF16, DTYPE_FP8 = 0, 1
-STATUS_BAD_INDEX, STATUS_DUPLICATE, STATUS_Y_ROWS = 1, 2, 4
+STATUS_BAD_INDEX, STATUS_DUPLICATE, STATUS_Y_ROWS, STATUS_SYNC_TIMEOUT = 1, 2, 4, 8
 _MODES = {"expert": MODE_EXPERT, "group": MODE_GROUP, MODE_EXPERT: MODE_EXPERT, MODE_GROUP: MODE_GROUP}
 _DTYPES = {"bf16": DTYPE_BF16, "fp8": DTYPE_FP8, DTYPE_BF16: DTYPE_BF16, DTYPE_FP8: DTYPE_FP8}
 

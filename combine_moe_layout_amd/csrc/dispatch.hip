@@ -75,6 +75,9 @@ __global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_kernel(
             if (FULL || j < nvec) v[i] = load16<NTL>(src + j);
         }
     };
+    if constexpr (PLACE) {
+        if (P.finalize && t == 0) finalize_role(P);
+    }
     load_pass(0);
     if constexpr (PLACE) place_token(P, t, K, s_dst);
     for (int base = 0; base < nvec; base += kDispatchBS * ITER) {
@@ -167,6 +170,9 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
 
     // The first pass is loaded and quantised before the token is placed
     // (PLACE), so the placement overlaps it.
+    if constexpr (PLACE) {
+        if (P.finalize && t == 0) finalize_role(P);
+    }
     u32x4 q0;
     float scale0;
     {
@@ -232,6 +238,9 @@ __global__ __launch_bounds__(BS) void dispatch_fp8_wave_kernel(
     const int nblk = nch / 8;
     const int64_t rows = (int64_t)gridDim.x * (K < nslot ? K : nslot);   // as in the bf16 kernel
 
+    if constexpr (PLACE) {
+        if (P.finalize && t == 0) finalize_role(P);
+    }
     u32x4 q[ITER];
     float sc[ITER];
     {
@@ -332,6 +341,8 @@ const Tuning &tuning()
         if (const char *f = getenv("MOE_EP_FP8_FORM")) r.fp8_form = atoi(f);
         if (const char *f = getenv("MOE_EP_LAYOUT_ONEPASS_MAX_PAIRS")) r.layout_onepass_max_pairs = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_ONEPASS_MAX_PAIRS")) r.fused_onepass_max_pairs = atoi(f);
+        if (const char *f = getenv("MOE_EP_FUSED_FINALIZE")) r.fused_finalize = atoi(f);
+        if (const char *f = getenv("MOE_EP_FUSED_FINALIZE_ROUNDS")) r.fused_finalize_rounds = atoi(f);
         return r;
     }();
     return t;
@@ -402,6 +413,8 @@ int fp8_small_bs(int H)
 }  // namespace
 
 bool fp8_wave_form(int H) { return fp8_small_bs(H) != 0; }
+
+int placing_dispatch_threads(bool fp8, int H) { return fp8 ? fp8_small_bs(H) : kDispatchBS; }
 
 hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
                                const float *topk_w, const int32_t *topk_idx, void *recv_q,

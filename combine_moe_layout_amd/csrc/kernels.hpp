@@ -61,11 +61,17 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
                          int32_t *ws, hipStream_t stream);
 
 // First half of the fused layout + dispatch for T > the small-batch limit
-// and top-k <= 8: the count kernel, then one workgroup that writes the
-// counts, offsets and status and each tile's bases into the workspace. The
-// dispatch kernels then place each token themselves (PlaceArgs).
+// and top-k <= 8: the count kernel, which also sets every tile's bases in
+// the workspace to -1 and the status to 0; then, unless `finalize_in_dispatch`,
+// one workgroup that writes the counts, offsets and status and each tile's
+// bases. The dispatch kernels then place each token themselves (PlaceArgs);
+// with `finalize_in_dispatch` their workgroup 0 computes the bases first.
 hipError_t launch_layout_count_finalize(const int32_t *idx, int T, int K, int E, int G,
-                                        const LayoutPtrs &L, int32_t *ws, hipStream_t stream);
+                                        const LayoutPtrs &L, int32_t *ws, bool finalize_in_dispatch,
+                                        hipStream_t stream);
+
+// Tiles per batch of the count-table loads of an in-dispatch finalize.
+constexpr int kFinTiles = 16;
 
 // What a dispatch kernel needs to compute its token's slots and write the
 // token's layout entries (see place_token in place.hpp).
@@ -74,7 +80,10 @@ struct PlaceArgs {
     int E, G;
     uint32_t gmagic;
     const uint32_t *words, *gwords;
-    const int32_t *bases;
+    int32_t *bases;            // [tiles][E + G]; -1 until written
+    const int32_t *table;      // the count kernel's per-tile counts and error bits
+    int ntiles;
+    int finalize;              // 1: workgroup 0 computes the bases, counts, offsets and status
     LayoutPtrs L;
     int mode;   // destinations: slot_e (0) or slot_tg (1)
 };
@@ -86,9 +95,10 @@ inline uint32_t group_magic(int E, int G)
 
 // Cache policy of the dispatch row loads and stores, the FP8 dispatch's form
 // and the largest batch of the one-launch layout. Defaults are the measured
-// best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2
-// and MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K> in the environment override them
-// (read once per process) for A/B runs.
+// best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2,
+// MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>, MOE_EP_FUSED_FINALIZE=0/1/2 and
+// MOE_EP_FUSED_FINALIZE_ROUNDS=<n> in the environment override them (read once
+// per process) for A/B runs.
 struct Tuning {
     bool dispatch_nt_load = true;    // x rows are read once
     bool dispatch_nt_store = false;  // receive rows
@@ -96,10 +106,15 @@ struct Tuning {
                                      // per token, 2 two waves per token (H <= 16 * BS * 8)
     int layout_onepass_max_pairs = 16384;   // moe_layout in one launch up to T * K pairs (top-k <= 8)
     int fused_onepass_max_pairs = 8192;     // moe_layout_dispatch as that layout + a plain dispatch
+    int fused_finalize = 2;                 // placing dispatch: 0 the finalize kernel, 1 its
+                                            // workgroup 0 (bf16), 2 workgroup 0 (bf16 and FP8)
+    int fused_finalize_rounds = 4;          // ... for E up to this many columns per thread
 };
 const Tuning &tuning();
 // Whether the FP8 dispatch of rows of H elements runs in a small-workgroup form.
 bool fp8_wave_form(int H);
+// Threads per workgroup of the placing dispatch (FP8: of its small-workgroup form).
+int placing_dispatch_threads(bool fp8, int H);
 
 // BF16 dispatch. slots: [T, nslot] (slot_e with nslot = K, or slot_tg with nslot = G).
 // place: NULL to read the destinations from `slots`, else the token's slots

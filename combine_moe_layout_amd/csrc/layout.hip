@@ -166,7 +166,7 @@ template <int KMAX, bool EXACT>
 __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic,
     uint32_t *__restrict__ tok_group_mask, int32_t *__restrict__ table, uint32_t *__restrict__ words,
-    uint32_t *__restrict__ gwords)
+    uint32_t *__restrict__ gwords, int32_t *__restrict__ clear_bases, int32_t *__restrict__ clear_status)
 {
     extern __shared__ unsigned long long emask[];   // [E][kWaves]
     __shared__ int gcnt[kMaxG][kWaves];
@@ -204,6 +204,10 @@ __global__ __launch_bounds__(kLayoutTile) void layout_count_kernel(
     }
     if (tid < G) row[E + tid] = gcnt[tid][0] + gcnt[tid][1] + gcnt[tid][2] + gcnt[tid][3];
     if (tid == 0) row[E + G] = s_err;
+    if (clear_bases) {   // fused path: the tile's bases are not yet known
+        for (int x = tid; x < E + G; x += kLayoutTile) clear_bases[(size_t)tile * (E + G) + x] = -1;
+        if (tile == 0 && tid == 0) *clear_status = 0;
+    }
     if constexpr (KMAX <= 8) {
         uint32_t *wt = words + (size_t)tile * E * kWaves * 2;
         for (int i = tid; i < E * kWaves; i += kLayoutTile) {
@@ -948,7 +952,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_empty_kernel(int E, int G,
 namespace {
 
 using CountFn = void (*)(const int32_t *, int, int, int, int, uint32_t, uint32_t *, int32_t *, uint32_t *,
-                         uint32_t *);
+                         uint32_t *, int32_t *, int32_t *);
 using PlaceFn = void (*)(const int32_t *, int, int, int, int, uint32_t, int, const int32_t *,
                          const uint32_t *, LayoutPtrs, int);
 using OnepassFn = void (*)(const int32_t *, int, int, int, int, uint32_t, LayoutPtrs, int);
@@ -1002,7 +1006,7 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
     PlaceFn place;
     pick_layout(K, E, count, place);
     hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G, gmagic,
-                       L.tok_group_mask, w.table, w.words, w.gwords);
+                       L.tok_group_mask, w.table, w.words, w.gwords, nullptr, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(place, dim3(ntiles), dim3(kLayoutTile), lds2, stream, idx, T, K, E, G, gmagic,
@@ -1011,7 +1015,8 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
 }
 
 hipError_t launch_layout_count_finalize(const int32_t *idx, int T, int K, int E, int G,
-                                        const LayoutPtrs &L, int32_t *ws, hipStream_t stream)
+                                        const LayoutPtrs &L, int32_t *ws, bool finalize_in_dispatch,
+                                        hipStream_t stream)
 {
     const int ntiles = layout_tiles(T);
     const LayoutWs w = layout_ws(ws, T, E, G);
@@ -1020,9 +1025,9 @@ hipError_t launch_layout_count_finalize(const int32_t *idx, int T, int K, int E,
     pick_layout(K, E, count, place);
     const size_t lds1 = (size_t)E * kWaves * sizeof(unsigned long long);
     hipLaunchKernelGGL(count, dim3(ntiles), dim3(kLayoutTile), lds1, stream, idx, T, K, E, G,
-                       group_magic(E, G), L.tok_group_mask, w.table, w.words, w.gwords);
+                       group_magic(E, G), L.tok_group_mask, w.table, w.words, w.gwords, w.bases, L.status);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || finalize_in_dispatch) return e;
     hipLaunchKernelGGL(layout_finalize_kernel, dim3(1), dim3(kFinBS), 0, stream, ntiles, E, G, w.table,
                        w.bases, L);
     return hipGetLastError();

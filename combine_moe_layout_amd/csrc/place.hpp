@@ -1,6 +1,6 @@
 // Placement of one token inside a dispatch kernel (the fused layout +
 // dispatch for large batches): the token's receive slots from the count
-// kernel's per-tile token masks and the finalize kernel's per-tile bases.
+// kernel's per-tile token masks and the per-tile bases.
 //
 // For expert x of token t (tile b = t / 256, wave w and lane l of t in b):
 //   slot = bases[b][x] + popcount of x's words of waves before w
@@ -11,7 +11,20 @@
 // lane g group g), writes the token's layout entries, and leaves the rows to
 // copy to (slot_e for the per-expert layout, slot_tg for the per-group one)
 // in dst[]; the call ends with a workgroup barrier.
+//
+// The bases come either from the finalize kernel, launched before, or from
+// workgroup 0 of the dispatch itself (finalize_role), which computes them
+// while the other workgroups load their rows. The count kernel sets every
+// base to -1 first (a valid base is >= 0), so a token's wave polls exactly the
+// base words it needs until they are valid: agent-scope atomic stores and
+// loads of those words, no flag and no state that outlives the call. Workgroup
+// 0 waits for nothing, and is the first workgroup dispatched; a wait is still
+// bounded (0.2 s by the constant clock, against the few µs it takes), after
+// which the token is skipped and MOE_STATUS_SYNC_TIMEOUT is set, so no wave
+// can wait forever.
 #pragma once
+
+#include "moe_ep.h"
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -37,6 +50,137 @@ __device__ __forceinline__ int place_rank(const uint32_t *__restrict__ q, int w,
     return r;
 }
 
+constexpr uint64_t kBaseWaitTicks = 20000000;   // 0.2 s of the constant 100 MHz clock
+constexpr int kFinBatch = kFinTiles;
+
+__device__ __forceinline__ int base_load(int32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The count table as a buffer resource: loads past its nt rows return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fin_table_rsrc(const int32_t *tab, int nt, int rows)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(tab), (short)0, nt * rows * 4, 0x00020000);
+}
+
+// Column `col` of the count table over the (at most kFinBatch) tiles: the
+// counts in v (0 past the last tile) and their total. One buffer load per
+// tile, all in flight together, from one running offset.
+__device__ __forceinline__ int fin_column_sum(__amdgpu_buffer_rsrc_t tab, int rows, int col,
+                                              int (&v)[kFinBatch])
+{
+    int off = col * 4;
+#pragma unroll
+    for (int u = 0; u < kFinBatch; ++u) {
+        v[u] = __builtin_amdgcn_raw_buffer_load_b32(tab, off, 0, 0);
+        off += rows * 4;
+    }
+    int s = 0;
+#pragma unroll
+    for (int u = 0; u < kFinBatch; ++u) s += v[u];
+    return s;
+}
+
+// Bases of column `col` in the nt tiles: the column's offset plus the counts
+// of the tiles before. `bases` is a buffer resource over the nt rows, so the
+// stores of rows past the last tile are dropped by the hardware; the stores
+// carry sc1, the agent-scope coherent form (what an agent-scope atomic store
+// compiles to), so the polling loads of other workgroups see them.
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ void fin_column_bases(int col, const int (&v)[kFinBatch], int offset,
+                                                 __amdgpu_buffer_rsrc_t bases, int cols)
+{
+    int r = offset, off = col * 4;
+#pragma unroll
+    for (int u = 0; u < kFinBatch; ++u) {
+        __builtin_amdgcn_raw_buffer_store_b32(r, bases, off, 0, kCpolSc1);
+        r += v[u];
+        off += cols * 4;
+    }
+}
+
+// Exclusive prefix sum over the workgroup (at most 16 waves); `total` gets
+// the sum of all. Ends with a barrier, so s_tot can be reused.
+__device__ __forceinline__ int fin_block_scan(int v, int *s_tot, int &total)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) s_tot[wave] = x;
+    __syncthreads();
+    int base = 0, all = 0;
+    for (int w = 0; w < nw; ++w) {
+        const int c = s_tot[w];
+        base += w < wave ? c : 0;
+        all += c;
+    }
+    __syncthreads();
+    total = all;
+    return base + x - v;
+}
+
+// Workgroup 0 of a placing dispatch (P.finalize; at most kFinBatch tiles):
+// what the finalize kernel computes, with the workgroup's threads (a whole
+// number of waves) taking the expert columns in rounds. A column's total over
+// the tiles is an expert's (group's) count, the exclusive prefix of the
+// totals its offset, and a tile's base in the column the offset plus the
+// counts of the tiles before it. The status was set to 0 by the count kernel;
+// the tiles' error bits are ORed into it.
+__device__ void finalize_role(const PlaceArgs &P)
+{
+    __shared__ int s_tot[16];
+    const int tid = threadIdx.x, lane = tid % kWave, nth = blockDim.x;
+    const int E = P.E, G = P.G, nt = P.ntiles, rows = E + G + 1, cols = E + G;
+    const __amdgpu_buffer_rsrc_t tab = fin_table_rsrc(P.table, nt, rows);
+    const __amdgpu_buffer_rsrc_t bases = __builtin_amdgcn_make_buffer_rsrc(P.bases, (short)0, nt * cols * 4, 0x00020000);
+    int carry = 0;
+    for (int c0 = 0; c0 < E; c0 += nth) {
+        const int e = c0 + tid;
+        const bool live = e < E;
+        int v[kFinBatch];
+        int tot = fin_column_sum(tab, rows, live ? e : E - 1, v);
+        tot = live ? tot : 0;
+        int all;
+        const int off = carry + fin_block_scan(tot, s_tot, all);
+        carry += all;
+        if (live) {
+            P.L.expert_count[e] = tot;
+            P.L.expert_offset[e] = off;
+            fin_column_bases(e, v, off, bases, cols);
+        }
+    }
+    if (tid == 0) P.L.expert_offset[E] = carry;
+    if (tid < kWave) {   // groups (G <= 32) and the error bits (column E + G): wave 0
+        const bool live = lane < G;
+        int v[kFinBatch];
+        int tot = fin_column_sum(tab, rows, live ? E + lane : E + G, v);
+        int incl = live ? tot : 0;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (live) {
+            const int goff = incl - tot;
+            P.L.group_count[lane] = tot;
+            P.L.group_offset[lane] = goff;
+            fin_column_bases(E + lane, v, goff, bases, cols);
+        }
+        if (lane == G - 1) P.L.group_offset[G] = incl;
+        if (lane == G) {   // G <= 32 < 64: this lane summed the error column; OR it instead
+            int er = 0;
+#pragma unroll
+            for (int u = 0; u < kFinBatch; ++u) er |= v[u];
+            if (er) atomicOr(P.L.status, er);
+        }
+    }
+}
+
 __device__ __forceinline__ void place_token(const PlaceArgs &P, int t, int K, int32_t *dst)
 {
     if (threadIdx.x < kWave) {
@@ -53,16 +197,31 @@ __device__ __forceinline__ void place_token(const PlaceArgs &P, int t, int K, in
         }
         const bool valid = mine && (unsigned)e < (unsigned)E && !rep;
         const int g = valid ? place_group_of(e, P.gmagic) : 0;
-        const int32_t *tb = P.bases + (size_t)tile * (E + G);
-        int se = -1;
-        if (valid) se = tb[e] + place_rank(P.words + ((size_t)tile * E + e) * 8, w, l);
         // the groups the token reaches, on every lane
         uint32_t gm = valid ? 1u << g : 0u;
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) gm |= __shfl_xor(gm, o);
-        int sgl = -1;   // lane g < G: the token's row in group g, or -1
-        if (lane < G && ((gm >> lane) & 1u))
-            sgl = tb[E + lane] + place_rank(P.gwords + ((size_t)tile * G + lane) * 8, w, l);
+        const bool hg = lane < G && ((gm >> lane) & 1u);
+        // ranks from the count kernel's words, then the tile's bases
+        const int re = valid ? place_rank(P.words + ((size_t)tile * E + e) * 8, w, l) : 0;
+        const int rg = hg ? place_rank(P.gwords + ((size_t)tile * G + lane) * 8, w, l) : 0;
+        int32_t *tb = P.bases + (size_t)tile * (E + G);
+        int be = 0, bg = 0;
+        bool ok = true;
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+            if (valid) be = base_load(tb + e);
+            if (hg) bg = base_load(tb + E + lane);
+            if (__all(be >= 0 && bg >= 0)) break;
+            if (wall_clock64() - t0 > kBaseWaitTicks) {
+                ok = false;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (!ok && lane == 0) atomicOr(P.L.status, MOE_STATUS_SYNC_TIMEOUT);
+        const int se = valid && ok ? be + re : -1;
+        const int sgl = hg && ok ? bg + rg : -1;   // lane g < G: the token's row in group g, or -1
         const int sg = __shfl(sgl, g);
         // (the receive lists hold T*K and T*min(K, G) entries; T = the grid)
         const int64_t T = gridDim.x;

@@ -55,6 +55,8 @@ enum moe_error {
 #define MOE_STATUS_BAD_INDEX 1 /* some topk_idx entry outside [0, E) */
 #define MOE_STATUS_DUPLICATE 2 /* some token lists one expert twice */
 #define MOE_STATUS_Y_ROWS 4    /* combine met a slot >= the rows of y */
+#define MOE_STATUS_SYNC_TIMEOUT 8 /* moe_layout_dispatch: a token's workgroup gave up waiting
+                                     (0.2 s) for its tile's bases and skipped the token */
 
 /* Receive-buffer layouts.
  * EXPERT: one row per valid (token, k) pair, rows ordered by expert, then
@@ -180,12 +182,16 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
  * T * K and E. Other batches need ws (moe_layout_workspace_bytes()). With
  * K <= 8 and T * K <= 8192 the call runs moe_layout() (one launch at these
  * sizes) and the dispatch. Larger batches with K <= 8 (BF16, or FP8 with
- * H <= 8192) run the layout's count kernel and one workgroup that computes
- * the offsets first, and each dispatch workgroup then computes its own
- * token's slots from the per-tile token masks while its row loads are in
- * flight, so the separate placement launch of moe_layout() disappears;
- * otherwise (K > 8, or FP8 with H > 8192) the call runs moe_layout() and
- * moe_dispatch().
+ * H <= 8192) run the layout's count kernel and then a dispatch in which each
+ * workgroup computes its own token's slots from the per-tile token masks
+ * while its row loads are in flight, so the separate placement launch of
+ * moe_layout() disappears. The offsets and per-tile bases come from
+ * workgroup 0 of that dispatch (T <= 4096 and at most four experts per
+ * dispatch thread: E <= 512 for BF16, E <= 256 for FP8), which the other
+ * workgroups wait for within a bounded time (MOE_STATUS_SYNC_TIMEOUT), or
+ * else from one workgroup launched in between. Otherwise (K > 8, or FP8 with
+ * H > 8192) the call runs moe_layout() and moe_dispatch(). The workspace
+ * holds no state from one call to the next.
  * Source: mori pull request 586, the IntraNodeLL reply in its review thread
  * (single-pass per-token routing, one block per token, copy fused in; latency
  * dominates at small token counts) and its profiling section (routing

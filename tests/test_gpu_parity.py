@@ -144,6 +144,28 @@ def test_layout_reuses_buffers_without_stale_state(moe, orc, T):
     check_layout(L, orc.layout(a, 256, 8))                           # status cleared again
 
 
+@pytest.mark.parametrize("T", [1500, 4096, 4097])   # offsets in the dispatch (two sizes); finalize kernel
+def test_fused_call_reuses_buffers_without_stale_state(moe, orc, T):
+    """moe_layout_dispatch into a layout, workspace and receive buffers that hold an
+    earlier, different call's results equals a fresh call: the per-tile bases and the
+    status of the earlier call must not leak into the next."""
+    E, G, K, H = 256, 8, 8, 256
+    a = si.make_inputs(T, H, E, K, seed=43)
+    b = si.make_inputs(T, H, E, K, seed=44)
+    b["topk_idx"][:5, 2] = -3                                         # invalid entries in b
+    L = moe.Layout.empty(T, K, E, G)
+    D = moe.alloc_dispatch(L, H, "expert", "bf16")
+    for d in (a, b, a):
+        x = dev_bf16(d["x"])
+        L, D = moe.moe_layout_dispatch(to_dev(d["topk_idx"]), E, G, x, to_dev(d["topk_w"]), "expert",
+                                       out_layout=L, out=D)
+        Lo = orc.layout(d["topk_idx"], E, G)
+        check_layout(L, Lo)
+        R = Lo["R_expert"]
+        src = Lo["recv_src_e"][:R] // K
+        assert torch.equal(D.recv_x[:R].view(torch.int16).cpu(), x.view(torch.int16).cpu()[torch.from_numpy(src).long()])
+
+
 @pytest.mark.parametrize("T,K,E,G", [(700, 8, 256, 8), (300, 4, 64, 4), (513, 2, 16, 8)])
 def test_layout_slot_arrays_4_byte_aligned(moe, orc, T, K, E, G):
     """Slot arrays that are 4-byte but not 16-byte aligned (allowed by the ABI) take
@@ -468,6 +490,8 @@ FUSED_SHAPES = [
     (600, 256, 64, 8, 13), (4097, 2048, 256, 8, 8), (3000, 128, 1024, 32, 8), (1030, 512, 64, 8, 8),
     (600, 8320, 32, 8, 8),    # rows over 8192 through the one-launch layout
     (1100, 8320, 32, 8, 8),   # rows over 8192: multi-pass placing bf16 dispatch; FP8 takes the two calls
+    (2000, 1024, 200, 8, 8),  # offsets computed in the dispatch: a partial second round of columns
+    (1500, 256, 256, 32, 8),  # ... with 32 groups
 ]
 
 
