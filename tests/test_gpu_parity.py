@@ -104,6 +104,8 @@ EDGE_SHAPES = [
     (2048, 8, 256, 8), (2049, 8, 256, 8), (4096, 4, 64, 8), (8192, 2, 8, 8), (5000, 3, 1024, 32),
     # every token takes every expert (K = E), with G = E, G = 1 and between; above the limit too
     (300, 32, 32, 32), (200, 8, 8, 1), (700, 16, 16, 4), (2500, 8, 8, 8),
+    # count + place: ragged tile, K not 2/4/8, G = 32, exactly 16 tiles
+    (3000, 7, 200, 8), (2300, 8, 256, 32), (4096, 8, 256, 8),
 ]
 
 
