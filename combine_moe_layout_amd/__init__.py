@@ -126,6 +126,22 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _need(t: torch.Tensor | None, dtype: torch.dtype, shape: tuple, name: str) -> None:
+    """Refuse an array the library would read or write out of bounds: the C ABI gets
+    only pointers and row counts, so a wrong dtype, shape or stride here would be a
+    GPU memory fault there, not an error code."""
+    if t is not None and t.dtype is dtype and t.shape == shape and t.is_contiguous():
+        return
+    got = "None" if t is None else f"{t.dtype} {tuple(t.shape)}" + ("" if t.is_contiguous() else " (strided)")
+    raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}; got {got}")
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    if t is None or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    return t.shape[0]
+
+
 def _mode(mode) -> int:
     if mode not in _MODES:
         raise MoeError(-7, f"mode {mode!r}")
@@ -192,10 +208,22 @@ class Layout:
         must not be replaced after its first use)."""
         st = self.__dict__.get("_struct")
         if st is None:
+            self._validate()
             st = _LayoutT(self.T, self.K, self.E, self.G, *(_ptr(getattr(self, n)) for n in self._FIELDS))
             self.__dict__["_struct"] = st
             self.__dict__["_struct_ref"] = ctypes.byref(st)
         return st
+
+    def _validate(self) -> None:
+        T, K, E, G = self.T, self.K, self.E, self.G
+        sizes = {"expert_count": E, "expert_offset": E + 1, "group_count": G, "group_offset": G + 1,
+                 "tok_group_mask": T, "slot_e": T * K, "slot_g": T * K, "slot_tg": T * G,
+                 "recv_src_e": T * K, "recv_src_g": T * min(K, G), "status": 1}
+        for n, size in sizes.items():
+            _need(getattr(self, n), torch.int32, (size,), f"Layout.{n}")
+        ws = self.workspace
+        if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+            raise ValueError("Layout.workspace must be a contiguous 1-D uint8 tensor")
 
     def ref(self):
         self.struct()
@@ -223,12 +251,39 @@ def moe_layout(topk_idx: torch.Tensor, E: int, G: int, *, out: Layout | None = N
     return L
 
 
-@dataclasses.dataclass
+@dataclasses.dataclass(frozen=True)
 class Dispatched:
+    """Receive arrays. Checked once, here, for agreeing shapes and dense storage; a
+    call then checks only H, K and the element type (the arrays must not be resized
+    in place afterwards)."""
     recv_x: torch.Tensor          # bf16 [cap, H] or uint8 [cap, H]
     recv_scale: torch.Tensor | None   # fp32 [cap, H/128] for FP8
     recv_topk_w: torch.Tensor     # fp32 [cap, K]
     recv_topk_idx: torch.Tensor   # int32 [cap, K]
+
+    def __post_init__(self):
+        x = self.recv_x
+        if x.dim() != 2 or x.dtype not in (torch.bfloat16, torch.uint8):
+            raise ValueError("recv_x must be a bf16 or uint8 [cap, H] tensor")
+        cap, H = x.shape
+        _need(x, x.dtype, (cap, H), "recv_x")
+        if self.recv_scale is not None:
+            _need(self.recv_scale, torch.float32, (cap, H // 128), "recv_scale")
+        if self.recv_topk_w.dim() != 2:
+            raise ValueError("recv_topk_w must be a [cap, K] tensor")
+        K = self.recv_topk_w.shape[1]
+        _need(self.recv_topk_w, torch.float32, (cap, K), "recv_topk_w")
+        _need(self.recv_topk_idx, torch.int32, (cap, K), "recv_topk_idx")
+
+
+def _check_dispatched(D: Dispatched, H: int, K: int, fp8: bool, name: str) -> None:
+    """Receive arrays (consistent since construction) fit this call's H, K and dtype."""
+    if D.recv_x.dtype is not (torch.uint8 if fp8 else torch.bfloat16) or D.recv_x.shape[1] != H:
+        raise ValueError(f"{name}.recv_x must be {'uint8' if fp8 else 'bf16'} [cap, {H}]")
+    if fp8 and D.recv_scale is None:
+        raise ValueError(f"{name}.recv_scale is needed for FP8 rows")
+    if D.recv_topk_w.shape[1] != K:
+        raise ValueError(f"{name}.recv_topk_w must have K = {K} columns")
 
 
 def alloc_dispatch(L: Layout, H: int, mode="expert", dtype="bf16", device="cuda",
@@ -251,8 +306,11 @@ def moe_dispatch(L: Layout, x: torch.Tensor, topk_w: torch.Tensor, topk_idx: tor
     for t, dt in ((topk_w, torch.float32), (topk_idx, torch.int32)):
         if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != (L.T, L.K):
             raise ValueError("topk_w / topk_idx must be contiguous [T, K] fp32 / int32")
+    if x.shape[0] != L.T:
+        raise ValueError("x must have one row per token of the layout")
     H = x.shape[1]
     D = out if out is not None else alloc_dispatch(L, H, mode, dtype, x.device)
+    _check_dispatched(D, H, L.K, _dtype(dtype) == DTYPE_FP8, "out")
     _check(_lib.moe_dispatch(L.ref(), _mode(mode), _dtype(dtype), H, _ptr(x),
                              _ptr(topk_w), _ptr(topk_idx), _ptr(D.recv_x), _ptr(D.recv_scale),
                              _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
@@ -269,7 +327,8 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
                         use_workspace: bool = True, stream=None) -> tuple[Layout, Dispatched]:
     """moe_layout + moe_dispatch as one call (moe_layout_dispatch): one launch for the
     smallest batches, the one-launch layout and a dispatch up to T * K = 8192, else the
-    count kernel, an offsets workgroup and a dispatch that places its own tokens.
+    count kernel and a dispatch that computes the offsets (its workgroup 0, or a
+    workgroup launched before it for large batches) and places its own tokens.
     use_workspace=False passes no workspace, which asks for the one-launch form
     (T <= 512 and T * K <= 16384)."""
     if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or not topk_idx.is_contiguous():
@@ -282,8 +341,11 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
     L = out_layout if out_layout is not None else Layout.empty(T, K, E, G, device=topk_idx.device)
     if (L.T, L.K, L.E, L.G) != (T, K, E, G):
         raise ValueError("layout buffers were made for other sizes")
+    if x.shape[0] != T:
+        raise ValueError("x must have one row per token of topk_idx")
     H = x.shape[1]
     D = out if out is not None else alloc_dispatch(L, H, mode, dtype, x.device)
+    _check_dispatched(D, H, K, _dtype(dtype) == DTYPE_FP8, "out")
     ws, nb = (_ptr(L.workspace), L.workspace.numel()) if use_workspace else (None, 0)
     _check(_lib.moe_layout_dispatch(_ptr(topk_idx), L.ref(), ws, nb,
                                     _mode(mode), _dtype(dtype), H,
@@ -297,9 +359,13 @@ def moe_regroup(L: Layout, Dg: Dispatched, *, out: Dispatched | None = None,
                 stream=None) -> Dispatched:
     """Per-group receive arrays -> per-expert receive arrays (moe_regroup)."""
     fp8 = Dg.recv_scale is not None
+    if Dg.recv_x.dim() != 2:
+        raise ValueError("the per-group receive rows must be a 2-D tensor")
     H = Dg.recv_x.shape[1]
+    _check_dispatched(Dg, H, L.K, fp8, "Dg")
     De = out if out is not None else alloc_dispatch(L, H, "expert", "fp8" if fp8 else "bf16",
                                                     Dg.recv_x.device)
+    _check_dispatched(De, H, L.K, fp8, "out")
     _check(_lib.moe_regroup(L.ref(), DTYPE_FP8 if fp8 else DTYPE_BF16, H, _ptr(Dg.recv_x),
                             _ptr(Dg.recv_scale), _ptr(Dg.recv_topk_w), _ptr(Dg.recv_topk_idx),
                             Dg.recv_x.shape[0], _ptr(De.recv_x), _ptr(De.recv_scale),
@@ -329,6 +395,7 @@ def moe_cast_transpose_fp8(L: Layout, x: torch.Tensor, scale: torch.Tensor, *,
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
         raise ValueError("x must be a contiguous bf16 [rows, H] tensor (per-expert layout)")
     rows, H = x.shape
+    _need(scale, torch.float32, (L.E,), "scale")
     nb = _lib.moe_cast_transpose_t_bytes(L.T, L.K, L.E, H)
     if nb < 0:
         raise MoeError(int(nb), "moe_cast_transpose_t_bytes")
@@ -337,6 +404,11 @@ def moe_cast_transpose_fp8(L: Layout, x: torch.Tensor, scale: torch.Tensor, *,
                              torch.empty(max(nb, 16), dtype=torch.uint8, device=x.device),
                              amax if amax is not None else torch.zeros(L.E, dtype=torch.float32, device=x.device),
                              torch.empty(L.E + 1, dtype=torch.int32, device=x.device))
+    _need(out.c, torch.uint8, (rows, H), "out.c")
+    if out.t.dtype != torch.uint8 or out.t.dim() != 1 or not out.t.is_contiguous():
+        raise ValueError("out.t must be a contiguous 1-D uint8 tensor")
+    _need(out.amax, torch.float32, (L.E,), "out.amax")
+    _need(out.pad_offset, torch.int32, (L.E + 1,), "out.pad_offset")
     _check(_lib.moe_cast_transpose_fp8(L.ref(), H, _ptr(x), rows, _ptr(scale), _ptr(out.c), _ptr(out.t),
                                        out.t.numel(), _ptr(out.amax), _ptr(out.pad_offset),
                                        _stream(stream)), "moe_cast_transpose_fp8")
@@ -349,7 +421,9 @@ def moe_combine(L: Layout, y: torch.Tensor, topk_w: torch.Tensor, mode="expert",
     if y.dtype != torch.bfloat16 or y.dim() != 2 or not y.is_contiguous():
         raise ValueError("y must be a contiguous bf16 [rows, H] tensor")
     H = y.shape[1]
+    _need(topk_w, torch.float32, (L.T, L.K), "topk_w")
     o = out if out is not None else torch.empty((L.T, H), dtype=torch.bfloat16, device=y.device)
+    _need(o, torch.bfloat16, (L.T, H), "out")
     _check(_lib.moe_combine(L.ref(), _mode(mode), H, _ptr(y), y.shape[0], _ptr(topk_w),
                             _ptr(o), _stream(stream)), "moe_combine")
     return o
@@ -358,8 +432,12 @@ def moe_combine(L: Layout, y: torch.Tensor, topk_w: torch.Tensor, mode="expert",
 def moe_fp8_dequant(L: Layout, q: torch.Tensor, scale: torch.Tensor, mode="expert", *,
                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Identity expert on FP8 receive rows: bf16(decode(q) * scale) (moe_fp8_dequant)."""
-    cap, H = q.shape
+    cap = _rows(q, "q")
+    H = q.shape[1]
+    _need(q, torch.uint8, (cap, H), "q")
+    _need(scale, torch.float32, (cap, H // 128), "scale")
     y = out if out is not None else torch.empty((cap, H), dtype=torch.bfloat16, device=q.device)
+    _need(y, torch.bfloat16, (cap, H), "out")
     _check(_lib.moe_fp8_dequant(L.ref(), _mode(mode), H, _ptr(q), _ptr(scale), _ptr(y),
                                 cap, _stream(stream)), "moe_fp8_dequant")
     return y
@@ -369,4 +447,7 @@ def moe_ref_copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int | None = None
                  stream=None) -> None:
     """Plain 16-byte streaming copy (measurement reference, not part of the method)."""
     n = src.numel() * src.element_size() if nbytes is None else nbytes
+    if not (src.is_contiguous() and dst.is_contiguous()) or n > min(src.numel() * src.element_size(),
+                                                                      dst.numel() * dst.element_size()):
+        raise ValueError("moe_ref_copy: contiguous src and dst of at least nbytes each")
     _check(_lib.moe_ref_copy(_ptr(dst), _ptr(src), n, _stream(stream)), "moe_ref_copy")
