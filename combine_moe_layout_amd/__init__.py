@@ -326,9 +326,9 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
                         out_layout: Layout | None = None, out: Dispatched | None = None,
                         use_workspace: bool = True, stream=None) -> tuple[Layout, Dispatched]:
     """moe_layout + moe_dispatch as one call (moe_layout_dispatch): one launch for the
-    smallest batches, the one-launch layout and a dispatch up to T * K = 8192, else the
-    count kernel and a dispatch that computes the offsets (its workgroup 0, or a
-    workgroup launched before it for large batches) and places its own tokens.
+    smallest batches (T * K * E <= 4096), else the count kernel and a dispatch that
+    computes the offsets (its workgroup 0, or a workgroup launched before it for large
+    batches) and places its own tokens.
     use_workspace=False passes no workspace, which asks for the one-launch form
     (T <= 512 and T * K <= 16384)."""
     if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or not topk_idx.is_contiguous():

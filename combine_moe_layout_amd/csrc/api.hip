@@ -13,10 +13,6 @@ namespace {
 
 thread_local char g_hip_msg[160] = "";
 
-// moe_layout_dispatch: the one-launch form is used up to this T * K * E (given
-// a workspace; without one, up to the header's limits).
-constexpr int64_t kOneLaunchWork = 1 << 17;
-
 int hip_fail(hipError_t e)
 {
     snprintf(g_hip_msg, sizeof g_hip_msg, "%s (%d)", hipGetErrorString(e), (int)e);
@@ -156,11 +152,11 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
     hipError_t e;
     // One launch for the smallest batches, where its per-token recomputation of
     // the routing (work growing with T * K and E per workgroup) is cheaper than
-    // the three launches of the other form (measured: at E = 256, K = 8 even up
-    // to T = 64, slower from T = 128; at E <= 64 faster up to T = 512), and
-    // whenever no workspace is given.
+    // the two launches of the placing form below (measured: at E = 8, K = 2
+    // 0.3-1 us faster up to T = 256, slower at T = 512; at E = 64 and 256 slower
+    // by 6-9 us from the smallest T), and whenever no workspace is given.
     const bool one_launch_fits = L->T <= MOE_FUSED_MAX_TOKENS && (int64_t)L->T * L->K <= MOE_FUSED_MAX_PAIRS;
-    const bool small = (int64_t)L->T * L->K * L->E <= kOneLaunchWork;
+    const bool small = (int64_t)L->T * L->K * L->E <= moe::tuning().fused_small_max_work;
     if (one_launch_fits && (small || !ws)) {
         e = moe::launch_layout_dispatch(topk_idx, L->T, L->K, L->E, L->G, ptrs_of(L), mode, fp8, H, x,
                                         topk_w, recv_x, recv_scale, recv_topk_w, recv_topk_idx,
@@ -176,7 +172,9 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
     // placement latency once per round of resident workgroups: few rounds for
     // the 128-thread bf16 and one-wave FP8 workgroups, several for the
     // row-sized FP8 ones (H > 8192), where it measured slower than the two
-    // calls. Otherwise: the two calls.
+    // calls. Otherwise: the two calls. (The one-launch layout + a plain
+    // dispatch, once used up to T * K = 8192, measured 1-2.5 us slower than the
+    // placing form at every size tried; it stays selectable for A/B runs.)
     const int64_t pairs = (int64_t)L->T * L->K;
     const bool via_onepass = L->K <= 8 && pairs <= moe::tuning().fused_onepass_max_pairs &&
                              pairs <= moe::tuning().layout_onepass_max_pairs;

@@ -343,6 +343,7 @@ const Tuning &tuning()
         if (const char *f = getenv("MOE_EP_FUSED_ONEPASS_MAX_PAIRS")) r.fused_onepass_max_pairs = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_FINALIZE")) r.fused_finalize = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_FINALIZE_ROUNDS")) r.fused_finalize_rounds = atoi(f);
+        if (const char *f = getenv("MOE_EP_FUSED_SMALL_MAX_WORK")) r.fused_small_max_work = atoi(f);
         return r;
     }();
     return t;

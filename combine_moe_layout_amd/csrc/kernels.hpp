@@ -96,16 +96,17 @@ inline uint32_t group_magic(int E, int G)
 // Cache policy of the dispatch row loads and stores, the FP8 dispatch's form
 // and the largest batch of the one-launch layout. Defaults are the measured
 // best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2,
-// MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>, MOE_EP_FUSED_FINALIZE=0/1/2 and
-// MOE_EP_FUSED_FINALIZE_ROUNDS=<n> in the environment override them (read once
-// per process) for A/B runs.
+// MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>, MOE_EP_FUSED_SMALL_MAX_WORK=<T*K*E>,
+// MOE_EP_FUSED_FINALIZE=0/1/2 and MOE_EP_FUSED_FINALIZE_ROUNDS=<n> in the
+// environment override them (read once per process) for A/B runs.
 struct Tuning {
     bool dispatch_nt_load = true;    // x rows are read once
     bool dispatch_nt_store = false;  // receive rows
     int fp8_form = 1;                // FP8 dispatch: 0 row-sized workgroups, 1 one wave
                                      // per token, 2 two waves per token (H <= 16 * BS * 8)
     int layout_onepass_max_pairs = 16384;   // moe_layout in one launch up to T * K pairs (top-k <= 8)
-    int fused_onepass_max_pairs = 8192;     // moe_layout_dispatch as that layout + a plain dispatch
+    int fused_onepass_max_pairs = 0;        // moe_layout_dispatch as that layout + a plain dispatch
+    int fused_small_max_work = 4096;        // moe_layout_dispatch in one launch up to T * K * E
     int fused_finalize = 2;                 // placing dispatch: 0 the finalize kernel, 1 its
                                             // workgroup 0 (bf16), 2 workgroup 0 (bf16 and FP8)
     int fused_finalize_rounds = 4;          // ... for E up to this many columns per thread

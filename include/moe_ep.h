@@ -175,17 +175,16 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
 /* moe_layout() and moe_dispatch() as one call. The layout arrays and the
  * receive buffers it writes are, bit for bit, those the two calls write
  * (layout->status included). Arguments as for moe_layout() and moe_dispatch().
- * The smallest batches (T * K * E <= 2^17), and any batch within
+ * The smallest batches (T * K * E <= 4096), and any batch within
  * T <= MOE_FUSED_MAX_TOKENS and T * K <= MOE_FUSED_MAX_PAIRS when ws is NULL,
  * take one launch and need no workspace: one workgroup per token recomputes
  * the routing it needs from the whole index array, a cost that grows with
  * T * K and E. Other batches need ws (moe_layout_workspace_bytes()). With
- * K <= 8 and T * K <= 8192 the call runs moe_layout() (one launch at these
- * sizes) and the dispatch. Larger batches with K <= 8 (BF16, or FP8 with
- * H <= 8192) run the layout's count kernel and then a dispatch in which each
- * workgroup computes its own token's slots from the per-tile token masks
- * while its row loads are in flight, so the separate placement launch of
- * moe_layout() disappears. The offsets and per-tile bases come from
+ * K <= 8 (BF16, or FP8 with H <= 8192) they run the layout's count kernel
+ * and then a dispatch in which each workgroup computes its own token's slots
+ * from the per-tile token masks while its row loads are in flight, so the
+ * separate placement launch of moe_layout() disappears. The offsets and
+ * per-tile bases come from
  * workgroup 0 of that dispatch (T <= 4096 and at most four experts per
  * dispatch thread: E <= 512 for BF16, E <= 256 for FP8), which the other
  * workgroups wait for within a bounded time (MOE_STATUS_SYNC_TIMEOUT), or

@@ -32,12 +32,12 @@ def _u16_to_bf16_tensor(a):
 
 
 # (T, H, E, G, K, fused): fused = capture moe_layout_dispatch instead of the two calls
-# (one launch for the smallest batches, the one-launch layout + a dispatch up to
-# T * K = 8192, count, offsets and a placing dispatch above); moe_layout takes one launch
-# up to T * K = 16384 and count + place above (2500 x 8)
+# (one launch for the smallest batches; else the count kernel and a placing dispatch
+# whose workgroup 0 computes the offsets); moe_layout takes one launch up to
+# T * K = 16384 and count + place above (2500 x 8)
 CASES = [(700, 1024, 64, 8, 6, False), (300, 512, 32, 4, 8, True), (2000, 2048, 256, 8, 8, False),
          (2000, 2048, 256, 8, 8, True), (1500, 512, 64, 8, 6, True), (2500, 1024, 256, 8, 8, False),
-         (700, 1024, 64, 8, 8, True)]   # the fused call as one-launch layout + dispatch
+         (700, 1024, 64, 8, 8, True), (64, 2048, 8, 8, 2, True)]   # the last in one launch
 
 
 @pytest.mark.parametrize("T,H,E,G,K,fused", CASES)

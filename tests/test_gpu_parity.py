@@ -481,16 +481,17 @@ def test_stream_ordering_on_side_stream(moe, orc):
 
 # ------------------------------------------------------------------ fused layout + dispatch
 
-# (T, H, E, G, K). Forms: one launch for T * K * E <= 2^17 (T <= 512); up to T * K = 8192
-# (K <= 8) the one-launch layout + a dispatch; above, count + offsets + a placing dispatch;
-# K > 8, the two calls
+# (T, H, E, G, K). Forms: one launch for T * K * E <= 4096 (and for T <= 512 without a
+# workspace); else (K <= 8) the count kernel + a placing dispatch whose workgroup 0 computes
+# the offsets (up to 16 tiles and 4 expert columns per thread; beyond, an offsets
+# workgroup in between); K > 8, the two calls
 FUSED_SHAPES = [
     (1, 8, 8, 8, 2), (16, 2048, 8, 8, 2), (256, 7168, 256, 8, 8), (512, 1024, 64, 8, 8),
     (300, 520, 16, 4, 3), (100, 1024, 1024, 32, 32), (511, 4096, 128, 1, 8), (77, 2048, 7, 7, 1),
     (257, 1152, 96, 4, 6),
     (513, 1024, 64, 8, 8), (1000, 512, 32, 4, 3), (2000, 256, 16, 16, 1), (777, 384, 40, 1, 5),
     (600, 256, 64, 8, 13), (4097, 2048, 256, 8, 8), (3000, 128, 1024, 32, 8), (1030, 512, 64, 8, 8),
-    (600, 8320, 32, 8, 8),    # rows over 8192 through the one-launch layout
+    (600, 8320, 32, 8, 8),    # rows over 8192: multi-pass placing bf16 dispatch
     (1100, 8320, 32, 8, 8),   # rows over 8192: multi-pass placing bf16 dispatch; FP8 takes the two calls
     (2000, 1024, 200, 8, 8),  # offsets computed in the dispatch: a partial second round of columns
     (1500, 256, 256, 32, 8),  # ... with 32 groups
