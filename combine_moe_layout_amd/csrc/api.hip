@@ -214,6 +214,7 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
     pa.table = w.table;
     pa.ntiles = moe::layout_tiles(L->T);
     pa.finalize = fin_in_dispatch ? 1 : 0;
+    pa.wait_ticks = moe::tuning().base_wait_ticks < 0 ? 0 : (uint64_t)moe::tuning().base_wait_ticks;
     pa.L = P;
     pa.mode = mode == MOE_MODE_EXPERT ? 0 : 1;
     e = fp8 ? moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, nullptr, topk_w, topk_idx, recv_x, recv_scale,

@@ -344,6 +344,7 @@ const Tuning &tuning()
         if (const char *f = getenv("MOE_EP_FUSED_FINALIZE")) r.fused_finalize = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_FINALIZE_ROUNDS")) r.fused_finalize_rounds = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_SMALL_MAX_WORK")) r.fused_small_max_work = atoi(f);
+        if (const char *f = getenv("MOE_EP_BASE_WAIT_TICKS")) r.base_wait_ticks = atoll(f);
         return r;
     }();
     return t;

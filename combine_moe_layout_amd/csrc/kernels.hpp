@@ -84,6 +84,7 @@ struct PlaceArgs {
     const int32_t *table;      // the count kernel's per-tile counts and error bits
     int ntiles;
     int finalize;              // 1: workgroup 0 computes the bases, counts, offsets and status
+    uint64_t wait_ticks;       // longest wait for a tile's bases (constant 100 MHz clock)
     LayoutPtrs L;
     int mode;   // destinations: slot_e (0) or slot_tg (1)
 };
@@ -97,8 +98,9 @@ inline uint32_t group_magic(int E, int G)
 // and the largest batch of the one-launch layout. Defaults are the measured
 // best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2,
 // MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>, MOE_EP_FUSED_SMALL_MAX_WORK=<T*K*E>,
-// MOE_EP_FUSED_FINALIZE=0/1/2 and MOE_EP_FUSED_FINALIZE_ROUNDS=<n> in the
-// environment override them (read once per process) for A/B runs.
+// MOE_EP_FUSED_FINALIZE=0/1/2, MOE_EP_FUSED_FINALIZE_ROUNDS=<n> and
+// MOE_EP_BASE_WAIT_TICKS=<ticks> in the environment override them (read once per
+// process) for A/B runs and tests.
 struct Tuning {
     bool dispatch_nt_load = true;    // x rows are read once
     bool dispatch_nt_store = false;  // receive rows
@@ -107,6 +109,9 @@ struct Tuning {
     int layout_onepass_max_pairs = 16384;   // moe_layout in one launch up to T * K pairs (top-k <= 8)
     int fused_onepass_max_pairs = 0;        // moe_layout_dispatch as that layout + a plain dispatch
     int fused_small_max_work = 4096;        // moe_layout_dispatch in one launch up to T * K * E
+    long long base_wait_ticks = 20000000;   // placing dispatch: longest wait for a tile's bases
+                                            // (0.2 s at 100 MHz; a tiny value forces the timeout
+                                            // path in tests)
     int fused_finalize = 2;                 // placing dispatch: 0 the finalize kernel, 1 its
                                             // workgroup 0 (bf16), 2 workgroup 0 (bf16 and FP8)
     int fused_finalize_rounds = 4;          // ... for E up to this many columns per thread

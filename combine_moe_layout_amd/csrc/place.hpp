@@ -19,9 +19,9 @@
 // base words it needs until they are valid: agent-scope atomic stores and
 // loads of those words, no flag and no state that outlives the call. Workgroup
 // 0 waits for nothing, and is the first workgroup dispatched; a wait is still
-// bounded (0.2 s by the constant clock, against the few µs it takes), after
-// which the token is skipped and MOE_STATUS_SYNC_TIMEOUT is set, so no wave
-// can wait forever.
+// bounded (P.wait_ticks of the constant 100 MHz clock, 0.2 s by default,
+// against the few µs it takes), after which the token is skipped and
+// MOE_STATUS_SYNC_TIMEOUT is set, so no wave can wait forever.
 #pragma once
 
 #include "moe_ep.h"
@@ -50,7 +50,6 @@ __device__ __forceinline__ int place_rank(const uint32_t *__restrict__ q, int w,
     return r;
 }
 
-constexpr uint64_t kBaseWaitTicks = 20000000;   // 0.2 s of the constant 100 MHz clock
 constexpr int kFinBatch = kFinTiles;
 
 __device__ __forceinline__ int base_load(int32_t *p)
@@ -213,7 +212,7 @@ __device__ __forceinline__ void place_token(const PlaceArgs &P, int t, int K, in
             if (valid) be = base_load(tb + e);
             if (hg) bg = base_load(tb + E + lane);
             if (__all(be >= 0 && bg >= 0)) break;
-            if (wall_clock64() - t0 > kBaseWaitTicks) {
+            if (wall_clock64() - t0 > P.wait_ticks) {
                 ok = false;
                 break;
             }

@@ -8,6 +8,10 @@ Shapes: every named workload at full size (the sizes bench.py times), small
 shapes spanning several layout tiles with ragged tails, and edge cases
 (T = 0 / 1, K = 1 / 32, G = 1 / E, ragged and multi-pass H, invalid entries).
 """
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -166,6 +170,17 @@ def test_fused_call_reuses_buffers_without_stale_state(moe, orc, T):
         R = Lo["R_expert"]
         src = Lo["recv_src_e"][:R] // K
         assert torch.equal(D.recv_x[:R].view(torch.int16).cpu(), x.view(torch.int16).cpu()[torch.from_numpy(src).long()])
+
+
+def test_sync_timeout_skips_tokens_cleanly():
+    """The placing dispatch's bounded wait for its tile's bases, forced from the host
+    (a wait limit of 0 ticks, set in a process of its own): tokens that give up are
+    skipped whole and reported, the others are placed exactly; no wave waits longer."""
+    env = dict(os.environ, MOE_EP_BASE_WAIT_TICKS="0")
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sync_timeout_child.py")
+    r = subprocess.run([sys.executable, "-u", child], env=env, capture_output=True, text=True, timeout=240)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
 
 
 @pytest.mark.parametrize("T,K,E,G", [(700, 8, 256, 8), (300, 4, 64, 4), (513, 2, 16, 8)])
