@@ -125,7 +125,8 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
                                       recv_topk_w, recv_topk_idx, nullptr, (hipStream_t)stream);
     else
         e = moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
-                                     recv_scale, recv_topk_w, recv_topk_idx, nullptr, (hipStream_t)stream);
+                                     recv_scale, recv_topk_w, recv_topk_idx, nullptr,
+                                     mode == MOE_MODE_GROUP, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
@@ -184,7 +185,7 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
         if (e == hipSuccess)
             e = fp8 ? moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
                                                recv_scale, recv_topk_w, recv_topk_idx, nullptr,
-                                               (hipStream_t)stream)
+                                               mode == MOE_MODE_GROUP, (hipStream_t)stream)
                     : moe::launch_dispatch_bf16(x, L->T, H, L->K, nslot, slots, topk_w, topk_idx, recv_x,
                                                 recv_topk_w, recv_topk_idx, nullptr, (hipStream_t)stream);
         return e == hipSuccess ? MOE_OK : hip_fail(e);
@@ -218,7 +219,7 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
     pa.L = P;
     pa.mode = mode == MOE_MODE_EXPERT ? 0 : 1;
     e = fp8 ? moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, nullptr, topk_w, topk_idx, recv_x, recv_scale,
-                                       recv_topk_w, recv_topk_idx, &pa, (hipStream_t)stream)
+                                       recv_topk_w, recv_topk_idx, &pa, mode == MOE_MODE_GROUP, (hipStream_t)stream)
             : moe::launch_dispatch_bf16(x, L->T, H, L->K, nslot, nullptr, topk_w, topk_idx, recv_x,
                                         recv_topk_w, recv_topk_idx, &pa, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);

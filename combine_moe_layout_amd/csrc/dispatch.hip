@@ -222,9 +222,11 @@ __global__ __launch_bounds__(kFp8MaxBS) void dispatch_fp8_kernel(
 // Small workgroups (BS = 64 or 128 lanes per token, H <= 16 * BS * 8): lane
 // l holds chunks l, l + BS, ..., l + BS (ITER - 1), so a 128-block is still
 // 8 consecutive lanes in every pass, and more workgroups are resident at once
-// than with the row-sized workgroups above.
-template <int BS, int ITER, bool NT, bool NTL, bool PLACE>
-__global__ __launch_bounds__(BS) void dispatch_fp8_wave_kernel(
+// than with the row-sized workgroups above. WPE: the fewest waves per SIMD the
+// register allocation must allow (1: no bound; 4: 128 VGPRs, which spills a
+// few bytes and pays off only for the plain per-group dispatch, measured).
+template <int BS, int ITER, bool NT, bool NTL, bool PLACE, int WPE>
+__global__ __launch_bounds__(BS) __attribute__((amdgpu_waves_per_eu(WPE))) void dispatch_fp8_wave_kernel(
     const u32x4 *__restrict__ x, int nch, int K, int nslot, const int32_t *__restrict__ slots,
     const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
     u32x4 *__restrict__ recv_q, float *__restrict__ recv_scale, float *__restrict__ recv_w,
@@ -345,6 +347,7 @@ const Tuning &tuning()
         if (const char *f = getenv("MOE_EP_FUSED_FINALIZE_ROUNDS")) r.fused_finalize_rounds = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_SMALL_MAX_WORK")) r.fused_small_max_work = atoi(f);
         if (const char *f = getenv("MOE_EP_BASE_WAIT_TICKS")) r.base_wait_ticks = atoll(f);
+        env("MOE_EP_FP8_GROUP_W4", r.fp8_group_w4);
         return r;
     }();
     return t;
@@ -383,26 +386,26 @@ auto pick_fp8(bool nt, bool ntl, bool full)
 
 namespace {
 
-template <int BS, bool NT, bool NTL, bool PLACE>
+template <int BS, bool NT, bool NTL, bool PLACE, int WPE>
 auto pick_fp8_wave(int iter)
 {
     switch (iter) {
-    case 1: return dispatch_fp8_wave_kernel<BS, 1, NT, NTL, PLACE>;
-    case 2: return dispatch_fp8_wave_kernel<BS, 2, NT, NTL, PLACE>;
-    case 3: return dispatch_fp8_wave_kernel<BS, 3, NT, NTL, PLACE>;
-    case 4: return dispatch_fp8_wave_kernel<BS, 4, NT, NTL, PLACE>;
-    case 5: return dispatch_fp8_wave_kernel<BS, 5, NT, NTL, PLACE>;
-    case 6: return dispatch_fp8_wave_kernel<BS, 6, NT, NTL, PLACE>;
-    case 7: return dispatch_fp8_wave_kernel<BS, 7, NT, NTL, PLACE>;
-    default: return dispatch_fp8_wave_kernel<BS, 8, NT, NTL, PLACE>;
+    case 1: return dispatch_fp8_wave_kernel<BS, 1, NT, NTL, PLACE, WPE>;
+    case 2: return dispatch_fp8_wave_kernel<BS, 2, NT, NTL, PLACE, WPE>;
+    case 3: return dispatch_fp8_wave_kernel<BS, 3, NT, NTL, PLACE, WPE>;
+    case 4: return dispatch_fp8_wave_kernel<BS, 4, NT, NTL, PLACE, WPE>;
+    case 5: return dispatch_fp8_wave_kernel<BS, 5, NT, NTL, PLACE, WPE>;
+    case 6: return dispatch_fp8_wave_kernel<BS, 6, NT, NTL, PLACE, WPE>;
+    case 7: return dispatch_fp8_wave_kernel<BS, 7, NT, NTL, PLACE, WPE>;
+    default: return dispatch_fp8_wave_kernel<BS, 8, NT, NTL, PLACE, WPE>;
     }
 }
 
-template <int BS, bool PLACE>
+template <int BS, bool PLACE, int WPE = 1>
 auto pick_fp8_wave_flags(int iter, bool nt, bool ntl)
 {
-    if (nt) return ntl ? pick_fp8_wave<BS, true, true, PLACE>(iter) : pick_fp8_wave<BS, true, false, PLACE>(iter);
-    return ntl ? pick_fp8_wave<BS, false, true, PLACE>(iter) : pick_fp8_wave<BS, false, false, PLACE>(iter);
+    if (nt) return ntl ? pick_fp8_wave<BS, true, true, PLACE, WPE>(iter) : pick_fp8_wave<BS, true, false, PLACE, WPE>(iter);
+    return ntl ? pick_fp8_wave<BS, false, true, PLACE, WPE>(iter) : pick_fp8_wave<BS, false, false, PLACE, WPE>(iter);
 }
 
 // lanes per token of the small-workgroup FP8 form (0: the row-sized form)
@@ -421,15 +424,19 @@ int placing_dispatch_threads(bool fp8, int H) { return fp8 ? fp8_small_bs(H) : k
 hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
                                const float *topk_w, const int32_t *topk_idx, void *recv_q,
                                float *recv_scale, float *recv_w, int32_t *recv_idx,
-                               const PlaceArgs *place, hipStream_t stream)
+                               const PlaceArgs *place, bool group_rows, hipStream_t stream)
 {
     const int nch = H / 16;
     const bool nt = tuning().dispatch_nt_store, ntl = tuning().dispatch_nt_load;
     if (const int sbs = fp8_small_bs(H)) {
         const int iter = (nch + sbs - 1) / sbs;
+        // the plain per-group dispatch: 4 waves per SIMD (38.5 against 40.6 us at
+        // t4096; the per-expert one and the placing forms are slower so)
+        const bool w4 = !place && group_rows && sbs == kWave && tuning().fp8_group_w4;
         auto fn = sbs == kWave
                       ? (place ? pick_fp8_wave_flags<kWave, true>(iter, nt, ntl)
-                               : pick_fp8_wave_flags<kWave, false>(iter, nt, ntl))
+                               : (w4 ? pick_fp8_wave_flags<kWave, false, 4>(iter, nt, ntl)
+                                     : pick_fp8_wave_flags<kWave, false>(iter, nt, ntl)))
                       : (place ? pick_fp8_wave_flags<2 * kWave, true>(iter, nt, ntl)
                                : pick_fp8_wave_flags<2 * kWave, false>(iter, nt, ntl));
         hipLaunchKernelGGL(fn, dim3(T), dim3(sbs), 0, stream, (const u32x4 *)x, nch, K, nslot, slots,

@@ -97,7 +97,8 @@ inline uint32_t group_magic(int E, int G)
 // Cache policy of the dispatch row loads and stores, the FP8 dispatch's form
 // and the largest batch of the one-launch layout. Defaults are the measured
 // best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2,
-// MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>, MOE_EP_FUSED_SMALL_MAX_WORK=<T*K*E>,
+// MOE_EP_FP8_GROUP_W4=0/1, MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>,
+// MOE_EP_FUSED_SMALL_MAX_WORK=<T*K*E>,
 // MOE_EP_FUSED_FINALIZE=0/1/2, MOE_EP_FUSED_FINALIZE_ROUNDS=<n> and
 // MOE_EP_BASE_WAIT_TICKS=<ticks> in the environment override them (read once per
 // process) for A/B runs and tests.
@@ -106,6 +107,7 @@ struct Tuning {
     bool dispatch_nt_store = false;  // receive rows
     int fp8_form = 1;                // FP8 dispatch: 0 row-sized workgroups, 1 one wave
                                      // per token, 2 two waves per token (H <= 16 * BS * 8)
+    bool fp8_group_w4 = true;        // plain per-group FP8 dispatch at 4 waves per SIMD
     int layout_onepass_max_pairs = 16384;   // moe_layout in one launch up to T * K pairs (top-k <= 8)
     int fused_onepass_max_pairs = 0;        // moe_layout_dispatch as that layout + a plain dispatch
     int fused_small_max_work = 4096;        // moe_layout_dispatch in one launch up to T * K * E
@@ -130,10 +132,11 @@ hipError_t launch_dispatch_bf16(const void *x, int T, int H, int K, int nslot, c
                                 float *recv_w, int32_t *recv_idx, const PlaceArgs *place,
                                 hipStream_t stream);
 
+// group_rows: the destinations are per-group rows (chooses the instance).
 hipError_t launch_dispatch_fp8(const void *x, int T, int H, int K, int nslot, const int32_t *slots,
                                const float *topk_w, const int32_t *topk_idx, void *recv_q,
                                float *recv_scale, float *recv_w, int32_t *recv_idx,
-                               const PlaceArgs *place, hipStream_t stream);
+                               const PlaceArgs *place, bool group_rows, hipStream_t stream);
 
 // Combine. slot: [T, K] (slot_e, or slot_g whose entries may repeat within a token).
 hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, const int32_t *slot,
