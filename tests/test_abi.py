@@ -154,3 +154,22 @@ def test_package_has_no_cpu_fallback():
         if fn.endswith(".py"):
             src = open(os.path.join(pkg, fn)).read()
             assert "import oracle" not in src and "from oracle" not in src, fn
+
+
+def test_binding_constants_match_the_header(moe):
+    """The Python binding's status bits, modes, dtypes and one-launch limits are the
+    values include/moe_ep.h defines (the binding restates them; this keeps them equal)."""
+    text = open(os.path.join(ROOT, "include", "moe_ep.h")).read()
+    defs = dict(re.findall(r"#define\s+(MOE_[A-Z0-9_]+)\s+(\d+)", text))
+    enums = dict(re.findall(r"(MOE_(?:MODE|DTYPE)_[A-Z0-9_]+)\s*=\s*(\d+)", text))
+    assert int(defs["MOE_STATUS_BAD_INDEX"]) == moe.STATUS_BAD_INDEX
+    assert int(defs["MOE_STATUS_DUPLICATE"]) == moe.STATUS_DUPLICATE
+    assert int(defs["MOE_STATUS_Y_ROWS"]) == moe.STATUS_Y_ROWS
+    assert int(defs["MOE_STATUS_SYNC_TIMEOUT"]) == moe.STATUS_SYNC_TIMEOUT
+    assert int(defs["MOE_FUSED_MAX_TOKENS"]) == moe.FUSED_MAX_TOKENS
+    assert int(defs["MOE_FUSED_MAX_PAIRS"]) == moe.FUSED_MAX_PAIRS
+    assert int(enums["MOE_MODE_EXPERT"]) == moe.MODE_EXPERT and int(enums["MOE_MODE_GROUP"]) == moe.MODE_GROUP
+    assert int(enums["MOE_DTYPE_BF16"]) == moe.DTYPE_BF16
+    assert int(enums["MOE_DTYPE_FP8_E4M3_B128"]) == moe.DTYPE_FP8
+    bits = [int(v) for k, v in defs.items() if k.startswith("MOE_STATUS_")]
+    assert sorted(bits) == [1 << i for i in range(len(bits))]      # distinct single bits
