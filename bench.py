@@ -210,7 +210,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the expert groups of one EP rank live in one GPU's HBM)", file=sys.stderr)
         sys.exit(2)
 

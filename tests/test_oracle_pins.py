@@ -385,7 +385,7 @@ def test_bf16_encode_against_torch(orc):
 def test_bf16_encode_non_finite(orc):
     """Infinities stay infinities, values past the largest bf16 round to them, and every
     NaN (either sign, any payload: quiet, signalling, all ones) becomes a NaN: the
-    canonical quiet NaN 0x7FC0 here (torch also gives a NaN, 0xFFFF on this build)."""
+    canonical quiet NaN 0x7FC0 (torch's CPU cast also gives a NaN, with another payload)."""
     special = np.array([0x7F800000, 0xFF800000, 0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F8000, 0x7F7F7FFF,
                         0x7FC00000, 0xFFC00000, 0x7F800001, 0xFF800001, 0x7FFFFFFF, 0xFFFFFFFF,
                         0x7FBFFFFF, 0xFFFF8000], np.uint32).view(np.float32)
