@@ -345,6 +345,29 @@ def test_dispatch_fp8_adversarial_blocks(moe, orc, mode, T, H, E, G, K):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("H", [2944, 4096, 5120, 6016, 8192])   # 3..8 passes of 64 lanes, two ragged
+def test_dispatch_fp8_every_pass_count(moe, orc, mode, H):
+    """The one-wave FP8 dispatch at every pass count it compiles (per-expert and
+    per-group instances differ), plain and through the fused call, on adversarial
+    blocks."""
+    T, E, G, K = 200, 64, 8, 8
+    d = si.make_inputs(T, 8, E, K, seed=H)
+    x = adversarial_rows(T, H, seed=H + 1)
+    idx_d, w_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"])
+    Lo = orc.layout(d["topk_idx"], E, G)
+    Do = orc.dispatch_fp8(Lo, mode, x, d["topk_w"], d["topk_idx"])
+    L = moe.moe_layout(idx_d, E, G)
+    fp8_check(dispatch_with_canary(moe, L, dev_bf16(x), w_d, idx_d, mode, "fp8"), Do)
+    L2 = moe.Layout.empty(T, K, E, G)
+    D2 = moe.alloc_dispatch(L2, H, mode, "fp8")
+    D2.recv_x.fill_(0xA5)
+    D2.recv_scale.fill_(-1.5)
+    L2, D2 = moe.moe_layout_dispatch(idx_d, E, G, dev_bf16(x), w_d, mode, "fp8", out_layout=L2, out=D2)
+    check_layout(L2, Lo)
+    fp8_check(D2, Do)
+
+
+@pytest.mark.parametrize("mode", MODES)
 def test_fp8_dequant_matches_oracle(moe, orc, mode):
     d = workload("fp8") if mode == "expert" else workload("t256")
     wl = d["workload"]
