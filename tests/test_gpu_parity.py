@@ -345,6 +345,31 @@ def test_dispatch_fp8_adversarial_blocks(moe, orc, mode, T, H, E, G, K):
 
 
 @pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("H", [2056, 3072, 5120, 6144, 6152, 8192])   # 3..8 vectors per lane, two ragged
+def test_dispatch_bf16_every_vector_count(moe, orc, mode, H):
+    """The bf16 dispatch at every vector count per lane it compiles, plain and through
+    the fused call (the placing instances), with ragged last passes."""
+    T, E, G, K = 300, 64, 8, 8
+    d = si.make_inputs(T, H, E, K, seed=H + 3)
+    idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
+    Lo = orc.layout(d["topk_idx"], E, G)
+    Do = orc.dispatch_bf16(Lo, mode, d["x"], d["topk_w"], d["topk_idx"])
+    R = Do["R"]
+    L = moe.moe_layout(idx_d, E, G)
+    D = dispatch_with_canary(moe, L, x_d, w_d, idx_d, mode)
+    L2 = moe.Layout.empty(T, K, E, G)
+    D2 = moe.alloc_dispatch(L2, H, mode, "bf16")
+    D2.recv_x.view(torch.int16).fill_(int(CANARY16.astype(np.int16)))
+    L2, D2 = moe.moe_layout_dispatch(idx_d, E, G, x_d, w_d, mode, out_layout=L2, out=D2)
+    check_layout(L2, Lo)
+    for got in (D, D2):
+        rx = host_u16(got.recv_x)
+        np.testing.assert_array_equal(rx[:R], Do["recv_x"])
+        assert np.all(rx[R:] == CANARY16)
+        np.testing.assert_array_equal(got.recv_topk_idx.cpu().numpy()[:R], Do["recv_idx"])
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("H", [2944, 4096, 5120, 6016, 8192])   # 3..8 passes of 64 lanes, two ragged
 def test_dispatch_fp8_every_pass_count(moe, orc, mode, H):
     """The one-wave FP8 dispatch at every pass count it compiles (per-expert and
