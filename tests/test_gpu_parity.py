@@ -448,7 +448,11 @@ def test_combine_full_workloads(moe, orc, name, mode):
 
 COMBINE_EDGE = [(1, 8, 8, 8, 2), (3, 520, 16, 4, 3), (200, 1024, 32, 8, 5), (40, 16392, 64, 8, 8),
                 (300, 4096, 128, 1, 8), (100, 2048, 64, 32, 32), (77, 7168, 256, 8, 4),
-                (90, 3072, 96, 4, 6), (64, 2048, 32, 32, 32), (33, 1024, 8, 2, 8), (5, 8, 1, 1, 1)]
+                (90, 3072, 96, 4, 6), (64, 2048, 32, 32, 32), (33, 1024, 8, 2, 8), (5, 8, 1, 1, 1),
+                # two vectors per lane (rows of 1025-2048 whole waves' vectors), and the 128-thread
+                # form at 2, 4 and 7 vectors per lane with ragged passes
+                (60, 12288, 64, 8, 8), (50, 16384, 32, 8, 5), (70, 1544, 32, 8, 8), (70, 3080, 32, 4, 6),
+                (70, 6152, 64, 8, 8)]
 
 
 @pytest.mark.parametrize("T,H,E,G,K", COMBINE_EDGE)
