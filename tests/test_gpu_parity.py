@@ -674,7 +674,10 @@ def test_fused_layout_dispatch_equals_two_calls(moe, name):
 # ------------------------------------------------------------------ receive-side regroup
 
 REGROUP_SHAPES = [("t256", None), ("skew", None), ("fp8", None), ("tiny", None),
-                  (None, (300, 520, 16, 4, 3)), (None, (129, 1024, 64, 1, 8)), (None, (50, 16392, 64, 8, 8))]
+                  (None, (300, 520, 16, 4, 3)), (None, (129, 1024, 64, 1, 8)), (None, (50, 16392, 64, 8, 8)),
+                  # 3, 5, 6 and 8 vectors per lane (bf16); 2 and 3 ragged, 3 and 4 whole (FP8)
+                  (None, (200, 3072, 32, 8, 8)), (None, (200, 5120, 32, 8, 8)), (None, (200, 6144, 64, 8, 8)),
+                  (None, (100, 8192, 32, 8, 8))]
 # FP8 needs H % 128 == 0: not for H = 520 or 16392
 REGROUP_CASES = [(n, s, dt) for n, s in REGROUP_SHAPES for dt in ("bf16", "fp8")
                  if not (dt == "fp8" and s is not None and s[1] % 128)]
