@@ -170,16 +170,21 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
     const int nslot = mode == MOE_MODE_EXPERT ? L->K : L->G;
     const int32_t *slots = mode == MOE_MODE_EXPERT ? L->slot_e : L->slot_tg;
     // The placing dispatch needs the per-tile masks (K <= 8) and pays its
-    // placement latency once per round of resident workgroups: few rounds for
-    // the 128-thread bf16 and one-wave FP8 workgroups, several for the
-    // row-sized FP8 ones (H > 8192), where it measured slower than the two
-    // calls. Otherwise: the two calls. (The one-launch layout + a plain
-    // dispatch, once used up to T * K = 8192, measured 1-2.5 us slower than the
-    // placing form at every size tried; it stays selectable for A/B runs.)
+    // placement latency once per round of resident workgroups. For bf16 (few
+    // rounds of 128-thread workgroups) it beats moe_layout + the plain dispatch
+    // at every size tried. The one-wave FP8 workgroups (3 per SIMD, so 3072 at
+    // once) measured 1-4 us faster up to T = 3072 and even to 1.2 us slower at
+    // T = 4096, where a second round pays the placement again: placing up to
+    // 3072 tokens, moe_layout + the plain FP8 dispatch above. The row-sized FP8
+    // workgroups (H > 8192) are slower placing. (The one-launch layout + a
+    // plain dispatch, once used up to T * K = 8192, measured 1-2.5 us slower
+    // than the bf16 placing form at every size tried; it stays selectable for
+    // A/B runs.)
     const int64_t pairs = (int64_t)L->T * L->K;
     const bool via_onepass = L->K <= 8 && pairs <= moe::tuning().fused_onepass_max_pairs &&
                              pairs <= moe::tuning().layout_onepass_max_pairs;
-    if (L->K > 8 || (fp8 && !moe::fp8_wave_form(H)) || via_onepass) {
+    if (L->K > 8 || (fp8 && (!moe::fp8_wave_form(H) || L->T > moe::tuning().fused_fp8_place_max_t)) ||
+        via_onepass) {
         e = moe::launch_layout(topk_idx, L->T, L->K, L->E, L->G, P, static_cast<int32_t *>(ws),
                                (hipStream_t)stream);
         if (e == hipSuccess)

@@ -97,7 +97,7 @@ inline uint32_t group_magic(int E, int G)
 // Cache policy of the dispatch row loads and stores, the FP8 dispatch's form
 // and the largest batch of the one-launch layout. Defaults are the measured
 // best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2,
-// MOE_EP_FP8_GROUP_W4=0/1, MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>,
+// MOE_EP_FP8_GROUP_W4=0/1, MOE_EP_FUSED_FP8_PLACE_MAX_T=<T>, MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>,
 // MOE_EP_FUSED_SMALL_MAX_WORK=<T*K*E>,
 // MOE_EP_FUSED_FINALIZE=0/1/2, MOE_EP_FUSED_FINALIZE_ROUNDS=<n> and
 // MOE_EP_BASE_WAIT_TICKS=<ticks> in the environment override them (read once per
@@ -108,6 +108,8 @@ struct Tuning {
     int fp8_form = 1;                // FP8 dispatch: 0 row-sized workgroups, 1 one wave
                                      // per token, 2 two waves per token (H <= 16 * BS * 8)
     bool fp8_group_w4 = true;        // plain per-group FP8 dispatch at 4 waves per SIMD
+    int fused_fp8_place_max_t = 3072;  // moe_layout_dispatch with FP8: a placing dispatch up
+                                       // to this T, moe_layout + the plain dispatch above
     int layout_onepass_max_pairs = 16384;   // moe_layout in one launch up to T * K pairs (top-k <= 8)
     int fused_onepass_max_pairs = 0;        // moe_layout_dispatch as that layout + a plain dispatch
     int fused_small_max_work = 4096;        // moe_layout_dispatch in one launch up to T * K * E

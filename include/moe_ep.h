@@ -180,17 +180,17 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
  * take one launch and need no workspace: one workgroup per token recomputes
  * the routing it needs from the whole index array, a cost that grows with
  * T * K and E. Other batches need ws (moe_layout_workspace_bytes()). With
- * K <= 8 (BF16, or FP8 with H <= 8192) they run the layout's count kernel
- * and then a dispatch in which each workgroup computes its own token's slots
- * from the per-tile token masks while its row loads are in flight, so the
- * separate placement launch of moe_layout() disappears. The offsets and
- * per-tile bases come from
- * workgroup 0 of that dispatch (T <= 4096 and at most four experts per
- * dispatch thread: E <= 512 for BF16, E <= 256 for FP8), which the other
- * workgroups wait for within a bounded time (MOE_STATUS_SYNC_TIMEOUT), or
- * else from one workgroup launched in between. Otherwise (K > 8, or FP8 with
- * H > 8192) the call runs moe_layout() and moe_dispatch(). The workspace
- * holds no state from one call to the next.
+ * K <= 8 (BF16, or FP8 with H <= 8192 and T <= 3072) they run the layout's
+ * count kernel and then a dispatch in which each workgroup computes its own
+ * token's slots from the per-tile token masks while its row loads are in
+ * flight, so the separate placement launch of moe_layout() disappears. The
+ * offsets and per-tile bases come from workgroup 0 of that dispatch
+ * (T <= 4096 and at most four experts per dispatch thread: E <= 512 for
+ * BF16, E <= 256 for FP8), which the other workgroups wait for within a
+ * bounded time (MOE_STATUS_SYNC_TIMEOUT), or else from one workgroup launched
+ * in between. Otherwise (K > 8, or FP8 with H > 8192 or T > 3072) the call
+ * runs moe_layout() and moe_dispatch(). The workspace holds no state from one
+ * call to the next.
  * Source: mori pull request 586, the IntraNodeLL reply in its review thread
  * (single-pass per-token routing, one block per token, copy fused in; latency
  * dominates at small token counts) and its profiling section (routing

@@ -172,6 +172,17 @@ def test_fused_call_reuses_buffers_without_stale_state(moe, orc, T):
         assert torch.equal(D.recv_x[:R].view(torch.int16).cpu(), x.view(torch.int16).cpu()[torch.from_numpy(src).long()])
 
 
+def test_fused_fp8_placing_form():
+    """The fused call's placing FP8 form at every batch size, including those the default
+    routing sends through moe_layout + the plain dispatch, matches the oracle; run in a
+    process of its own so the knob takes effect."""
+    env = dict(os.environ, MOE_EP_FUSED_FP8_PLACE_MAX_T="1000000")
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "fp8_place_child.py")
+    r = subprocess.run([sys.executable, "-u", child], env=env, capture_output=True, text=True, timeout=240)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
 def test_sync_timeout_skips_tokens_cleanly():
     """The placing dispatch's bounded wait for its tile's bases, forced from the host
     (a wait limit of 0 ticks, set in a process of its own): tokens that give up are
