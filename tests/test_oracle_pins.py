@@ -557,6 +557,147 @@ def test_dequant_identity_on_exact_codes(orc):
     np.testing.assert_array_equal(y[0], bits)
 
 
+def e4m3_closed_form(codes):
+    """float64 value of each e4m3fn code, written from the format's definition (not
+    through the oracle): (-1)^s * 2^(e-7) * (1 + m/8), subnormals (e = 0)
+    2^-6 * m/8, and S.1111.111 a NaN."""
+    c = np.asarray(codes, np.int64)
+    s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+    v = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    v = np.where(s == 1, -v, v)
+    return np.where((e == 15) & (m == 7), np.nan, v)
+
+
+def test_dequant_multi_block_closed_form(orc):
+    """Several rows of several 128-blocks, every block with its own scale (none of
+    them 1, most not powers of two): each element is the closed-form value of its
+    code times the scale of ITS row and block, one fp32 multiply, rounded to bf16
+    by torch's CPU cast. A dequant that divided by the scale, or took the scale of
+    another block or row, fails here."""
+    rng = np.random.default_rng(44)
+    R, nb = 5, 6
+    H = nb * 128
+    codes = rng.integers(0, 256, (R, H)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C                      # NaN codes: below
+    scale = (rng.uniform(0.5, 2.0, (R, nb)) * 2.0 ** rng.integers(-14, 8, (R, nb))).astype(np.float32)
+    scale[0, :4] = [np.float32(1) / np.float32(448), 3.0, 0.1, 2.0 ** -7]
+    assert len(np.unique(scale)) == R * nb and not np.any(scale == 1.0)
+    y = orc.dequant_fp8(codes, scale)
+    prod = e4m3_closed_form(codes).astype(np.float32) * np.repeat(scale, 128, axis=1)
+    assert prod.dtype == np.float32                             # one fp32 rounding
+    np.testing.assert_array_equal(y, bf16_bits_of(prod))
+    # rows past R are not written; a NaN code comes back a NaN
+    y3 = orc.dequant_fp8(codes, scale, R=3)
+    np.testing.assert_array_equal(y3[:3], y[:3])
+    assert np.all(y3[3:] == 0)
+    q = codes[:1].copy()
+    q[0, 5], q[0, 300] = 0x7F, 0xFF
+    yn = bf16_to_float(orc.dequant_fp8(q, scale[:1]))
+    assert np.isnan(yn[0, 5]) and np.isnan(yn[0, 300]) and np.isfinite(np.delete(yn[0], [5, 300])).all()
+
+
+def test_fp8_round_trip_error_bound_on_fp8_workload(orc):
+    """Rows of the FP8 workload's input through quantize_row_fp8 and then the
+    oracle's dequant: for every element, with d = decode(q),
+      |y - x| <= 2^-4 |x| + 2^-8 |y|           where |d| >= 2^-6 (normal e4m3)
+      |y - x| <= 2^-10 scale + 2^-8 |y|        where |d| <  2^-6 (subnormal e4m3)
+    (half an e4m3 ulp of x * inv, scaled back; then half a bf16 ulp of the dequant's
+    rounding; the 1 + 2^-23 from inv * scale is covered by a 1e-6 slack). The element
+    of largest |x| in each block comes back bit for bit: it encodes to +-448, and
+    448 * scale rounds back to amax in bf16."""
+    d = si.make_workload("fp8")
+    rows = d["x"][::16][:256]                                   # 256 of the 4096 rows
+    H = rows.shape[1]
+    q = np.zeros_like(rows, dtype=np.uint8)
+    sc = np.zeros((rows.shape[0], H // 128), np.float32)
+    for r in range(rows.shape[0]):
+        q[r], sc[r] = orc.quantize_row_fp8(rows[r])
+    y = bf16_to_float(orc.dequant_fp8(q, sc)).astype(np.float64)
+    x = bf16_to_float(rows).astype(np.float64)
+    dq = e4m3_closed_form(q)
+    s = np.repeat(sc.astype(np.float64), 128, axis=1)
+    err = np.abs(y - x)
+    normal = np.abs(dq) >= 2.0 ** -6
+    bound = np.where(normal, 2.0 ** -4 * np.abs(x), 2.0 ** -10 * s) * (1 + 1e-6) + 2.0 ** -8 * np.abs(y)
+    assert np.all(err <= bound)
+    xb = np.abs(x).reshape(x.shape[0], -1, 128)
+    j = xb.argmax(axis=2)
+    yb, xs = y.reshape(xb.shape), x.reshape(xb.shape)
+    np.testing.assert_array_equal(np.take_along_axis(yb, j[..., None], 2), np.take_along_axis(xs, j[..., None], 2))
+
+
+def _expected_sources(idx, E, G):
+    """Source token of every receive row, from library routines alone: per-expert
+    rows in the order of a stable argsort of the flat pair list; per-group rows from
+    the deduplicated (token, group) pairs, enumerated token-major, stably sorted by
+    group."""
+    T, K = idx.shape
+    src_e = np.argsort(idx.ravel(), kind="stable") // K
+    epg = E // G
+    tg = np.array(sorted({(t, int(e) // epg) for t in range(T) for e in idx[t]}), np.int64).reshape(-1, 2)
+    src_g = tg[np.argsort(tg[:, 1], kind="stable"), 0]
+    return {"expert": src_e, "group": src_g}
+
+
+@pytest.mark.parametrize("T,H,E,G,K", [(60, 512, 32, 4, 4), (33, 384, 12, 12, 3), (40, 256, 16, 1, 5)])
+def test_dispatch_fp8_rows_are_their_sources_quantised(orc, T, H, E, G, K):
+    """Every receive row of the FP8 dispatch, in both layouts, holds exactly the codes
+    and the H/128 scales that quantize_row_fp8 gives for its source token's row, and
+    the token's K weights and indices; the source of each row is found without the
+    oracle's layout."""
+    d = si.make_inputs(T, H, E, K, seed=T + H + K)
+    x = d["x"].copy()
+    x[3, 128:256] = 0                                            # an all-zero block: scale 0
+    L = orc.layout(d["topk_idx"], E, G)
+    src = _expected_sources(d["topk_idx"], E, G)
+    per_tok = [orc.quantize_row_fp8(x[t]) for t in range(T)]
+    for mode in ("expert", "group"):
+        D = orc.dispatch_fp8(L, mode, x, d["topk_w"], d["topk_idx"])
+        assert D["R"] == len(src[mode])
+        for r, t in enumerate(src[mode]):
+            np.testing.assert_array_equal(D["recv_q"][r], per_tok[t][0], err_msg=f"{mode} row {r}")
+            np.testing.assert_array_equal(D["recv_scale"][r].view(np.uint32), per_tok[t][1].view(np.uint32))
+            np.testing.assert_array_equal(D["recv_w"][r], d["topk_w"][t])
+            np.testing.assert_array_equal(D["recv_idx"][r], d["topk_idx"][t])
+
+
+def test_dispatch_fp8_hand_worked_row_lands_in_its_rows(orc, golden_dir):
+    """The hand-worked two-block row (tests/golden/fp8_block_hand.json) as token 1 of
+    three tokens, top-2 over E = 4 experts in G = 2 groups:
+        token 0 -> experts 0, 2;  token 1 -> experts 3, 1;  token 2 -> experts 2, 0.
+    Per expert the rows are expert 0: tokens 0, 2; expert 1: token 1; expert 2:
+    tokens 0, 2; expert 3: token 1, so token 1 owns per-expert rows 2 and 5. Every
+    token reaches both groups (experts 0, 1 are group 0; 2, 3 group 1), so the
+    per-group rows are tokens 0, 1, 2 in group 0 and again in group 1: token 1 owns
+    rows 1 and 4. Those rows carry the hand-worked codes, scale 1 for block A and
+    fp32(1/448) for block B, in that order."""
+    g = json.load(open(os.path.join(golden_dir, "fp8_block_hand.json")))
+    H = 256
+    row = np.zeros(H, np.float32)
+    codes = np.zeros(H, np.uint8)
+    for i, (v, c) in enumerate(g["block_a"]):
+        row[i], codes[i] = v, c
+    for i, (v, c) in enumerate(g["block_b"]):
+        row[128 + i], codes[128 + i] = v, c
+    rng = np.random.default_rng(9)
+    x = bf16_bits_of(np.stack([rng.standard_normal(H).astype(np.float32), row,
+                               rng.standard_normal(H).astype(np.float32)]))
+    idx = np.array([[0, 2], [3, 1], [2, 0]], np.int32)
+    w = np.array([[0.25, 0.75], [0.5, 0.5], [0.125, 0.875]], np.float32)
+    L = orc.layout(idx, 4, 2)
+    scales = np.array([g["block_a_scale"], np.float32(1) / np.float32(448)], np.float32)
+    for mode, rows in (("expert", (2, 5)), ("group", (1, 4))):
+        D = orc.dispatch_fp8(L, mode, x, w, idx)
+        assert D["R"] == 6
+        for r in rows:
+            np.testing.assert_array_equal(D["recv_q"][r], codes, err_msg=f"{mode} row {r}")
+            np.testing.assert_array_equal(D["recv_scale"][r], scales)
+            np.testing.assert_array_equal(D["recv_w"][r], w[1])
+            np.testing.assert_array_equal(D["recv_idx"][r], idx[1])
+        others = [r for r in range(6) if r not in rows]
+        assert not any(np.array_equal(D["recv_q"][r], codes) for r in others)
+
+
 # ------------------------------------------------------------------ combine
 
 @pytest.mark.parametrize("name", ["tiny", "t256"])
