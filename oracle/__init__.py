@@ -5,12 +5,19 @@ this package. It loads `liboracle.so`, built from `oracle.c` with gcc
 (`-O2 -ffp-contract=off`, single thread), and wraps each function for numpy
 arrays. It shares nothing with the HIP library and never imports it.
 
+A second build of the same source, `liboracle_omp.so` (gcc -fopenmp), runs the
+oracle's independent per-token and per-row loops on several threads; it exists
+to time the oracle on every host core and gives the same bits as the canonical
+build (tested). `with oracle.variant("openmp"): ...` routes the calls in the
+block to it; `set_threads(n)` and `threads()` control and report its threads.
+
 Every function follows the plain definition written out in `oracle.c`; see the
 header of that file for the passages of the pages each one follows and for
 the readings taken where the pages are silent.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -22,31 +29,65 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11",
-             "-Wall", "-Wextra"]
+             "-Wall", "-Wextra", "-Wno-unknown-pragmas"]
+# variant -> (library file, extra gcc flags)
+VARIANTS = {"serial": ("liboracle.so", ()), "openmp": ("liboracle_omp.so", ("-fopenmp",))}
 
 STATUS_BAD_INDEX = 1
 STATUS_DUPLICATE = 2
 
 
-def build(force: bool = True, extra_flags=()) -> str:
-    """Compile oracle.c into liboracle.so (gcc, host only)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
-        return _LIB
-    tmp = _LIB + f".tmp{os.getpid()}"
-    cmd = ["gcc", *GCC_FLAGS, *extra_flags, "-o", tmp, _SRC, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+def _lib_path(v: str) -> str:
+    return _LIB if v == "serial" else os.path.join(_HERE, VARIANTS[v][0])
 
 
-_lib = None
+def build(force: bool = True, extra_flags=(), variant: str | None = None) -> str:
+    """Compile oracle.c (gcc, host only): the canonical single-thread liboracle.so and,
+    with variant=None, also the OpenMP build; returns the path of the canonical one
+    (or of the one variant asked for)."""
+    for v in ([variant] if variant else list(VARIANTS)):
+        path = _lib_path(v)
+        if not force and os.path.exists(path) and os.path.getmtime(path) >= os.path.getmtime(_SRC):
+            continue
+        tmp = path + f".tmp{os.getpid()}"
+        cmd = ["gcc", *GCC_FLAGS, *VARIANTS[v][1], *extra_flags, "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, path)
+    return _lib_path(variant or "serial")
+
+
+_libs: dict = {}
+_active = "serial"
+
+
+@contextlib.contextmanager
+def variant(name: str):
+    """Route the oracle calls made inside the block to the build `name` ("serial",
+    the canonical one, or "openmp")."""
+    global _active
+    if name not in VARIANTS:
+        raise ValueError(name)
+    old, _active = _active, name
+    try:
+        yield
+    finally:
+        _active = old
+
+
+def threads() -> int:
+    """Threads the active build's parallel loops use (1 for the canonical build)."""
+    return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
 
 
 def _load():
-    global _lib
-    if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB)
+    v = _active
+    if v not in _libs:
+        build(force=False, variant=v)
+        lib = ctypes.CDLL(_lib_path(v))
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int, ctypes.c_int64
         lib.oracle_layout.argtypes = [i32, i32, i32, i32, P] + [P] * 10
@@ -77,8 +118,12 @@ def _load():
         lib.oracle_regroup_rows.restype = None
         lib.oracle_cast_transpose_fp8.argtypes = [i32, i32, P, P, P, P, P, P, P]
         lib.oracle_cast_transpose_fp8.restype = None
-        _lib = lib
-    return _lib
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = i32
+        lib.oracle_set_threads.argtypes = [i32]
+        lib.oracle_set_threads.restype = None
+        _libs[v] = lib
+    return _libs[v]
 
 
 def _p(a: np.ndarray):

@@ -8,8 +8,15 @@
  * benchmark's CPU-baseline leg may load it; the product path never does. It
  * shares no code, header, table or helper with the HIP library.
  *
- * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no OpenMP, no fast-math), so
- * every float operation below is one IEEE binary32 operation in the order written.
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math), so every float
+ * operation below is one IEEE binary32 operation in the order written. The
+ * canonical build has no OpenMP: the `omp` pragmas below are ignored and it runs
+ * on one thread. A second build of this same file with -fopenmp (used only to
+ * time the oracle on every host core) runs the loops marked `omp parallel for`
+ * on several threads: each marks a loop over tokens or receive rows whose
+ * iterations write disjoint outputs from inputs no iteration writes, with the
+ * same arithmetic per element, so both builds give the same bits (a test
+ * checks it). The cursor walks that assign slots stay serial in both.
  *
  * Sources (pages of the method):
  *  - "perf(ep): optimize IntraNode dispatch kernel for MI350X" (ROCm/mori pull
@@ -45,6 +52,9 @@
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -131,6 +141,7 @@ int oracle_layout(int T, int K, int E, int G, const int32_t *idx,
     int32_t *gcur = (int32_t *)calloc((size_t)G + 1, sizeof(int32_t));
 
     /* validity: in range, and not a repeat of an earlier k of the same token */
+#pragma omp parallel for reduction(| : status)
     for (int t = 0; t < T; ++t)
         for (int k = 0; k < K; ++k) {
             int e = idx[(size_t)t * K + k];
@@ -163,6 +174,7 @@ int oracle_layout(int T, int K, int E, int G, const int32_t *idx,
         }
 
     /* groups: which groups each token reaches (each group once per token) */
+#pragma omp parallel for
     for (int t = 0; t < T; ++t) {
         uint32_t m = 0;
         for (int k = 0; k < K; ++k)
@@ -187,6 +199,7 @@ int oracle_layout(int T, int K, int E, int G, const int32_t *idx,
                 slot_tg[q] = -1;
             }
         }
+#pragma omp parallel for
     for (int t = 0; t < T; ++t)
         for (int k = 0; k < K; ++k) {
             size_t p = (size_t)t * K + k;
@@ -213,6 +226,7 @@ void oracle_dispatch_bf16(int mode, int K, int H, int64_t R, const int32_t *recv
                           const uint16_t *x, const float *topk_w, const int32_t *topk_idx,
                           uint16_t *recv_x, float *recv_w, int32_t *recv_idx)
 {
+#pragma omp parallel for
     for (int64_t r = 0; r < R; ++r) {
         int t = src_token(mode, K, recv_src, r);
         for (int i = 0; i < H; ++i) recv_x[r * H + i] = x[(int64_t)t * H + i];
@@ -253,8 +267,10 @@ void oracle_dispatch_fp8(int mode, int T, int K, int H, int64_t R, const int32_t
     int nb = H / 128;
     uint8_t *qt = (uint8_t *)malloc((size_t)T * H + 1);
     float *st = (float *)malloc(((size_t)T * nb + 1) * sizeof(float));
+#pragma omp parallel for
     for (int t = 0; t < T; ++t)
         oracle_quantize_row_fp8(H, x + (int64_t)t * H, qt + (int64_t)t * H, st + (int64_t)t * nb);
+#pragma omp parallel for
     for (int64_t r = 0; r < R; ++r) {
         int t = src_token(mode, K, recv_src, r);
         memcpy(recv_q + r * H, qt + (int64_t)t * H, (size_t)H);
@@ -271,6 +287,7 @@ void oracle_dispatch_fp8(int mode, int T, int K, int H, int64_t R, const int32_t
 void oracle_dequant_fp8(int64_t R, int H, const uint8_t *q, const float *scale, uint16_t *y)
 {
     int nb = H / 128;
+#pragma omp parallel for
     for (int64_t r = 0; r < R; ++r)
         for (int i = 0; i < H; ++i) {
             float v = oracle_e4m3_to_f32(q[r * H + i]) * scale[r * nb + i / 128];
@@ -287,6 +304,7 @@ void oracle_dequant_fp8(int64_t R, int H, const uint8_t *q, const float *scale, 
 void oracle_combine(int T, int K, int H, const int32_t *slot, const uint16_t *y,
                     const float *topk_w, uint16_t *out)
 {
+#pragma omp parallel for
     for (int t = 0; t < T; ++t)
         for (int i = 0; i < H; ++i) {
             float acc = -0.0f;
@@ -323,6 +341,7 @@ void oracle_regroup_rows(int64_t R, int64_t row_bytes, const int32_t *recv_src_e
 {
     const unsigned char *in = (const unsigned char *)in_rows;
     unsigned char *out = (unsigned char *)out_rows;
+#pragma omp parallel for
     for (int64_t r = 0; r < R; ++r) {
         int32_t p = recv_src_e[r];
         int32_t s = slot_g[p];
@@ -363,4 +382,24 @@ void oracle_cast_transpose_fp8(int E, int H, const int32_t *expert_offset, const
         po += np;
     }
     pad_offset[E] = (int32_t)po;
+}
+
+/* ---------------------------------------------------------------- threads
+ * Threads the parallel loops may use: 1 in the canonical build. */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
 }
