@@ -25,11 +25,12 @@ import os
 import torch
 
 __all__ = [
-    "MoeError", "Layout", "Dispatched", "moe_layout", "moe_dispatch", "moe_combine",
+    "MoeError", "MoeDataError", "Layout", "Dispatched", "moe_layout", "moe_dispatch", "moe_combine",
     "moe_layout_dispatch", "moe_regroup", "moe_cast_transpose_fp8", "CastTransposed",
-    "moe_fp8_dequant", "moe_ref_copy", "recv_rows_bound", "layout_workspace_bytes",
+    "moe_fp8_dequant", "moe_ref_copy", "moe_ref_mix", "recv_rows_bound", "layout_workspace_bytes",
     "library_path", "MODE_EXPERT", "MODE_GROUP", "DTYPE_BF16", "DTYPE_FP8",
-    "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS", "STATUS_SYNC_TIMEOUT",
+    "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS", "STATUS_SYNC_FALLBACK",
+    "STATUS_ERRORS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +39,8 @@ _LIB_PATH = os.environ.get("MOE_EP_LIB") or os.path.join(_PKG, "libmoe_ep.so")
 
 MODE_EXPERT, MODE_GROUP = 0, 1
 DTYPE_BF16, DTYPE_FP8 = 0, 1
-STATUS_BAD_INDEX, STATUS_DUPLICATE, STATUS_Y_ROWS, STATUS_SYNC_TIMEOUT = 1, 2, 4, 8
+STATUS_BAD_INDEX, STATUS_DUPLICATE, STATUS_Y_ROWS, STATUS_SYNC_FALLBACK = 1, 2, 4, 8
+STATUS_ERRORS = STATUS_BAD_INDEX | STATUS_DUPLICATE | STATUS_Y_ROWS
 _MODES = {"expert": MODE_EXPERT, "group": MODE_GROUP, MODE_EXPERT: MODE_EXPERT, MODE_GROUP: MODE_GROUP}
 _DTYPES = {"bf16": DTYPE_BF16, "fp8": DTYPE_FP8, DTYPE_BF16: DTYPE_BF16, DTYPE_FP8: DTYPE_FP8}
 
@@ -74,6 +76,7 @@ def _load_library() -> ctypes.CDLL:
         "moe_cast_transpose_fp8": (i32, [LP, i32, _P, i64, _P, _P, _P, i64, _P, _P, _P]),
         "moe_fp8_dequant": (i32, [LP, i32, i32, _P, _P, _P, i64, _P]),
         "moe_ref_copy": (i32, [_P, _P, i64, _P]),
+        "moe_ref_mix": (i32, [_P, _P, i64, i64, i32, i32, _P]),
         "moe_status_string": (ctypes.c_char_p, [i32]),
     }
     for name, (res, args) in sig.items():
@@ -94,6 +97,17 @@ class MoeError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
         super().__init__(f"{where}: {_lib.moe_status_string(code).decode()} (code {code})")
+
+
+class MoeDataError(RuntimeError):
+    """The device status word reports bad input (see Layout.check_status)."""
+
+    def __init__(self, status: int):
+        self.status = status
+        why = [n for b, n in ((STATUS_BAD_INDEX, "expert index out of range"),
+                              (STATUS_DUPLICATE, "expert repeated within a token"),
+                              (STATUS_Y_ROWS, "combine slot past the rows of y")) if status & b]
+        super().__init__(f"layout status {status:#x}: " + ", ".join(why))
 
 
 def _check(rc: int, where: str) -> None:
@@ -235,6 +249,17 @@ class Layout:
 
     def slots(self, mode="expert") -> torch.Tensor:
         return self.slot_e if _mode(mode) == MODE_EXPERT else self.slot_g
+
+    def check_status(self) -> int:
+        """Read the device status word (this waits for the work queued before it on the
+        current stream) and raise MoeDataError if an error bit is set: an expert index
+        out of range, an expert repeated within a token, or a combine slot past the rows
+        of y. Returns the word, which may also hold the diagnostic STATUS_SYNC_FALLBACK
+        (results exact). The calls themselves stay asynchronous and never read it."""
+        st = int(self.status.item())
+        if st & STATUS_ERRORS:
+            raise MoeDataError(st)
+        return st
 
 
 def moe_layout(topk_idx: torch.Tensor, E: int, G: int, *, out: Layout | None = None,
@@ -451,3 +476,16 @@ def moe_ref_copy(dst: torch.Tensor, src: torch.Tensor, nbytes: int | None = None
                                                                       dst.numel() * dst.element_size()):
         raise ValueError("moe_ref_copy: contiguous src and dst of at least nbytes each")
     _check(_lib.moe_ref_copy(_ptr(dst), _ptr(src), n, _stream(stream)), "moe_ref_copy")
+
+
+def moe_ref_mix(dst: torch.Tensor, src: torch.Tensor, row_bytes: int, nr: int, nw: int,
+                stream=None) -> int:
+    """Read/write-mix reference (measurement aid, not part of the method): nr rows of src
+    read per nw rows of dst written, rows of row_bytes bytes, as many units as both
+    buffers hold; returns the number of units."""
+    nbs, nbd = src.numel() * src.element_size(), dst.numel() * dst.element_size()
+    if not (src.is_contiguous() and dst.is_contiguous()) or row_bytes <= 0:
+        raise ValueError("moe_ref_mix: contiguous src and dst and a positive row size")
+    units = min(nbs // (row_bytes * nr), nbd // (row_bytes * nw))
+    _check(_lib.moe_ref_mix(_ptr(dst), _ptr(src), row_bytes, units, nr, nw, _stream(stream)), "moe_ref_mix")
+    return int(units)

@@ -221,6 +221,7 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
     pa.ntiles = moe::layout_tiles(L->T);
     pa.finalize = fin_in_dispatch ? 1 : 0;
     pa.wait_ticks = moe::tuning().base_wait_ticks < 0 ? 0 : (uint64_t)moe::tuning().base_wait_ticks;
+    pa.self_bases = moe::tuning().base_wait_ticks < 0 ? 1 : 0;
     pa.L = P;
     pa.mode = mode == MOE_MODE_EXPERT ? 0 : 1;
     e = fp8 ? moe::launch_dispatch_fp8(x, L->T, H, L->K, nslot, nullptr, topk_w, topk_idx, recv_x, recv_scale,
@@ -323,6 +324,21 @@ int moe_ref_copy(void *dst, const void *src, int64_t bytes, void *stream)
     if (!dst || !src) return MOE_ERR_NULL_PTR;
     if (!aligned16(dst) || !aligned16(src)) return MOE_ERR_MISALIGNED;
     hipError_t e = moe::launch_ref_copy(dst, src, bytes, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+int moe_ref_mix(void *dst, const void *src, int64_t row_bytes, int64_t units, int nr, int nw,
+                void *stream)
+{
+    auto pow2_le8 = [](int v) { return v == 1 || v == 2 || v == 4 || v == 8; };
+    if (!pow2_le8(nr) || !pow2_le8(nw) || (nr > 1 && nw > 1)) return MOE_ERR_BAD_MODE;
+    if (row_bytes <= 0 || row_bytes % 16 != 0 || row_bytes / 16 > (1 << 24) || units < 0 ||
+        units >= ((int64_t)1 << 31))
+        return MOE_ERR_BAD_SHAPE;
+    if (units == 0) return MOE_OK;
+    if (!dst || !src) return MOE_ERR_NULL_PTR;
+    if (!aligned16(dst) || !aligned16(src)) return MOE_ERR_MISALIGNED;
+    hipError_t e = moe::launch_ref_mix(dst, src, row_bytes, units, nr, nw, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 

@@ -43,12 +43,6 @@ constexpr int kCtEpt = (kMaxE + kCtBS - 1) / kCtBS;   // experts per thread in t
 // (2048 / Q) columns x (Q + 1) words, plus the c/8 shift
 constexpr int kCtLdsWords = 512 * 5 + 64;
 
-template <bool HI>
-__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
-{
-    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-}
-
 
 // Exclusive scan of two values over the 256 threads, with both totals, and
 // the OR of a flag over the threads (returned).
@@ -199,12 +193,8 @@ __global__ __launch_bounds__(kCtBS) void cast_transpose_kernel(
             }
 #pragma unroll
             for (int m = 0; m < 8; ++m) a = amax_step(a, f[m]);
-            int p0 = cvt_pk_e4m3<false>(sat448(f[0] * s), sat448(f[1] * s), 0);
-            p0 = cvt_pk_e4m3<true>(sat448(f[2] * s), sat448(f[3] * s), p0);
-            int p1 = cvt_pk_e4m3<false>(sat448(f[4] * s), sat448(f[5] * s), 0);
-            p1 = cvt_pk_e4m3<true>(sat448(f[6] * s), sat448(f[7] * s), p1);
-            p0 = (int)e4m3_nan_canon((uint32_t)p0);
-            p1 = (int)e4m3_nan_canon((uint32_t)p1);
+            const int p0 = (int)e4m3x4(f[0], f[1], f[2], f[3], s);
+            const int p1 = (int)e4m3x4(f[4], f[5], f[6], f[7], s);
             b[i][0] = (uint32_t)p0;
             b[i][1] = (uint32_t)p1;
             const int row = 4 * q + i;

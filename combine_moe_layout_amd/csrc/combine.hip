@@ -238,6 +238,29 @@ __global__ __launch_bounds__(256) void ref_copy_kernel(const u32x4 *__restrict__
         dst[i] = src[i];
 }
 
+// Measurement aid: the read/write mix of a combine (NR rows read per row
+// written) or of a dispatch (one row read, NW written) over contiguous rows,
+// with the same cache policy (non-temporal loads, plain stores) and shape (one
+// workgroup per unit, one 16-byte vector per lane and pass). Unit u reads rows
+// u * NR .. u * NR + NR - 1 of src, all NR loads in flight, and writes their
+// XOR to rows u * NW .. u * NW + NW - 1 of dst.
+template <int NR, int NW>
+__global__ __launch_bounds__(kCombineMaxBS) void ref_mix_kernel(const u32x4 *__restrict__ src,
+                                                                u32x4 *__restrict__ dst, int nvec)
+{
+    const size_t u = blockIdx.x;
+    for (int j = threadIdx.x; j < nvec; j += blockDim.x) {
+        u32x4 v[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) v[r] = load16<true>(src + (u * NR + r) * nvec + j);
+        u32x4 acc = v[0];
+#pragma unroll
+        for (int r = 1; r < NR; ++r) acc ^= v[r];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) store16<false>(dst + (u * NW + w) * nvec + j, acc);
+    }
+}
+
 inline int iters_for(int n, int bs)
 {
     const int it = (n + bs - 1) / bs;
@@ -245,6 +268,20 @@ inline int iters_for(int n, int bs)
 }
 
 }  // namespace
+
+hipError_t launch_ref_mix(void *dst, const void *src, int64_t row_bytes, int64_t units, int nr, int nw,
+                          hipStream_t stream)
+{
+    const int nvec = (int)(row_bytes / 16);
+    int bs = (nvec + kWave - 1) / kWave * kWave;
+    if (bs > kCombineMaxBS) bs = kCombineMaxBS;
+    void (*fn)(const u32x4 *, u32x4 *, int) = nullptr;
+    if (nr == 1 && nw == 1) fn = ref_mix_kernel<1, 1>;
+    else if (nw == 1) fn = nr == 2 ? ref_mix_kernel<2, 1> : (nr == 4 ? ref_mix_kernel<4, 1> : ref_mix_kernel<8, 1>);
+    else fn = nw == 2 ? ref_mix_kernel<1, 2> : (nw == 4 ? ref_mix_kernel<1, 4> : ref_mix_kernel<1, 8>);
+    hipLaunchKernelGGL(fn, dim3((unsigned)units), dim3(bs), 0, stream, (const u32x4 *)src, (u32x4 *)dst, nvec);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const void *y, int64_t y_rows, int T, int H, int K, const int32_t *slot,
                           bool rows_repeat, const float *topk_w, void *out, int32_t *status,

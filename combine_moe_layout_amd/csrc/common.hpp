@@ -79,4 +79,52 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane)
     return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Group of expert x, floor(x / epg), without a division: a multiply-high by
+// magic = floor(2^32 / epg) + 1 (for x < 2^16 the product's error is below
+// 2^-16 and cannot cross an integer), or x itself when epg = 1 (magic = 0;
+// the host computes magic with group_magic()).
+__device__ __forceinline__ int group_of(int x, uint32_t magic)
+{
+    return magic == 0 ? x : (int)__umulhi((uint32_t)x, magic);
+}
+
+// Four values times s -> four e4m3fn codes in one word (value 0 in the low
+// byte): saturated to +-448 (sat448), converted in pairs by gfx950's packed
+// conversion (round to nearest even), the NaN byte mapped to 0x7F.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d, float s)
+{
+    int p = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a * s), sat448(b * s), 0, false);
+    p = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c * s), sat448(d * s), p, true);
+    return e4m3_nan_canon((uint32_t)p);
+}
+
+// One lane's 16-element chunk of a bf16 row (a, b: 16 bf16, in order) quantised
+// with one fp32 scale per 1x128 block, the block being 8 consecutive lanes of
+// the wave (every lane of the wave must call this together): the block's amax
+// (NaNs passed over, see amax_step) by three xor-shuffles, scale = amax / 448
+// and inv = 448 / amax (0 when amax = 0; correctly rounded divisions, the
+// library is built with -fhip-fp32-correctly-rounded-divide-sqrt), and the 16
+// codes of x * inv.
+__device__ __forceinline__ void quantize16(u32x4 a, u32x4 b, u32x4 &q, float &scale)
+{
+    float f[16];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f[2 * m] = bf16_lo(a[m]);
+        f[2 * m + 1] = bf16_hi(a[m]);
+        f[8 + 2 * m] = bf16_lo(b[m]);
+        f[8 + 2 * m + 1] = bf16_hi(b[m]);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) amax = amax_step(amax, f[m]);
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    amax = fmaxf(amax, __shfl_xor(amax, 4));
+    scale = amax / 448.f;
+    const float inv = amax > 0.f ? 448.f / amax : 0.f;
+    q = u32x4{e4m3x4(f[0], f[1], f[2], f[3], inv), e4m3x4(f[4], f[5], f[6], f[7], inv),
+              e4m3x4(f[8], f[9], f[10], f[11], inv), e4m3x4(f[12], f[13], f[14], f[15], inv)};
+}
+
 }  // namespace moe

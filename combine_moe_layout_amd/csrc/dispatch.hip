@@ -108,45 +108,6 @@ __global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_kernel(
     }
 }
 
-// Two packed e4m3 values into the low (HI = false) or high 16 bits of `old`.
-template <bool HI>
-__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
-{
-    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-}
-
-
-// One lane's 16-element chunk (a, b: 16 bf16): the amax of its 128-block over
-// the block's 8 lanes (8 consecutive lanes of a wave; every lane of the wave
-// must call this together), the block's scale, and the 16 packed e4m3 codes.
-__device__ __forceinline__ void quantize16(u32x4 a, u32x4 b, u32x4 &q, float &scale)
-{
-    float f[16];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        f[2 * m] = bf16_lo(a[m]);
-        f[2 * m + 1] = bf16_hi(a[m]);
-        f[8 + 2 * m] = bf16_lo(b[m]);
-        f[8 + 2 * m + 1] = bf16_hi(b[m]);
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) amax = amax_step(amax, f[m]);
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    amax = fmaxf(amax, __shfl_xor(amax, 4));
-    scale = amax / 448.f;
-    const float inv = amax > 0.f ? 448.f / amax : 0.f;
-    int w[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        int p = cvt_pk_e4m3<false>(sat448(f[4 * m] * inv), sat448(f[4 * m + 1] * inv), 0);
-        p = cvt_pk_e4m3<true>(sat448(f[4 * m + 2] * inv), sat448(f[4 * m + 3] * inv), p);
-        w[m] = (int)e4m3_nan_canon((uint32_t)p);
-    }
-    q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
-}
-
 // One 16-element chunk per lane per pass; the workgroup has as many lanes as
 // the row has chunks (rounded up to whole waves, at most kFp8MaxBS), so a
 // lane holds one chunk's state and occupancy stays high.

@@ -26,17 +26,6 @@ constexpr int kFusedWaves = kFusedBS / kWave;
 constexpr int kMaxG = 32;
 constexpr int kMaxK = 32;
 
-__device__ __forceinline__ int group_of(int x, uint32_t magic)
-{
-    return magic == 0 ? x : (int)__umulhi((uint32_t)x, magic);
-}
-
-template <bool HI>
-__device__ __forceinline__ int cvt_pk_e4m3(float a, float b, int old)
-{
-    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
-}
-
 
 // LDS layout (ints): idx[T*K] | vmask[T] | gmask[T] | cnt[E] | off[E+1] | gcnt[G] | goff[G+1]
 //                    | rank[K] | grank[G] | dst[max(K, G)] | misc
@@ -261,30 +250,9 @@ __global__ __launch_bounds__(kFusedBS) void fused_layout_dispatch_kernel(
                 a = __builtin_nontemporal_load(src + 2 * j);
                 b = __builtin_nontemporal_load(src + 2 * j + 1);
             }
-            float f[16];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f[2 * m] = bf16_lo(a[m]);
-                f[2 * m + 1] = bf16_hi(a[m]);
-                f[8 + 2 * m] = bf16_lo(b[m]);
-                f[8 + 2 * m + 1] = bf16_hi(b[m]);
-            }
-            float amax = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) amax = amax_step(amax, f[m]);
-            amax = fmaxf(amax, __shfl_xor(amax, 1));
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
-            amax = fmaxf(amax, __shfl_xor(amax, 4));
-            const float scale = amax / 448.f;
-            const float inv = amax > 0.f ? 448.f / amax : 0.f;
-            int w[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                int p = cvt_pk_e4m3<false>(sat448(f[4 * m] * inv), sat448(f[4 * m + 1] * inv), 0);
-                p = cvt_pk_e4m3<true>(sat448(f[4 * m + 2] * inv), sat448(f[4 * m + 3] * inv), p);
-                w[m] = (int)e4m3_nan_canon((uint32_t)p);
-            }
-            const u32x4 q = u32x4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+            u32x4 q;
+            float scale;
+            quantize16(a, b, q, scale);
             if (in) {
                 for (int d = 0; d < nslot; ++d) {
                     const int s = s_dst[d];
@@ -322,8 +290,7 @@ hipError_t launch_layout_dispatch(const int32_t *idx, int T, int K, int E, int G
                                   void *recv_x, float *recv_scale, float *recv_w, int32_t *recv_idx,
                                   hipStream_t stream)
 {
-    const int epg = E / G;
-    const uint32_t gmagic = epg == 1 ? 0u : (uint32_t)((1ull << 32) / (unsigned)epg) + 1u;
+    const uint32_t gmagic = group_magic(E, G);
     static const hipError_t lds_ok = hipFuncSetAttribute(
         reinterpret_cast<const void *>(fused_layout_dispatch_kernel),
         hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);

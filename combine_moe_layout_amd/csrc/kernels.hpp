@@ -85,6 +85,7 @@ struct PlaceArgs {
     int ntiles;
     int finalize;              // 1: workgroup 0 computes the bases, counts, offsets and status
     uint64_t wait_ticks;       // longest wait for a tile's bases (constant 100 MHz clock)
+    int self_bases;            // 1: every token computes its bases from the table (no wait; tests)
     LayoutPtrs L;
     int mode;   // destinations: slot_e (0) or slot_tg (1)
 };
@@ -114,8 +115,9 @@ struct Tuning {
     int fused_onepass_max_pairs = 0;        // moe_layout_dispatch as that layout + a plain dispatch
     int fused_small_max_work = 4096;        // moe_layout_dispatch in one launch up to T * K * E
     long long base_wait_ticks = 20000000;   // placing dispatch: longest wait for a tile's bases
-                                            // (0.2 s at 100 MHz; a tiny value forces the timeout
-                                            // path in tests)
+                                            // (0.2 s at 100 MHz) before a token computes them
+                                            // itself; 0 makes most tokens do so, -1 every token
+                                            // (tests of that path)
     int fused_finalize = 2;                 // placing dispatch: 0 the finalize kernel, 1 its
                                             // workgroup 0 (bf16), 2 workgroup 0 (bf16 and FP8)
     int fused_finalize_rounds = 4;          // ... for E up to this many columns per thread
@@ -150,6 +152,9 @@ hipError_t launch_fp8_dequant(const void *q, const float *scale, void *y, int64_
                               const int32_t *nrows, hipStream_t stream);
 
 hipError_t launch_ref_copy(void *dst, const void *src, int64_t bytes, hipStream_t stream);
+// (nr, nw): (1, 1), (2|4|8, 1) or (1, 2|4|8), checked by the caller.
+hipError_t launch_ref_mix(void *dst, const void *src, int64_t row_bytes, int64_t units, int nr, int nw,
+                          hipStream_t stream);
 
 // Receive-side regroup: per-group rows -> per-expert rows (row_bytes % 16 == 0).
 hipError_t launch_regroup(const void *in_rows, int row_bytes, const float *in_scale, int nscale,

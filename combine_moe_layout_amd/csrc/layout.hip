@@ -52,14 +52,6 @@ constexpr int kWaves = kLayoutTile / kWave;   // 4
 constexpr int kMaxG = 32;
 constexpr int kMaxEChunks = (1024 + kLayoutTile - 1) / kLayoutTile;   // E <= 1024
 
-// Group of expert x, floor(x / epg), without a division: a multiply-high by
-// magic = floor(2^32 / epg) + 1 (for x < 2^16 the product's error is below
-// 2^-16 and cannot cross an integer), or x itself when epg = 1.
-__device__ __forceinline__ int group_of(int x, uint32_t magic)
-{
-    return magic == 0 ? x : (int)__umulhi((uint32_t)x, magic);
-}
-
 // A token's K expert indices, loaded into registers at kernel entry so the
 // loads overlap other work. The loads are unconditional, from clamped in-range
 // addresses (T >= 1), so they issue back to back with no branches; mask_row

@@ -20,8 +20,10 @@
 // loads of those words, no flag and no state that outlives the call. Workgroup
 // 0 waits for nothing, and is the first workgroup dispatched; a wait is still
 // bounded (P.wait_ticks of the constant 100 MHz clock, 0.2 s by default,
-// against the few µs it takes), after which the token is skipped and
-// MOE_STATUS_SYNC_TIMEOUT is set, so no wave can wait forever.
+// against the few µs it takes). A wave that waited that long computes its
+// token's bases itself from the count table (self_bases: a few hundred loads,
+// exact) and sets the diagnostic bit MOE_STATUS_SYNC_FALLBACK, so no wave waits
+// forever and a late workgroup 0 costs time, never results.
 #pragma once
 
 #include "moe_ep.h"
@@ -30,11 +32,6 @@
 #include "kernels.hpp"
 
 namespace moe {
-
-__device__ __forceinline__ int place_group_of(int x, uint32_t magic)
-{
-    return magic == 0 ? x : (int)__umulhi((uint32_t)x, magic);
-}
 
 // The rank of token lane `l` of wave `w` among a tile's tokens whose masks
 // are words q[0..3] (32-bit halves): tokens of earlier waves, then of earlier
@@ -180,6 +177,55 @@ __device__ void finalize_role(const PlaceArgs &P)
     }
 }
 
+// The bases of this wave's token from the count table alone (what workgroup 0
+// or the finalize kernel writes): lane k with a valid expert e gets be = the
+// expert's offset (the totals of every column before e, over all tiles) plus
+// the counts of e in the tiles before `tile`; lane g < G gets bg likewise for
+// group g. Lane j of the wave first totals the expert columns of its chunk
+// [j * cpl, (j + 1) * cpl); a scan over the lanes gives each chunk's offset;
+// lane k then adds the columns of e's chunk before e. Every lane of the wave
+// calls this together (shuffles).
+__device__ __forceinline__ void self_bases(const PlaceArgs &P, int tile, bool valid, int e, bool hg, int &be,
+                                        int &bg)
+{
+    const int lane = threadIdx.x % kWave;
+    const int E = P.E, G = P.G, nt = P.ntiles, rows = E + G + 1;
+    const int32_t *tab = P.table;
+    const int cpl = (E + kWave - 1) / kWave;
+    const int c0 = lane * cpl, c1 = min(c0 + cpl, E);
+    int tot = 0;
+    for (int c = c0; c < c1; ++c)
+        for (int b = 0; b < nt; ++b) tot += tab[(size_t)b * rows + c];
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    const int owner = valid ? e / cpl : 0;
+    int x = __shfl(incl - tot, owner);
+    if (valid) {
+        for (int c = owner * cpl; c < e; ++c)
+            for (int b = 0; b < nt; ++b) x += tab[(size_t)b * rows + c];
+        for (int b = 0; b < tile; ++b) x += tab[(size_t)b * rows + e];
+        be = x;
+    }
+    int gt = 0;
+    if (lane < G)
+        for (int b = 0; b < nt; ++b) gt += tab[(size_t)b * rows + E + lane];
+    int gincl = gt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(gincl, o);
+        if (lane >= o) gincl += y;
+    }
+    if (hg) {
+        int y = gincl - gt;
+        for (int b = 0; b < tile; ++b) y += tab[(size_t)b * rows + E + lane];
+        bg = y;
+    }
+}
+
 __device__ __forceinline__ void place_token(const PlaceArgs &P, int t, int K, int32_t *dst)
 {
     if (threadIdx.x < kWave) {
@@ -195,7 +241,7 @@ __device__ __forceinline__ void place_token(const PlaceArgs &P, int t, int K, in
             rep = rep || (j < lane && ej == e);
         }
         const bool valid = mine && (unsigned)e < (unsigned)E && !rep;
-        const int g = valid ? place_group_of(e, P.gmagic) : 0;
+        const int g = valid ? group_of(e, P.gmagic) : 0;
         // the groups the token reaches, on every lane
         uint32_t gm = valid ? 1u << g : 0u;
 #pragma unroll
@@ -206,21 +252,22 @@ __device__ __forceinline__ void place_token(const PlaceArgs &P, int t, int K, in
         const int rg = hg ? place_rank(P.gwords + ((size_t)tile * G + lane) * 8, w, l) : 0;
         int32_t *tb = P.bases + (size_t)tile * (E + G);
         int be = 0, bg = 0;
-        bool ok = true;
+        // (wall_clock64 is a scalar read, so the time test and `ok` are wave-uniform)
+        bool ok = !P.self_bases;
         const uint64_t t0 = wall_clock64();
-        for (;;) {
+        while (ok) {
             if (valid) be = base_load(tb + e);
             if (hg) bg = base_load(tb + E + lane);
             if (__all(be >= 0 && bg >= 0)) break;
-            if (wall_clock64() - t0 > P.wait_ticks) {
-                ok = false;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
+            if (wall_clock64() - t0 > P.wait_ticks) ok = false;
+            else __builtin_amdgcn_s_sleep(2);
         }
-        if (!ok && lane == 0) atomicOr(P.L.status, MOE_STATUS_SYNC_TIMEOUT);
-        const int se = valid && ok ? be + re : -1;
-        const int sgl = hg && ok ? bg + rg : -1;   // lane g < G: the token's row in group g, or -1
+        if (!ok) {
+            self_bases(P, tile, valid, e, hg, be, bg);
+            if (lane == 0) atomicOr(P.L.status, MOE_STATUS_SYNC_FALLBACK);
+        }
+        const int se = valid ? be + re : -1;
+        const int sgl = hg ? bg + rg : -1;   // lane g < G: the token's row in group g, or -1
         const int sg = __shfl(sgl, g);
         // (the receive lists hold T*K and T*min(K, G) entries; T = the grid)
         const int64_t T = gridDim.x;

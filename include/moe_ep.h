@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define MOE_EP_ABI_VERSION 2
+#define MOE_EP_ABI_VERSION 3
 
 /* Limits checked at the boundary. */
 #define MOE_MAX_EXPERTS 1024 /* E */
@@ -55,8 +55,12 @@ enum moe_error {
 #define MOE_STATUS_BAD_INDEX 1 /* some topk_idx entry outside [0, E) */
 #define MOE_STATUS_DUPLICATE 2 /* some token lists one expert twice */
 #define MOE_STATUS_Y_ROWS 4    /* combine met a slot >= the rows of y */
-#define MOE_STATUS_SYNC_TIMEOUT 8 /* moe_layout_dispatch: a token's workgroup gave up waiting
-                                     (0.2 s) for its tile's bases and skipped the token */
+#define MOE_STATUS_SYNC_FALLBACK 8 /* diagnostic, not an error: in moe_layout_dispatch a
+                                      token's workgroup waited longer than its limit (0.2 s)
+                                      for its tile's bases and computed them itself from the
+                                      count table; every result is still exact */
+/* The bits that mark bad input or output that cannot be trusted. */
+#define MOE_STATUS_ERRORS (MOE_STATUS_BAD_INDEX | MOE_STATUS_DUPLICATE | MOE_STATUS_Y_ROWS)
 
 /* Receive-buffer layouts.
  * EXPERT: one row per valid (token, k) pair, rows ordered by expert, then
@@ -125,12 +129,24 @@ typedef struct moe_layout_t {
  * error bits and, for K <= 8, each tile's token-by-expert bit masks (about
  * T * E / 8 bytes); its contents need no initialisation and are dead after
  * the call.
- * Returns MOE_ERR_BAD_SHAPE for sizes outside the limits. */
+ * Returns MOE_ERR_BAD_SHAPE for sizes outside the limits.
+ * Source: the per-destination counts of mori pull request 586 (the per-block
+ * count, reserved base and running index its launch-geometry table sizes),
+ * here one row per tile of tokens; the caller allocates it once at the size
+ * this query gives, as DeepEP pull request 347 ("Feature/sm free normal
+ * kernel", Design, RDMA buffer management) has callers size their buffer with
+ * a size-hint function, and as the challenge write-up, section 3.1
+ * ("Persistent Buffer Reuse"), preallocates for the largest problem. */
 int moe_layout_workspace_bytes(int T, int K, int E, int G, size_t *bytes);
 
 /* Rows a receive buffer must hold for moe_dispatch() in `mode`: T*K for
  * EXPERT (exact when all entries are valid), T*min(K, G) for GROUP (an upper
- * bound on the deduplicated pairs). Returns a negative moe_error on bad input. */
+ * bound on the deduplicated pairs). Returns a negative moe_error on bad input.
+ * Source: mori pull request 586, Technical Details 1 (receive rows are bounded
+ * by a fixed per-destination capacity, MaxNumTokensToSend, so no count needs
+ * to come back to the host before the copy); DeepEP pull request 347, Design
+ * (a size-hint function for the buffer that receives every token of a batch);
+ * the challenge write-up, section 3.1 (buffers sized for the maximum problem). */
 int64_t moe_recv_rows_bound(int T, int K, int G, int mode);
 
 /* Routing layout of topk_idx (device int32 [T, K], row-major) into L's arrays.
@@ -173,8 +189,9 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
                  void *stream);
 
 /* moe_layout() and moe_dispatch() as one call. The layout arrays and the
- * receive buffers it writes are, bit for bit, those the two calls write
- * (layout->status included). Arguments as for moe_layout() and moe_dispatch().
+ * receive buffers it writes are, bit for bit, those the two calls write, and
+ * so is layout->status apart from the diagnostic bit MOE_STATUS_SYNC_FALLBACK.
+ * Arguments as for moe_layout() and moe_dispatch().
  * The smallest batches (T * K * E <= 4096), and any batch within
  * T <= MOE_FUSED_MAX_TOKENS and T * K <= MOE_FUSED_MAX_PAIRS when ws is NULL,
  * take one launch and need no workspace: one workgroup per token recomputes
@@ -187,7 +204,8 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
  * offsets and per-tile bases come from workgroup 0 of that dispatch
  * (T <= 4096 and at most four experts per dispatch thread: E <= 512 for
  * BF16, E <= 256 for FP8), which the other workgroups wait for within a
- * bounded time (MOE_STATUS_SYNC_TIMEOUT), or else from one workgroup launched
+ * bounded time (past it a workgroup computes its bases itself from the count
+ * table and sets MOE_STATUS_SYNC_FALLBACK), or else from one workgroup launched
  * in between. Otherwise (K > 8, or FP8 with H > 8192 or T > 3072) the call
  * runs moe_layout() and moe_dispatch(). The workspace holds no state from one
  * call to the next.
@@ -262,7 +280,13 @@ int moe_combine(const moe_layout_t *L, int mode, int H, const void *y, int64_t y
  * of the timed path): y[r, i] = bf16_rne(e4m3_decode(q[r, i]) * scale[r, i / 128])
  * for r < the layout's row count in `mode` (read on the device); rows beyond
  * it are not written. q: device uint8 [capacity, H]; scale: fp32
- * [capacity, H / 128]; y: bf16 [capacity, H]. H % 128 == 0. */
+ * [capacity, H / 128]; y: bf16 [capacity, H]. H % 128 == 0.
+ * Source: mori pull request 586 measures dispatch and combine with zero-copy
+ * combine (Motivation: combine reads the experts' outputs where they are) and
+ * regression-tests FP8 dispatch with a bf16 combine (Test Plan); the challenge
+ * write-up, section 3.1, stands a simple per-rank function in for the expert
+ * computation. Here the stand-in is the identity on the dequantised rows, so
+ * the FP8 round trip can be checked against its error bound. */
 int moe_fp8_dequant(const moe_layout_t *L, int mode, int H, const void *q, const float *scale,
                     void *y, int64_t capacity, void *stream);
 
@@ -271,8 +295,22 @@ int moe_fp8_dequant(const moe_layout_t *L, int mode, int H, const void *q, const
  * calibrates hardware traffic counters and gives a measured copy ceiling. */
 int moe_ref_copy(void *dst, const void *src, int64_t bytes, void *stream);
 
+/* Measurement aid, not part of the method: the read/write mix of a combine or
+ * a dispatch over contiguous rows, the ceiling of each call's own mix. For
+ * each of `units` units u, rows u*nr .. u*nr + nr - 1 of src (rows of
+ * row_bytes bytes) are read and their bitwise XOR is written to rows
+ * u*nw .. u*nw + nw - 1 of dst; src holds units*nr rows, dst units*nw rows.
+ * (nr, nw) is (1, 1), (2, 4 or 8, 1) — a combine's K reads per written row —
+ * or (1, 2, 4 or 8) — a dispatch's K writes per read row; else
+ * MOE_ERR_BAD_MODE. row_bytes % 16 == 0; pointers 16-byte aligned. */
+int moe_ref_mix(void *dst, const void *src, int64_t row_bytes, int64_t units, int nr, int nw,
+                void *stream);
+
 /* Text for a moe_error code (static storage). For MOE_ERR_HIP the text of the
- * last HIP error seen by this library on the calling thread is appended. */
+ * last HIP error seen by this library on the calling thread is appended.
+ * Not a step of the method: the pages define no error codes. It reports this
+ * ABI's host-side argument checks (the stress test and FP8 regression command of
+ * mori pull request 586's Test Plan are where such failures would surface). */
 const char *moe_status_string(int code);
 
 /* MOE_EP_ABI_VERSION of the built library. */

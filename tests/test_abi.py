@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(moe):
     lib = ctypes.CDLL(moe.library_path())
     missing = [n for n in header_functions() if not hasattr(lib, n)]
     assert not missing, missing
-    assert moe._lib.moe_abi_version() == 2
+    assert moe._lib.moe_abi_version() == 3
 
 
 def test_query_functions(moe):
@@ -143,6 +143,11 @@ def test_host_validation_errors(moe):
     assert lib.moe_ref_copy(A, A, 15, NULL) == -2
     assert lib.moe_ref_copy(A, M, 16, NULL) == -3
     assert lib.moe_ref_copy(A, A, 0, NULL) == 0
+    mix = lambda rb=14336, u=8, nr=8, nw=1, d=A: lib.moe_ref_mix(d, A, rb, u, nr, nw, NULL)
+    assert mix(nr=3) == -7 and mix(nr=2, nw=2) == -7 and mix(nw=16) == -7
+    assert mix(rb=15) == -2 and mix(u=-1) == -2
+    assert mix(d=M) == -3 and mix(d=NULL) == -1
+    assert mix(u=0, d=NULL) == 0
     for code in range(-7, 1):
         assert lib.moe_status_string(code)
 
@@ -165,7 +170,7 @@ def test_binding_constants_match_the_header(moe):
     assert int(defs["MOE_STATUS_BAD_INDEX"]) == moe.STATUS_BAD_INDEX
     assert int(defs["MOE_STATUS_DUPLICATE"]) == moe.STATUS_DUPLICATE
     assert int(defs["MOE_STATUS_Y_ROWS"]) == moe.STATUS_Y_ROWS
-    assert int(defs["MOE_STATUS_SYNC_TIMEOUT"]) == moe.STATUS_SYNC_TIMEOUT
+    assert int(defs["MOE_STATUS_SYNC_FALLBACK"]) == moe.STATUS_SYNC_FALLBACK
     assert int(defs["MOE_FUSED_MAX_TOKENS"]) == moe.FUSED_MAX_TOKENS
     assert int(defs["MOE_FUSED_MAX_PAIRS"]) == moe.FUSED_MAX_PAIRS
     assert int(enums["MOE_MODE_EXPERT"]) == moe.MODE_EXPERT and int(enums["MOE_MODE_GROUP"]) == moe.MODE_GROUP

@@ -183,12 +183,15 @@ def test_fused_fp8_placing_form():
     assert r.returncode == 0, r.stdout + r.stderr
 
 
-def test_sync_timeout_skips_tokens_cleanly():
-    """The placing dispatch's bounded wait for its tile's bases, forced from the host
-    (a wait limit of 0 ticks, set in a process of its own): tokens that give up are
-    skipped whole and reported, the others are placed exactly; no wave waits longer."""
-    env = dict(os.environ, MOE_EP_BASE_WAIT_TICKS="0")
-    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sync_timeout_child.py")
+@pytest.mark.parametrize("wait", ["0", "-1"])
+def test_sync_fallback_is_exact(wait):
+    """The placing dispatch's bounded wait for its tile's bases, cut short from the
+    host in a process of its own: with a wait limit of 0 ticks the tokens whose bases
+    are not written at their first poll, and with -1 every token, compute the bases
+    themselves from the count table; every layout array and receive row is still
+    exactly the oracle's, and only the diagnostic status bit is added."""
+    env = dict(os.environ, MOE_EP_BASE_WAIT_TICKS=wait)
+    child = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sync_fallback_child.py")
     r = subprocess.run([sys.executable, "-u", child], env=env, capture_output=True, text=True, timeout=240)
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
