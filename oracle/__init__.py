@@ -170,8 +170,24 @@ def _rows_and_src(L: dict, mode: str):
     raise ValueError(mode)
 
 
+def _out_arrays(out, specs):
+    """The output arrays of a call: those of `out` (a previous result of the same call,
+    reused so that a timed call does not allocate), else new ones."""
+    if out is None:
+        return [np.full(shape, fill, dt) for shape, dt, fill in specs]
+    arrs = []
+    for (name, (shape, dt, _)) in zip(out["_names"], specs):
+        a = out[name]
+        if a.shape != shape or a.dtype != dt or not a.flags.c_contiguous:
+            raise ValueError(f"out[{name!r}] must be a contiguous {np.dtype(dt)} array of shape {shape}")
+        arrs.append(a)
+    return arrs
+
+
 def dispatch_bf16(L: dict, mode: str, x: np.ndarray, topk_w: np.ndarray,
-                  topk_idx: np.ndarray, capacity: int | None = None, fill: int = 0) -> dict:
+                  topk_idx: np.ndarray, capacity: int | None = None, fill: int = 0,
+                  out: dict | None = None) -> dict:
+    """bf16 dispatch; `out` (an earlier result of the same shapes) is written in place."""
     x = _c(x, np.uint16)
     w = _c(topk_w, np.float32)
     idx = _c(topk_idx, np.int32)
@@ -179,16 +195,17 @@ def dispatch_bf16(L: dict, mode: str, x: np.ndarray, topk_w: np.ndarray,
     K = L["K"]
     m, R, src = _rows_and_src(L, mode)
     cap = R if capacity is None else capacity
-    recv_x = np.full((cap, H), fill, np.uint16)
-    recv_w = np.zeros((cap, K), np.float32)
-    recv_i = np.zeros((cap, K), np.int32)
+    recv_x, recv_w, recv_i = _out_arrays(out, [((cap, H), np.uint16, fill), ((cap, K), np.float32, 0),
+                                               ((cap, K), np.int32, 0)])
     _load().oracle_dispatch_bf16(m, K, H, R, _p(src), _p(x), _p(w), _p(idx), _p(recv_x),
                                  _p(recv_w), _p(recv_i))
-    return {"recv_x": recv_x, "recv_w": recv_w, "recv_idx": recv_i, "R": R}
+    return {"recv_x": recv_x, "recv_w": recv_w, "recv_idx": recv_i, "R": R,
+            "_names": ("recv_x", "recv_w", "recv_idx")}
 
 
 def dispatch_fp8(L: dict, mode: str, x: np.ndarray, topk_w: np.ndarray,
-                 topk_idx: np.ndarray, capacity: int | None = None) -> dict:
+                 topk_idx: np.ndarray, capacity: int | None = None, out: dict | None = None) -> dict:
+    """FP8 dispatch; `out` (an earlier result of the same shapes) is written in place."""
     x = _c(x, np.uint16)
     w = _c(topk_w, np.float32)
     idx = _c(topk_idx, np.int32)
@@ -198,13 +215,13 @@ def dispatch_fp8(L: dict, mode: str, x: np.ndarray, topk_w: np.ndarray,
     K = L["K"]
     m, R, src = _rows_and_src(L, mode)
     cap = R if capacity is None else capacity
-    recv_q = np.zeros((cap, H), np.uint8)
-    recv_s = np.zeros((cap, H // 128), np.float32)
-    recv_w = np.zeros((cap, K), np.float32)
-    recv_i = np.zeros((cap, K), np.int32)
+    recv_q, recv_s, recv_w, recv_i = _out_arrays(out, [
+        ((cap, H), np.uint8, 0), ((cap, H // 128), np.float32, 0), ((cap, K), np.float32, 0),
+        ((cap, K), np.int32, 0)])
     _load().oracle_dispatch_fp8(m, T, K, H, R, _p(src), _p(x), _p(w), _p(idx), _p(recv_q),
                                 _p(recv_s), _p(recv_w), _p(recv_i))
-    return {"recv_q": recv_q, "recv_scale": recv_s, "recv_w": recv_w, "recv_idx": recv_i, "R": R}
+    return {"recv_q": recv_q, "recv_scale": recv_s, "recv_w": recv_w, "recv_idx": recv_i, "R": R,
+            "_names": ("recv_q", "recv_scale", "recv_w", "recv_idx")}
 
 
 def quantize_row_fp8(xrow: np.ndarray):
@@ -226,13 +243,18 @@ def dequant_fp8(q: np.ndarray, scale: np.ndarray, R: int | None = None) -> np.nd
     return y
 
 
-def combine(L: dict, mode: str, y: np.ndarray, topk_w: np.ndarray) -> np.ndarray:
+def combine(L: dict, mode: str, y: np.ndarray, topk_w: np.ndarray,
+            out: np.ndarray | None = None) -> np.ndarray:
+    """Combine; `out` (a bf16-bits [T, H] array) is written in place if given."""
     y = _c(y, np.uint16)
     w = _c(topk_w, np.float32)
     T, K = L["T"], L["K"]
     H = y.shape[1]
     slot = L["slot_e"] if mode == "expert" else L["slot_g"]
-    out = np.zeros((T, H), np.uint16)
+    if out is None:
+        out = np.zeros((T, H), np.uint16)
+    elif out.shape != (T, H) or out.dtype != np.uint16 or not out.flags.c_contiguous:
+        raise ValueError(f"out must be a contiguous uint16 array of shape {(T, H)}")
     _load().oracle_combine(T, K, H, _p(slot), _p(y), _p(w), _p(out))
     return out
 
