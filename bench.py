@@ -378,7 +378,11 @@ def main():
     for _ in range(args.warmup):
         for f in fns:
             f()
+        # (also warms torch's kernel for it: the first launch of a torch kernel in a
+        # process loads its code object, tens of ms, which must not land in the timing)
+        status_or.bitwise_or_(L.status)
     torch.cuda.synchronize()
+    status_or.zero_()
 
     # Per-call HIP events on every EVENT_EVERY-th timed step: a sample of the timed
     # region for the per-call times, while most steps carry no event records (each
