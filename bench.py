@@ -314,6 +314,10 @@ def main():
                     help="only run the read/write-mix references of the t4096 dispatch (1 row "
                          "read per 8 written) and combine (8 read per 1 written), 5 times each "
                          "back to back: for taking their counters")
+    ap.add_argument("--profile", default=None, metavar="WORKLOAD:LAYOUT",
+                    help="only the three calls moe_layout, moe_dispatch and moe_combine (and the "
+                         "FP8 dequant between them) of one workload and receive layout, 5 times "
+                         "in a row, e.g. t4096:group: for taking counters of those kernels")
     ap.add_argument("--processes", type=int, default=3,
                     help="time the step in this many separate processes in all (this one included; "
                          "run one after another); `value` is the median of their values")
@@ -348,13 +352,31 @@ def main():
     if args.mix_probes:
         wl = si.WORKLOADS["t4096"]
         row = wl.H * 2
+        xs = torch.full((wl.T * row,), 3, dtype=torch.uint8, device="cuda")
         a = torch.full((wl.T * wl.K * row,), 1, dtype=torch.uint8, device="cuda")
         b = torch.full((wl.T * row,), 2, dtype=torch.uint8, device="cuda")
         for _ in range(5):
-            moe.moe_ref_mix(a, b, row, 1, wl.K)    # dispatch's mix: b -> a
-            moe.moe_ref_mix(b, a, row, wl.K, 1)    # combine's mix: a -> b
+            moe.moe_ref_mix(a, xs, row, 1, wl.K)   # the dispatch's mix: xs -> a
+            moe.moe_ref_mix(b, a, row, wl.K, 1)    # the combine's mix: a -> b
         torch.cuda.synchronize()
         print(json.dumps({"mix_probes": {"row_bytes": row, "units": wl.T, "k": wl.K, "launches": 5}}))
+        return
+    if args.profile:
+        name, mode = args.profile.split(":")
+        d = si.make_workload(name)
+        wl = d["workload"]
+        dt = "fp8" if wl.fp8 else "bf16"
+        dv = Dev(moe, d, modes=(mode,), dtype=dt)
+        L, D = dv.L, dv.D[mode]
+        for _ in range(5):
+            moe.moe_layout(dv.idx, wl.E, wl.G, out=L)
+            moe.moe_dispatch(L, dv.x, dv.w, dv.idx, mode, dt, out=D)
+            y = moe.moe_fp8_dequant(L, D.recv_x, D.recv_scale, mode) if wl.fp8 else D.recv_x
+            moe.moe_combine(L, y, dv.w, mode, out=dv.out)
+        torch.cuda.synchronize()
+        L.check_status()
+        print(json.dumps({"profile": args.profile, "rows": int(L.rows(mode).item()),
+                          "group_rows": int(L.group_offset[wl.G].item()), "launches": 5}))
         return
     if args.table:
         names = tuple(args.table.split(","))
@@ -596,11 +618,14 @@ def extras(moe, d, dv, args):
 
     # Read/write-mix ceilings: the dispatch's mix (one 14 KiB row read, K written) and
     # the combine's (K read, one written) over contiguous rows of the same size and
-    # count, with the kernels' cache policy; back to back as in the step, and alone.
+    # count, with the kernels' cache policy; back to back as in the step (the first
+    # reads a buffer that nothing wrote recently, as the dispatch reads x, and writes the
+    # rows the second reads; the second writes a third buffer), and alone.
     row = H * 2
+    xs = torch.full((T * row,), 3, dtype=torch.uint8, device="cuda")
     a = torch.full((R * row,), 1, dtype=torch.uint8, device="cuda")
     b = torch.full((T * row,), 2, dtype=torch.uint8, device="cuda")
-    mix_d = lambda: moe.moe_ref_mix(a, b, row, 1, K)
+    mix_d = lambda: moe.moe_ref_mix(a, xs, row, 1, K)
     mix_c = lambda: moe.moe_ref_mix(b, a, row, K, 1)
     mix_d(); mix_c()
     tp = time_calls([mix_d, mix_c], it)
@@ -615,7 +640,7 @@ def extras(moe, d, dv, args):
         "alone": {"dispatch_us": stats(tda)["median"], "combine_us": stats(tca)["median"],
                   "dispatch_gbs": round(mb_d / stats(tda)["median"] / 1e3, 1),
                   "combine_gbs": round(mb_c / stats(tca)["median"] / 1e3, 1)}}
-    del a, b
+    del a, b, xs
 
     # plain copy ceiling: 2 x 512 MiB streaming copy (half reads, half writes)
     n = 512 << 20
