@@ -26,7 +26,7 @@ import torch
 
 __all__ = [
     "MoeError", "MoeDataError", "Layout", "Dispatched", "moe_layout", "moe_dispatch", "moe_combine",
-    "moe_layout_dispatch", "moe_regroup", "moe_cast_transpose_fp8", "CastTransposed",
+    "moe_layout_dispatch", "moe_layout_dispatch_noalloc", "moe_regroup", "moe_cast_transpose_fp8", "CastTransposed",
     "moe_fp8_dequant", "moe_ref_copy", "moe_ref_mix", "recv_rows_bound", "layout_workspace_bytes",
     "library_path", "MODE_EXPERT", "MODE_GROUP", "DTYPE_BF16", "DTYPE_FP8",
     "STATUS_BAD_INDEX", "STATUS_DUPLICATE", "STATUS_Y_ROWS", "STATUS_SYNC_FALLBACK",
@@ -71,6 +71,7 @@ def _load_library() -> ctypes.CDLL:
         "moe_dispatch": (i32, [LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, _P, i64, _P]),
         "moe_combine": (i32, [LP, i32, i32, _P, i64, _P, _P, _P]),
         "moe_layout_dispatch": (i32, [_P, LP, _P, ctypes.c_size_t, i32, i32, i32, _P, _P, _P, _P, _P, _P, i64, _P]),
+        "moe_layout_dispatch_noalloc": (i32, [_P, LP, i32, i32, i32, _P, _P, _P, _P, _P, _P, i64, _P]),
         "moe_regroup": (i32, [LP, i32, i32, _P, _P, _P, _P, i64, _P, _P, _P, _P, i64, _P]),
         "moe_cast_transpose_t_bytes": (i64, [i32, i32, i32, i32]),
         "moe_cast_transpose_fp8": (i32, [LP, i32, _P, i64, _P, _P, _P, i64, _P, _P, _P]),
@@ -377,6 +378,37 @@ def moe_layout_dispatch(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
                                     _ptr(x), _ptr(topk_w), _ptr(D.recv_x), _ptr(D.recv_scale),
                                     _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
                                     _stream(stream)), "moe_layout_dispatch")
+    return L, D
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def moe_layout_dispatch_noalloc(topk_idx: torch.Tensor, E: int, G: int, x: torch.Tensor,
+                                topk_w: torch.Tensor, mode="expert", dtype="bf16", *,
+                                out_layout: Layout, out: Dispatched, stream=None) -> tuple[Layout, Dispatched]:
+    """moe_layout_dispatch without a workspace (moe_layout_dispatch_noalloc): the library's
+    own fixed workspace is used, and nothing is allocated, here or in the library. The
+    layout and receive arrays must be passed (out_layout, out). Calls overlapping on one
+    GPU race on the library's workspace."""
+    if topk_idx.dtype != torch.int32 or topk_idx.dim() != 2 or not topk_idx.is_contiguous():
+        raise ValueError("topk_idx must be a contiguous int32 [T, K] tensor")
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bf16 [T, H] tensor")
+    T, K = topk_idx.shape
+    if topk_w.dtype != torch.float32 or not topk_w.is_contiguous() or tuple(topk_w.shape) != (T, K):
+        raise ValueError("topk_w must be a contiguous fp32 [T, K] tensor")
+    L, D = out_layout, out
+    if (L.T, L.K, L.E, L.G) != (T, K, E, G):
+        raise ValueError("layout buffers were made for other sizes")
+    if x.shape[0] != T:
+        raise ValueError("x must have one row per token of topk_idx")
+    H = x.shape[1]
+    _check_dispatched(D, H, K, _dtype(dtype) == DTYPE_FP8, "out")
+    _check(_lib.moe_layout_dispatch_noalloc(_ptr(topk_idx), L.ref(), _mode(mode), _dtype(dtype), H,
+                                            _ptr(x), _ptr(topk_w), _ptr(D.recv_x), _ptr(D.recv_scale),
+                                            _ptr(D.recv_topk_w), _ptr(D.recv_topk_idx), D.recv_x.shape[0],
+                                            _stream(stream)), "moe_layout_dispatch_noalloc")
     return L, D
 
 

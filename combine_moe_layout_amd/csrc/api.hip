@@ -6,10 +6,43 @@
 
 #include "kernels.hpp"
 
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
 namespace {
+
+// Library-owned layout workspace of moe_layout_dispatch_noalloc(), for callers
+// that cannot allocate. Each GPU the library runs on holds its own copy until
+// the process ends. In host code `scratch` only names the symbol; its device
+// address on the current GPU comes from hipGetSymbolAddress (scratch_ptr).
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current GPU, looked up once per device
+// (with that device current) and kept; NULL with *err set if the lookup fails.
+void *scratch_ptr(hipError_t *err)
+{
+    int dev = -1;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= kMaxDevices) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 thread_local char g_hip_msg[160] = "";
 
@@ -130,10 +163,36 @@ int moe_dispatch(const moe_layout_t *L, int mode, int dtype, int H, const void *
     return e == hipSuccess ? MOE_OK : hip_fail(e);
 }
 
-int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t ws_bytes,
-                        int mode, int dtype, int H, const void *x, const float *topk_w, void *recv_x,
-                        float *recv_scale, float *recv_topk_w, int32_t *recv_topk_idx,
-                        int64_t recv_capacity, void *stream)
+}  // extern "C"
+
+namespace {
+
+// The argument checks of moe_layout_dispatch() that do not concern the workspace.
+int check_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, int mode, int dtype, int H,
+                          const void *x, const float *topk_w, const void *recv_x, const float *recv_scale,
+                          const float *recv_topk_w, const int32_t *recv_topk_idx, int64_t recv_capacity)
+{
+    if (int rc = check_layout_ptrs(L)) return rc;
+    if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
+    if (mode != MOE_MODE_EXPERT && mode != MOE_MODE_GROUP) return MOE_ERR_BAD_MODE;
+    if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_FP8_E4M3_B128) return MOE_ERR_BAD_MODE;
+    if (H <= 0 || H % 8 != 0) return MOE_ERR_BAD_SHAPE;
+    if (dtype == MOE_DTYPE_FP8_E4M3_B128 && H % 128 != 0) return MOE_ERR_BAD_SHAPE;
+    if (L->T == 0) return MOE_OK;
+    if (!topk_idx || !x || !topk_w || !recv_x || !recv_topk_w || !recv_topk_idx)
+        return MOE_ERR_NULL_PTR;
+    if (dtype == MOE_DTYPE_FP8_E4M3_B128 && !recv_scale) return MOE_ERR_NULL_PTR;
+    if (recv_capacity < rows_bound(L->T, L->K, L->G, mode)) return MOE_ERR_CAPACITY;
+    if (!aligned4(topk_idx) || !aligned16(x) || !aligned16(recv_x) || !aligned4(topk_w) ||
+        !aligned4(recv_topk_w) || !aligned4(recv_topk_idx) || (recv_scale && !aligned4(recv_scale)))
+        return MOE_ERR_MISALIGNED;
+    return MOE_OK;
+}
+
+int layout_dispatch_impl(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t ws_bytes,
+                         int mode, int dtype, int H, const void *x, const float *topk_w, void *recv_x,
+                         float *recv_scale, float *recv_topk_w, int32_t *recv_topk_idx,
+                         int64_t recv_capacity, void *stream)
 {
     if (int rc = check_layout_ptrs(L)) return rc;
     if (int rc = check_dims(L->T, L->K, L->E, L->G)) return rc;
@@ -229,6 +288,35 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
             : moe::launch_dispatch_bf16(x, L->T, H, L->K, nslot, nullptr, topk_w, topk_idx, recv_x,
                                         recv_topk_w, recv_topk_idx, &pa, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t ws_bytes,
+                        int mode, int dtype, int H, const void *x, const float *topk_w, void *recv_x,
+                        float *recv_scale, float *recv_topk_w, int32_t *recv_topk_idx,
+                        int64_t recv_capacity, void *stream)
+{
+    return layout_dispatch_impl(topk_idx, L, ws, ws_bytes, mode, dtype, H, x, topk_w, recv_x, recv_scale,
+                                recv_topk_w, recv_topk_idx, recv_capacity, stream);
+}
+
+int moe_layout_dispatch_noalloc(const int32_t *topk_idx, const moe_layout_t *L, int mode, int dtype, int H,
+                                const void *x, const float *topk_w, void *recv_x, float *recv_scale,
+                                float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
+                                void *stream)
+{
+    if (int rc = check_layout_dispatch(topk_idx, L, mode, dtype, H, x, topk_w, recv_x, recv_scale, recv_topk_w,
+                                       recv_topk_idx, recv_capacity))
+        return rc;
+    if (L->T > 0 && layout_ws_bytes(L->T, L->E, L->G) > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+    hipError_t err;
+    void *ws = scratch_ptr(&err);
+    if (!ws) return hip_fail(err);
+    return layout_dispatch_impl(topk_idx, L, ws, kScratchBytes, mode, dtype, H, x, topk_w, recv_x, recv_scale,
+                                recv_topk_w, recv_topk_idx, recv_capacity, stream);
 }
 
 int moe_regroup(const moe_layout_t *L, int dtype, int H, const void *recv_g, const float *recv_scale_g,
@@ -353,6 +441,9 @@ const char *moe_status_string(int code)
     case MOE_ERR_CAPACITY: return "receive buffer smaller than moe_recv_rows_bound()";
     case MOE_ERR_WORKSPACE: return "layout workspace missing or smaller than moe_layout_workspace_bytes()";
     case MOE_ERR_BAD_MODE: return "unknown mode or dtype";
+    case MOE_ERR_SCRATCH_LIMIT:
+        return "sizes need more layout workspace than moe_layout_dispatch_noalloc() holds "
+               "(MOE_NOALLOC_SCRATCH_BYTES); use moe_layout_dispatch() with a workspace";
     case MOE_ERR_HIP:
         snprintf(buf, sizeof buf, "HIP error: %s", g_hip_msg);
         return buf;

@@ -39,6 +39,7 @@ extern "C" {
 #define MOE_MAX_TOPK 32      /* K */
 #define MOE_FUSED_MAX_TOKENS 512   /* T of moe_layout_dispatch()'s one-launch form */
 #define MOE_FUSED_MAX_PAIRS 16384  /* T * K of moe_layout_dispatch()'s one-launch form */
+#define MOE_NOALLOC_SCRATCH_BYTES 8388608 /* layout workspace held by moe_layout_dispatch_noalloc() */
 
 enum moe_error {
     MOE_OK = 0,
@@ -48,7 +49,8 @@ enum moe_error {
     MOE_ERR_CAPACITY = -4,   /* a receive buffer is smaller than its bound */
     MOE_ERR_WORKSPACE = -5,  /* workspace missing or too small */
     MOE_ERR_HIP = -6,        /* a HIP runtime call or launch failed */
-    MOE_ERR_BAD_MODE = -7    /* unknown mode or dtype */
+    MOE_ERR_BAD_MODE = -7,   /* unknown mode or dtype */
+    MOE_ERR_SCRATCH_LIMIT = -8 /* sizes need more than MOE_NOALLOC_SCRATCH_BYTES of layout workspace */
 };
 
 /* Bits of layout->status (device int32). */
@@ -217,6 +219,25 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
                         int mode, int dtype, int H, const void *x, const float *topk_w, void *recv_x,
                         float *recv_scale, float *recv_topk_w, int32_t *recv_topk_idx,
                         int64_t recv_capacity, void *stream);
+
+/* moe_layout_dispatch() for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, results and forms as moe_layout_dispatch()
+ * without ws / ws_bytes: the layout workspace is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES (8 MiB) inside the library, one per GPU, held until
+ * the process ends. Sizes whose workspace (moe_layout_workspace_bytes()) exceeds
+ * it return MOE_ERR_SCRATCH_LIMIT before anything is launched (E = 256, G = 8:
+ * up to about 200,000 tokens; E = 1024, G = 32: about 50,000). The call
+ * allocates nothing: it looks up the array's device address once per GPU, on
+ * its first call there. The workspace needs no initialisation (each call
+ * writes what it reads before reading it), so nothing carries over between
+ * calls; but every call on one GPU uses the same array, so calls that overlap
+ * on one GPU (other streams, other threads, concurrently replayed graphs)
+ * race and must be serialised by the caller. */
+int moe_layout_dispatch_noalloc(const int32_t *topk_idx, const moe_layout_t *L, int mode, int dtype, int H,
+                                const void *x, const float *topk_w, void *recv_x, float *recv_scale,
+                                float *recv_topk_w, int32_t *recv_topk_idx, int64_t recv_capacity,
+                                void *stream);
 
 /* Receive-side regroup: the arrays of a per-group (GROUP) dispatch result ->
  * the per-expert (EXPERT) layout, i.e. for every EXPERT row r with pair

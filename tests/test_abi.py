@@ -148,7 +148,13 @@ def test_host_validation_errors(moe):
     assert mix(rb=15) == -2 and mix(u=-1) == -2
     assert mix(d=M) == -3 and mix(d=NULL) == -1
     assert mix(u=0, d=NULL) == 0
-    for code in range(-7, 1):
+    # the no-allocation call: a workspace beyond its fixed array is refused before any HIP call
+    nd = lambda Lp, mode=0, cap=1 << 20: lib.moe_layout_dispatch_noalloc(A, ref(Lp), mode, 0, 2048, A, A, A, NULL,
+                                                                          A, A, cap, NULL)
+    big = _fake_layout(moe, T=60000, K=8, E=1024, G=32)
+    assert nd(big, cap=60000 * 8) == -8
+    assert nd(big, mode=3) == -7 and nd(big, cap=10) == -4
+    for code in range(-8, 1):
         assert lib.moe_status_string(code)
 
 
@@ -173,6 +179,8 @@ def test_binding_constants_match_the_header(moe):
     assert int(defs["MOE_STATUS_SYNC_FALLBACK"]) == moe.STATUS_SYNC_FALLBACK
     assert int(defs["MOE_FUSED_MAX_TOKENS"]) == moe.FUSED_MAX_TOKENS
     assert int(defs["MOE_FUSED_MAX_PAIRS"]) == moe.FUSED_MAX_PAIRS
+    assert int(defs["MOE_NOALLOC_SCRATCH_BYTES"]) == moe.NOALLOC_SCRATCH_BYTES
+    assert moe.STATUS_ERRORS == moe.STATUS_BAD_INDEX | moe.STATUS_DUPLICATE | moe.STATUS_Y_ROWS
     assert int(enums["MOE_MODE_EXPERT"]) == moe.MODE_EXPERT and int(enums["MOE_MODE_GROUP"]) == moe.MODE_GROUP
     assert int(enums["MOE_DTYPE_BF16"]) == moe.DTYPE_BF16
     assert int(enums["MOE_DTYPE_FP8_E4M3_B128"]) == moe.DTYPE_FP8
