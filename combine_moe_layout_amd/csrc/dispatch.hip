@@ -310,6 +310,7 @@ const Tuning &tuning()
         if (const char *f = getenv("MOE_EP_BASE_WAIT_TICKS")) r.base_wait_ticks = atoll(f);
         env("MOE_EP_FP8_GROUP_W4", r.fp8_group_w4);
         if (const char *f = getenv("MOE_EP_FUSED_FP8_PLACE_MAX_T")) r.fused_fp8_place_max_t = atoi(f);
+        env("MOE_EP_REGROUP_XCD_ORDER", r.regroup_xcd_order);
         return r;
     }();
     return t;

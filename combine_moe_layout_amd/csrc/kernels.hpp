@@ -121,6 +121,7 @@ struct Tuning {
     int fused_finalize = 2;                 // placing dispatch: 0 the finalize kernel, 1 its
                                             // workgroup 0 (bf16), 2 workgroup 0 (bf16 and FP8)
     int fused_finalize_rounds = 4;          // ... for E up to this many columns per thread
+    bool regroup_xcd_order = true;          // regroup: each XCD takes a contiguous run of group rows
 };
 const Tuning &tuning();
 // Whether the FP8 dispatch of rows of H elements runs in a small-workgroup form.
