@@ -65,6 +65,8 @@ KERNEL_SOURCES = {
     "dispatch": ("dispatch.hip", "place.hpp", "common.hpp", "kernels.hpp"),
     "combine": ("combine.hip", "common.hpp", "kernels.hpp"),
     "layout": ("layout.hip", "common.hpp", "kernels.hpp"),
+    "regroup": ("regroup.hip", "common.hpp", "kernels.hpp"),
+    "cast_transpose": ("cast_transpose.hip", "common.hpp", "kernels.hpp"),
 }
 
 
@@ -711,19 +713,19 @@ def extras(moe, d, dv, args):
 
 
 def add_ceilings(extra):
-    """Each workload report row's share of the measured copy ceilings of the same run:
-    the read/write-mix reference of its call (dispatch or combine rows) and the plain
-    copy for the rest."""
+    """Each workload report row's share of the measured ceiling of the same run: the
+    read/write-mix reference of its call (the dispatch's or the combine's mix); none for
+    the latency-bound layout."""
     mix = extra["mix_ceiling"]["pair"]
-    copy = extra["copy_ceiling"]["gbs"]
     for name, r in extra["workloads"].items():
         if not isinstance(r, dict):
             continue
         for row in r.get("report", []):
-            ref = mix["dispatch_gbs"] if row["call"] == "dispatch" else (
-                mix["combine_gbs"] if row["call"] == "combine" else copy)
-            if row.get("gbs") is not None:
-                row["of_ceiling"] = round(row["gbs"] / ref, 3)
+            if row["call"] == "layout":      # latency-bound: no bandwidth ceiling applies
+                row["of_ceiling"] = None
+                continue
+            ref = mix["dispatch_gbs"] if row["call"] == "dispatch" else mix["combine_gbs"]
+            row["of_ceiling"] = round(row["gbs"] / ref, 3)
 
 
 def device_clocks():
@@ -891,6 +893,13 @@ def workload_table(moe, names=WORKLOAD_NAMES, it=30, oracle_threads=0):
                  "of_peak": round(nb / st["median"] / 1e3 / PEAK_HBM_GBS, 4),
                  "payload_gbs": (round(rows_here * H * (1 if wl.fp8 and call == "dispatch" else 2)
                                        / st["median"] / 1e3, 1) if call != "layout" else None)}
+            # HBM traffic per launch from the committed counters (None unless they were
+            # taken on this kernel's current sources), and its ratio to the algorithmic bytes
+            if call != "layout":
+                tk = f"{name}.{call}_{mode}_{'fp8' if wl.fp8 and call == 'dispatch' else 'bf16'}"
+                tb = load_traffic(tk)
+                r["traffic_bytes"] = tb
+                r["traffic_over_algorithmic"] = None if tb is None else round(tb / nb, 4)
             if orc is not None:
                 n = orc["threads"]
                 r["oracle_us"] = {"1": orc["calls"][key]["us_1"], str(n): orc["calls"][key][f"us_{n}"]}
