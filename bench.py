@@ -341,6 +341,10 @@ def main():
     import synth_inputs as si
 
     torch.cuda.init()
+    # the GPU should be idle: record how much of its memory is already in use (mori's
+    # benchmark script refuses to run above 15%)
+    free_b, total_b = torch.cuda.mem_get_info()
+    used_before = round(1 - free_b / total_b, 4)
     if args.calibrate_copy:
         n = 256 << 20
         src = torch.full((n,), 3, dtype=torch.uint8, device="cuda")
@@ -481,6 +485,7 @@ def main():
         "bytes": {"layout": b_layout, "dispatch": d_r + d_w, "combine": c_r + c_w, "rows": R,
                   "group_rows": P},
         "source_hash": source_hash(),
+        "gpu_memory_in_use_at_start": used_before,
     }
     if procs is not None:
         result["processes"] = procs
@@ -559,7 +564,7 @@ def extras(moe, d, dv, args):
     import synth_inputs as si
     wl = dv.wl
     T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K
-    it = 30
+    it = 50     # timed calls per measurement (median, p10/p90 over these)
     res = {}
     L = dv.L
     moe.moe_layout(dv.idx, E, G, out=L)
@@ -752,7 +757,7 @@ def _layout_host(L):
         "slot_g", "slot_tg", "recv_src_e", "recv_src_g", "status")}
 
 
-def workload_table(moe, names=WORKLOAD_NAMES, it=30, oracle_threads=0):
+def workload_table(moe, names=WORKLOAD_NAMES, it=50, oracle_threads=0):
     """Per-workload timings of every call in both receive layouts (median µs over `it`
     event-timed calls; GB/s = algorithmic bytes / median), the per-expert step
     replayed from a captured HIP graph (no host launch cost), and, with

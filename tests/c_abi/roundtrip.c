@@ -89,6 +89,42 @@ static int run_mode(const moe_layout_t *L, int mode, const uint16_t *x, const in
     return 0;
 }
 
+/* moe_layout_dispatch_noalloc (the library's own workspace): rows equal to their
+ * source tokens in the per-expert layout, counts equal to moe_layout's. */
+static int run_noalloc(moe_layout_t *L, const uint16_t *x, const int32_t *idx, const void *x_d,
+                       const float *w_d, const int32_t *idx_d, const int32_t *want_off)
+{
+    const int64_t cap = moe_recv_rows_bound(T, K, G, MOE_MODE_EXPERT);
+    void *recv = dmalloc((size_t)cap * H * 2);
+    float *rw = (float *)dmalloc((size_t)cap * K * 4);
+    int32_t *ri = (int32_t *)dmalloc((size_t)cap * K * 4);
+    EXPECT(recv && rw && ri, "hipMalloc");
+    EXPECT(moe_layout_dispatch_noalloc(idx_d, L, MOE_MODE_EXPERT, MOE_DTYPE_BF16, H, x_d, w_d, recv, NULL, rw, ri,
+                                       cap, NULL) == MOE_OK,
+           "moe_layout_dispatch_noalloc");
+    CHECK_HIP(hipDeviceSynchronize());
+    int32_t off[E + 1], status = -1;
+    static int32_t src[T * K];
+    uint16_t *hrecv = (uint16_t *)malloc((size_t)T * K * H * 2);
+    CHECK_HIP(hipMemcpy(off, L->expert_offset, sizeof off, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(&status, L->status, 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(src, L->recv_src_e, T * K * 4, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(hrecv, recv, (size_t)T * K * H * 2, hipMemcpyDeviceToHost));
+    EXPECT(status == 0, "noalloc status %d", status);
+    for (int e = 0; e <= E; ++e) EXPECT(off[e] == want_off[e], "noalloc expert offset %d", e);
+    for (int r = 0; r < T * K; ++r) {
+        const int t = src[r] / K;
+        EXPECT(t >= 0 && t < T && memcmp(hrecv + (size_t)r * H, x + (size_t)t * H, H * 2) == 0,
+               "noalloc row %d", r);
+    }
+    (void)idx;
+    free(hrecv);
+    hipFree(recv);
+    hipFree(rw);
+    hipFree(ri);
+    return 0;
+}
+
 int main(void)
 {
     EXPECT(moe_abi_version() == MOE_EP_ABI_VERSION, "ABI version %d", moe_abi_version());
@@ -177,6 +213,7 @@ int main(void)
 
     if (run_mode(&L, MOE_MODE_EXPERT, x, idx, x_d, w_d, idx_d, src_e, off[E])) return 1;
     if (run_mode(&L, MOE_MODE_GROUP, x, idx, x_d, w_d, idx_d, src_g, goff[G])) return 1;
+    if (run_noalloc(&L, x, idx, x_d, w_d, idx_d, off)) return 1;
     printf("ok\n");
     return 0;
 }

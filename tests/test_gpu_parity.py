@@ -197,6 +197,20 @@ def test_sync_fallback_is_exact(wait):
     assert r.returncode == 0, r.stdout + r.stderr
 
 
+def test_check_status_raises_on_bad_input(moe):
+    """Layout.check_status() reads the device status word and raises on its error bits
+    (here an index out of range, then a repeated expert); a clean layout returns 0."""
+    L = moe.moe_layout(to_dev(np.array([[0, 1], [2, 9]], np.int32)), 8, 4)
+    with pytest.raises(moe.MoeDataError) as ei:
+        L.check_status()
+    assert ei.value.status & moe.STATUS_BAD_INDEX
+    L = moe.moe_layout(to_dev(np.array([[0, 1], [3, 3]], np.int32)), 8, 4)
+    with pytest.raises(moe.MoeDataError):
+        L.check_status()
+    L = moe.moe_layout(to_dev(np.array([[0, 1], [2, 3]], np.int32)), 8, 4)
+    assert L.check_status() == 0
+
+
 @pytest.mark.parametrize("T,K,E,G", [(700, 8, 256, 8), (300, 4, 64, 4), (513, 2, 16, 8)])
 def test_layout_slot_arrays_4_byte_aligned(moe, orc, T, K, E, G):
     """Slot arrays that are 4-byte but not 16-byte aligned (allowed by the ABI) take
