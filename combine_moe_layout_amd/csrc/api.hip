@@ -23,21 +23,35 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices] = {};
 
-// Device address of `scratch` on the current GPU, looked up once per device
-// (with that device current) and kept; NULL with *err set if the lookup fails.
-void *scratch_ptr(hipError_t *err)
+// Device address of `scratch` on the GPU the call's kernels run on (the
+// stream's device; the current device for the null stream), looked up once per
+// device with that device current and kept; NULL with *err set if the lookup
+// fails. The caller's current device is restored after a lookup.
+void *scratch_ptr(hipStream_t stream, hipError_t *err)
 {
-    int dev = -1;
-    *err = hipGetDevice(&dev);
+    int dev = -1, cur = -1;
+    *err = hipGetDevice(&cur);
     if (*err != hipSuccess) return nullptr;
+    dev = cur;
+    if (stream) {
+        hipDevice_t sd = -1;
+        *err = hipStreamGetDevice(stream, &sd);
+        if (*err != hipSuccess) return nullptr;
+        dev = sd;
+    }
     if (dev < 0 || dev >= kMaxDevices) {
         *err = hipErrorInvalidDevice;
         return nullptr;
     }
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (*err = hipSetDevice(dev)) != hipSuccess) return nullptr;
         void *p = nullptr;
         *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (*err == hipSuccess) *err = e2;
+        }
         if (*err != hipSuccess) return nullptr;
         g_scratch_ptr[dev] = p;
     }
@@ -313,7 +327,7 @@ int moe_layout_dispatch_noalloc(const int32_t *topk_idx, const moe_layout_t *L, 
         return rc;
     if (L->T > 0 && layout_ws_bytes(L->T, L->E, L->G) > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
     hipError_t err;
-    void *ws = scratch_ptr(&err);
+    void *ws = scratch_ptr((hipStream_t)stream, &err);
     if (!ws) return hip_fail(err);
     return layout_dispatch_impl(topk_idx, L, ws, kScratchBytes, mode, dtype, H, x, topk_w, recv_x, recv_scale,
                                 recv_topk_w, recv_topk_idx, recv_capacity, stream);

@@ -228,8 +228,9 @@ int moe_layout_dispatch(const int32_t *topk_idx, const moe_layout_t *L, void *ws
  * the process ends. Sizes whose workspace (moe_layout_workspace_bytes()) exceeds
  * it return MOE_ERR_SCRATCH_LIMIT before anything is launched (E = 256, G = 8:
  * up to about 200,000 tokens; E = 1024, G = 32: about 50,000). The call
- * allocates nothing: it looks up the array's device address once per GPU, on
- * its first call there. The workspace needs no initialisation (each call
+ * allocates nothing: it looks up the array's device address once per GPU (the
+ * GPU of `stream`, or the current one for the null stream), on its first call
+ * there. The workspace needs no initialisation (each call
  * writes what it reads before reading it), so nothing carries over between
  * calls; but every call on one GPU uses the same array, so calls that overlap
  * on one GPU (other streams, other threads, concurrently replayed graphs)
