@@ -20,6 +20,9 @@ PAIRS = [
     ((4096, 7168, 256, 8, 8, "expert", "bf16"), (1000, 2048, 64, 8, 6, "group", "bf16")),
     ((2048, 1024, 128, 8, 8, "expert", "fp8"), (300, 512, 16, 4, 4, "group", "fp8")),
     ((5000, 512, 64, 8, 8, "group", "bf16"), (64, 256, 8, 8, 2, "expert", "bf16")),
+    # top-k above 8 (moe_layout + moe_dispatch inside the call, on the library's workspace) and
+    # FP8 rows longer than 8192 (the row-sized form, also layout + dispatch inside)
+    ((3000, 1024, 64, 8, 12, "group", "bf16"), (700, 16384, 128, 8, 8, "expert", "fp8")),
 ]
 FIELDS = ("expert_count", "expert_offset", "group_count", "group_offset", "tok_group_mask", "slot_e",
           "slot_g", "slot_tg", "status")
@@ -87,3 +90,19 @@ def test_noalloc_equals_workspace_call(moe, first, second):
         assert torch.equal(D1.recv_topk_w.view(torch.int32), D2.recv_topk_w.view(torch.int32)), case
         assert torch.equal(D1.recv_topk_idx, D2.recv_topk_idx), case
         print(f"{case}: {rows} rows equal, status {int(L2.status.item())}", flush=True)
+
+
+def test_noalloc_no_tokens(moe):
+    """T = 0: the call zeroes the counts, offsets and status, as moe_layout_dispatch does."""
+    L = moe.Layout.empty(0, 8, 256, 8)
+    L.expert_offset.fill_(7)
+    L.group_count.fill_(7)
+    L.status.fill_(5)
+    D = moe.alloc_dispatch(L, 1024, "expert", "bf16")
+    idx = torch.zeros((0, 8), dtype=torch.int32, device="cuda")
+    x = torch.zeros((0, 1024), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((0, 8), dtype=torch.float32, device="cuda")
+    moe.moe_layout_dispatch_noalloc(idx, 256, 8, x, w, "expert", "bf16", out_layout=L, out=D)
+    torch.cuda.synchronize()
+    assert int(L.expert_offset.abs().sum().item()) == 0 and int(L.group_count.abs().sum().item()) == 0
+    assert int(L.status.item()) == 0
