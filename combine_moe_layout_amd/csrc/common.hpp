@@ -13,6 +13,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Cache-policy operand of the buffer load / store builtins for the
+// agent-scope coherent form (sc1: what an agent-scope atomic load or store
+// compiles to), for data exchanged between workgroups of one launch.
+constexpr int kCpolSc1 = 16;
+
 // Non-temporal 16-byte store: the destination rows are written once and not
 // re-read by this kernel, so they should not displace useful lines in the
 // write-allocate L2.

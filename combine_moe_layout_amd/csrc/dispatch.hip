@@ -303,6 +303,7 @@ const Tuning &tuning()
         env("MOE_EP_DISPATCH_NT_STORE", r.dispatch_nt_store);
         if (const char *f = getenv("MOE_EP_FP8_FORM")) r.fp8_form = atoi(f);
         if (const char *f = getenv("MOE_EP_LAYOUT_ONEPASS_MAX_PAIRS")) r.layout_onepass_max_pairs = atoi(f);
+        if (const char *f = getenv("MOE_EP_LAYOUT_EXCHANGE_MAX_TILES")) r.layout_exchange_max_tiles = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_ONEPASS_MAX_PAIRS")) r.fused_onepass_max_pairs = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_FINALIZE")) r.fused_finalize = atoi(f);
         if (const char *f = getenv("MOE_EP_FUSED_FINALIZE_ROUNDS")) r.fused_finalize_rounds = atoi(f);

@@ -99,7 +99,7 @@ inline uint32_t group_magic(int E, int G)
 // and the largest batch of the one-launch layout. Defaults are the measured
 // best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2,
 // MOE_EP_FP8_GROUP_W4=0/1, MOE_EP_FUSED_FP8_PLACE_MAX_T=<T>, MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>,
-// MOE_EP_FUSED_SMALL_MAX_WORK=<T*K*E>,
+// MOE_EP_FUSED_SMALL_MAX_WORK=<T*K*E>, MOE_EP_LAYOUT_EXCHANGE_MAX_TILES=<tiles>,
 // MOE_EP_FUSED_FINALIZE=0/1/2, MOE_EP_FUSED_FINALIZE_ROUNDS=<n> and
 // MOE_EP_BASE_WAIT_TICKS=<ticks> in the environment override them (read once per
 // process) for A/B runs and tests.
@@ -111,7 +111,10 @@ struct Tuning {
     bool fp8_group_w4 = true;        // plain per-group FP8 dispatch at 4 waves per SIMD
     int fused_fp8_place_max_t = 3072;  // moe_layout_dispatch with FP8: a placing dispatch up
                                        // to this T, moe_layout + the plain dispatch above
-    int layout_onepass_max_pairs = 16384;   // moe_layout in one launch up to T * K pairs (top-k <= 8)
+    int layout_exchange_max_tiles = 64;     // moe_layout in one launch exchanging per-tile counts, up to
+                                            // this many tiles of 256 tokens (top-k <= 8; 0: never)
+    int layout_onepass_max_pairs = 16384;   // else in one launch counting every token per tile, up to
+                                            // T * K pairs (top-k <= 8)
     int fused_onepass_max_pairs = 0;        // moe_layout_dispatch as that layout + a plain dispatch
     int fused_small_max_work = 4096;        // moe_layout_dispatch in one launch up to T * K * E
     long long base_wait_ticks = 20000000;   // placing dispatch: longest wait for a tile's bases

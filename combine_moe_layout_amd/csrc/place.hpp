@@ -81,9 +81,8 @@ __device__ __forceinline__ int fin_column_sum(__amdgpu_buffer_rsrc_t tab, int ro
 // Bases of column `col` in the nt tiles: the column's offset plus the counts
 // of the tiles before. `bases` is a buffer resource over the nt rows, so the
 // stores of rows past the last tile are dropped by the hardware; the stores
-// carry sc1, the agent-scope coherent form (what an agent-scope atomic store
-// compiles to), so the polling loads of other workgroups see them.
-constexpr int kCpolSc1 = 16;
+// carry sc1 (kCpolSc1), the agent-scope coherent form, so the polling loads of
+// other workgroups see them.
 __device__ __forceinline__ void fin_column_bases(int col, const int (&v)[kFinBatch], int offset,
                                                  __amdgpu_buffer_rsrc_t bases, int cols)
 {

@@ -5,10 +5,14 @@
  * The expert-parallel "ranks" of an EP group are expert groups inside one
  * GPU's HBM: expert e belongs to group g = e / (E / G). Every call is
  * asynchronous on the caller's HIP stream and is ordered only by that stream.
- * The library allocates no device memory and keeps no state between calls:
- * every array is owned by the caller (device memory unless stated), and the
- * receive buffers are sized at the bounds given by moe_recv_rows_bound(), so no
- * device-to-host synchronisation is needed anywhere on the path.
+ * The library allocates no device memory: every array is owned by the caller
+ * (device memory unless stated), and the receive buffers are sized at the
+ * bounds given by moe_recv_rows_bound(), so no device-to-host synchronisation
+ * is needed anywhere on the path. What it keeps between calls is fixed in
+ * size: on each GPU, the workspace of moe_layout_dispatch_noalloc() and the
+ * exchange tables of moe_layout() (arrays in its own code object, zero when
+ * it is loaded), and on the host a call counter per stream for those tables.
+ * No result depends on what they hold when a call starts.
  *
  * Errors. Every entry point returns 0 (MOE_OK) or a negative moe_error code.
  * All argument checks happen on the host before anything is launched; a call
@@ -57,10 +61,12 @@ enum moe_error {
 #define MOE_STATUS_BAD_INDEX 1 /* some topk_idx entry outside [0, E) */
 #define MOE_STATUS_DUPLICATE 2 /* some token lists one expert twice */
 #define MOE_STATUS_Y_ROWS 4    /* combine met a slot >= the rows of y */
-#define MOE_STATUS_SYNC_FALLBACK 8 /* diagnostic, not an error: in moe_layout_dispatch a
-                                      token's workgroup waited longer than its limit (0.2 s)
-                                      for its tile's bases and computed them itself from the
-                                      count table; every result is still exact */
+#define MOE_STATUS_SYNC_FALLBACK 8 /* diagnostic, not an error: a workgroup waited longer
+                                      than its limit (0.2 s) for values other workgroups of
+                                      its launch write and computed them itself (in
+                                      moe_layout_dispatch a token's bases, from the count
+                                      table; in moe_layout the first tile's counts, from the
+                                      indices); every result is still exact */
 /* The bits that mark bad input or output that cannot be trusted. */
 #define MOE_STATUS_ERRORS (MOE_STATUS_BAD_INDEX | MOE_STATUS_DUPLICATE | MOE_STATUS_Y_ROWS)
 
@@ -158,10 +164,21 @@ int64_t moe_recv_rows_bound(int T, int K, int G, int mode);
  * entries get slot -1, are not counted, and set status bits.
  * Requires 1 <= K <= MOE_MAX_TOPK, K <= E <= MOE_MAX_EXPERTS,
  * 1 <= G <= MOE_MAX_GROUPS, E % G == 0, T >= 0, T * max(K, G) < 2^30.
- * ws: device workspace of at least moe_layout_workspace_bytes() bytes (for
- * K <= 8 and T * K <= 16384 the layout runs as one launch that does not touch
- * it; it is required in every case).
+ * ws: device workspace of at least moe_layout_workspace_bytes() bytes,
+ * required in every case (the one-launch forms below do not touch it).
  * stream: a hipStream_t (NULL = the null stream).
+ * Forms. For K <= 8 the layout is one launch with a workgroup per tile of 256
+ * tokens. When the tiles' table of (tiles * (E + G + 2)) entries fits 16384
+ * (T <= 15616 at E = 256, G = 8) the workgroups learn one another's per-tile
+ * counts through a table in library memory, one per stream on each GPU (8
+ * streams per GPU get one; later streams, streams under graph capture and
+ * hipStreamPerThread take the forms below): each entry carries the call's
+ * number on its stream, so an entry of an earlier call or of a concurrent
+ * call is never taken, and a workgroup that has waited 0.2 s for the others
+ * counts every token itself (exact; MOE_STATUS_SYNC_FALLBACK is set when the
+ * first tile's workgroup does so). Otherwise, for T * K <= 16384, each
+ * workgroup counts every token itself; otherwise two launches (per-tile
+ * counts into ws, then the placement).
  * Source: mori pull request 586, Motivation and Technical Details 1; the
  * separate routing launch is the one its profiling section proposes. */
 int moe_layout(const int32_t *topk_idx, const moe_layout_t *L, void *ws, size_t ws_bytes,
