@@ -974,16 +974,18 @@ __global__ __launch_bounds__(kOpBS) void layout_onepass_kernel(
     tile_write_recv_src_e(npairs, s_src, s_dst, L.recv_src_e, tid, kOpBS);
 }
 
-// One-launch layout with an exchange between tiles (moe_layout, top-k <= 8, a
-// table of at most kXchEntries entries): the count and place kernels above as
+// One-launch layout with an exchange between tiles (moe_layout, top-k <= 8, up
+// to 64 tiles): the count and place kernels above as
 // one workgroup per tile, which learns what it needs of the other tiles from a
 // table in library memory instead of from a second launch. The workgroup
 // counts its tile as the count kernel does (the per-(expert, wave) words stay
 // in LDS) and takes the tile's own exclusive prefix of its counts over the
 // experts, and over the groups. It writes, per column (E experts, G groups,
-// then a summary column), one 64-bit entry tag << 32 | value with one atomic
-// store, the value packing the tile's count and its prefix (the summary: the
-// tile's error bits and its numbers of expert and group pairs). Summed over
+// two summary columns: the tile's numbers of expert and group pairs, and its
+// error bits; one padding column to an even count), one 64-bit entry
+// tag << 32 | value with one atomic store, the value packing the tile's count
+// and its prefix. Each thread then reads two adjacent columns of every tile
+// (one 16-byte read per tile). Summed over
 // the tiles, the prefixes give each expert's offset, and the counts of the
 // tiles before this one its first receive row in this tile, so no scan is
 // left after the exchange. The tag is this call's number on its stream, which
@@ -1103,17 +1105,17 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
     uint64_t *__restrict__ xt, uint32_t tag, uint64_t wait_ticks, int recount, LayoutPtrs L, int vec)
 {
     static_assert(KMAX <= 8, "the tile's entries are staged for at most 8 per token");
-    constexpr int NCOL = NCH + 1;                  // columns a thread owns (E + G + 2 <= NCOL * 256)
-    constexpr int kXR = 12;                        // 16-byte table reads per thread and round (48 KiB)
+    constexpr int NCOL = NCH + 1;                  // columns a thread publishes (E + G + 3 <= NCOL * 256)
+    constexpr int NPJ = NCH == 1 ? 1 : 3;          // column pairs a thread reads ((E + G + 3) / 2 <= NPJ * 256)
+    constexpr int kXB = 16;                        // tiles per round of reads
     // dynamic LDS: emask [E][kWaves] u64; int loff_e [E][kWaves], lstart [E], base_e [E],
-    // s_tot [E+G+1], s_pre [E+G+1] (the fallback's); then the table's values [ntiles][E+G+2] (+2)
+    // s_tot [E+G+1], s_pre [E+G+1] (the fallback's)
     extern __shared__ unsigned long long emask[];
     int *loff_e = reinterpret_cast<int *>(emask + E * kWaves);   // rank base of (expert, wave) in the tile
     int *lstart = loff_e + E * kWaves;                           // expert's first place in the tile's pair list
     int *base_e = lstart + E;                                    // expert's first receive row of the tile
     int *s_tot = base_e + E;
     int *s_pre = s_tot + E + G + 1;
-    uint32_t *xcopy = reinterpret_cast<uint32_t *>(s_pre + E + G + 1);   // 8-byte aligned: 16E + 2G + 2 ints before it
     __shared__ int32_t s_src[kLayoutTile * KMAX];   // the tile's pair ids in slot order
     __shared__ int32_t s_dst[kLayoutTile * KMAX];   // and their receive slots
     __shared__ int s_wave_tot[kWaves];
@@ -1127,7 +1129,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int tile = blockIdx.x;
     const int t = tile * kLayoutTile + tid;
-    const int rows = E + G + 2;   // table columns: experts, groups, pairs, error bits
+    const int rows = (E + G + 3) & ~1;   // table columns: experts, groups, pairs, error bits (+1: even)
     const uint64_t below = lanemask_lt(lane);
 
     // Count the tile (as the count kernel).
@@ -1208,27 +1210,27 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
     }
     __syncthreads();
 
-    // Publish (or, with one tile, keep) the tile's value of each owned column
-    // c = tid + j * 256.
-    if (!recount) {
+    // The tile's value of column c (see xch_pack).
+    auto own_value = [&](int c) -> uint32_t {
+        if (c < E) {
+            const unsigned long long *m = emask + c * kWaves;
+            return xch_pack(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]), lstart[c]);
+        }
+        if (c < E + G) {
+            const int g = c - E;
+            return xch_pack(gcnt[g][0] + gcnt[g][1] + gcnt[g][2] + gcnt[g][3], lgstart[g]);
+        }
+        if (c == E + G) return xch_pack(npairs, s_gpairs);
+        if (c == E + G + 1) return xch_err_pack(s_err);
+        return 0u;   // the padding column
+    };
+    // Publish it, for the columns c = tid + j * 256.
+    const bool xch = xt != nullptr && !recount;   // uniform
+    if (xch) {
 #pragma unroll
         for (int j = 0; j < NCOL; ++j) {
             const int c = tid + j * kLayoutTile;
-            if (c < rows) {
-                uint32_t v;
-                if (c < E) {
-                    v = xch_pack(cnt_x[j < NCH ? j : 0], lstart[c]);
-                } else if (c < E + G) {
-                    const int g = c - E;
-                    v = xch_pack(gcnt[g][0] + gcnt[g][1] + gcnt[g][2] + gcnt[g][3], lgstart[g]);
-                } else if (c == E + G) {
-                    v = xch_pack(npairs, s_gpairs);
-                } else {
-                    v = xch_err_pack(s_err);
-                }
-                if (xt) xch_put(xt + (size_t)tile * rows + c, tag, v);
-                else xcopy[c] = v;
-            }
+            if (c < rows) xch_put(xt + (size_t)tile * rows + c, tag, own_value(c));
         }
     }
 
@@ -1249,92 +1251,104 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
         lg[k] = loff_g[g][wave] + __popcll(gball[g][wave] & below);
         li[k] = lstart[x] + lr[k];
     }
-    // The first round of the exchange reads (below) goes out now, overlapping
-    // the staging; by the time it is checked the other tiles, which publish at
-    // about the same time, have mostly landed.
-    const bool xch = xt != nullptr && !recount;   // uniform
-    const int n = ntiles * rows;                  // table entries
-    const __amdgpu_buffer_rsrc_t tab = __builtin_amdgcn_make_buffer_rsrc(xt, (short)0, n * 8, 0x00020000);
-    u32x4 v[kXR];
-    auto issue = [&](int q0) {
-        // The offset passes through an empty asm each time, so the compiler
-        // cannot take the reads as loop-invariant and hoist them out of the
-        // wait (the buffer-load builtin counts as a plain read of its buffer).
-        // Reads past the table return 0 (not used).
-        int off = (q0 + tid * 2) * 8;
-        __asm__ volatile("" : "+v"(off));
-#pragma unroll
-        for (int i = 0; i < kXR; ++i)
-            v[i] = __builtin_amdgcn_raw_buffer_load_b128(tab, off + i * kLayoutTile * 16, 0, kCpolSc1);
-    };
-    if (xch) issue(0);
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
         if ((ok_k >> k) & 1u) s_src[li[k]] = (int32_t)(p0 + k);
 
-    // Every tile's values: the whole table (ntiles * rows entries, tile-major)
-    // in rounds of 16-byte reads of two entries, kXR per thread per round, all
-    // in flight together; a round is read again until each of its entries
-    // carries the tag or the wait runs out (both uniform per wave), and its
-    // values go to an LDS copy of the table. (Wide reads: 8-byte reads cost a
-    // workgroup about 25 ns each to issue. A 16-byte read racing with the
-    // 8-byte atomic stores of its two entries can see one old and one new,
-    // never half of an entry, both being single requests within one cache
-    // line.)
+    // Every tile's values of the column pairs this thread owns (columns 2p and
+    // 2p + 1, p = tid + j * 256), summed: a column's total, its offset (the
+    // tiles' prefixes summed) and its count in the tiles before this one. A
+    // pair is one 16-byte read per tile, and a wave reads consecutive pairs of
+    // one tile row; kXB tiles per round, their reads in flight together; a
+    // round is read again until each of its entries carries the tag or the
+    // wait runs out (both uniform per wave). Within a round the packed values
+    // are summed whole (no carry crosses a 16-bit field in 16 tiles). (A
+    // 16-byte read racing with the 8-byte atomic stores of its two entries can
+    // see one old and one new, never half of an entry, both being single
+    // requests within one cache line.) With one tile the values are this
+    // tile's own.
+    const int npair = rows / 2;
+    int ctot[2 * NPJ], coff[2 * NPJ], cpre[2 * NPJ];
+#pragma unroll
+    for (int q = 0; q < 2 * NPJ; ++q) ctot[q] = coff[q] = cpre[q] = 0;
     if (xch) {
+        const __amdgpu_buffer_rsrc_t tab =
+            __builtin_amdgcn_make_buffer_rsrc(xt, (short)0, ntiles * rows * 8, 0x00020000);
         const uint64_t t0 = wall_clock64();
         bool late = false;
-        for (int q0 = 0; q0 < n && !late; q0 += kXR * kLayoutTile * 2) {
-            if (q0 > 0) issue(q0);
-            while (true) {
-                uint32_t miss = 0;
 #pragma unroll
-                for (int i = 0; i < kXR; ++i) {
-                    const int q = q0 + (i * kLayoutTile + tid) * 2;
-                    miss |= (q < n ? v[i].y ^ tag : 0u) | (q + 1 < n ? v[i].w ^ tag : 0u);
-                }
-                if (__all(miss == 0)) break;
-                if (wall_clock64() - t0 > wait_ticks) {
-                    late = true;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-                issue(q0);
-            }
+        for (int j = 0; j < NPJ; ++j) {
+            if (j * kLayoutTile + wave * kWave < npair) {   // uniform per wave: some lane has a pair
+                const int pc = tid + j * kLayoutTile < npair ? tid + j * kLayoutTile : npair - 1;
+                for (int b0 = 0; b0 < ntiles && !late; b0 += kXB) {
+                    u32x4 v[kXB];
+                    while (true) {
+                        // The offset passes through an empty asm on each pass, so
+                        // the compiler cannot take the reads as loop-invariant and
+                        // hoist them out of the wait (the buffer-load builtin counts
+                        // as a plain read of its buffer).
+                        int off = pc * 16;
+                        __asm__ volatile("" : "+v"(off));
 #pragma unroll
-            for (int i = 0; i < kXR; ++i) {
-                const int q = q0 + (i * kLayoutTile + tid) * 2;
-                if (q < n) *reinterpret_cast<u32x2 *>(xcopy + q) = u32x2{v[i].x, v[i].z};
+                        for (int u = 0; u < kXB; ++u) {
+                            const int b = b0 + u < ntiles ? b0 + u : ntiles - 1;
+                            v[u] = __builtin_amdgcn_raw_buffer_load_b128(tab, off, b * rows * 8, kCpolSc1);
+                        }
+                        uint32_t miss = 0;
+#pragma unroll
+                        for (int u = 0; u < kXB; ++u)
+                            miss |= b0 + u < ntiles ? (v[u].y ^ tag) | (v[u].w ^ tag) : 0u;
+                        if (__all(miss == 0)) break;
+                        if (wall_clock64() - t0 > wait_ticks) {
+                            late = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                    uint32_t s0 = 0, s1 = 0, p0s = 0, p1s = 0;
+#pragma unroll
+                    for (int u = 0; u < kXB; ++u) {
+                        s0 += b0 + u < ntiles ? v[u].x : 0u;
+                        s1 += b0 + u < ntiles ? v[u].z : 0u;
+                        p0s += b0 + u < tile ? v[u].x : 0u;
+                        p1s += b0 + u < tile ? v[u].z : 0u;
+                    }
+                    ctot[2 * j] += (int)(s0 & 0xFFFFu);
+                    coff[2 * j] += (int)(s0 >> 16);
+                    cpre[2 * j] += (int)(p0s & 0xFFFFu);
+                    ctot[2 * j + 1] += (int)(s1 & 0xFFFFu);
+                    coff[2 * j + 1] += (int)(s1 >> 16);
+                    cpre[2 * j + 1] += (int)(p1s & 0xFFFFu);
+                }
             }
         }
         if (late) s_late = 1;
+    } else if (!recount) {
+#pragma unroll
+        for (int j = 0; j < NPJ; ++j) {
+            const int pc = tid + j * kLayoutTile;
+            if (pc < npair) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t w = own_value(2 * pc + h);
+                    ctot[2 * j + h] = (int)(w & 0xFFFFu);
+                    coff[2 * j + h] = (int)(w >> 16);
+                }
+            }
+        }
     }
     __syncthreads();
     const bool fell_back = s_late != 0;   // uniform
     if (!fell_back) {
-        // Column sums over the tiles: a column's total, offset (the sum of the
-        // tiles' prefixes) and the count of the tiles before this one.
-        const int nt = xt ? ntiles : 1;
+        // Each owned column's results: an expert's (group's) first receive row
+        // in this tile is its offset + its count in earlier tiles; tile 0
+        // writes the counts, offsets and status.
 #pragma unroll
-        for (int j = 0; j < NCOL; ++j) {
-            const int c = tid + j * kLayoutTile;
-            if (j * kLayoutTile + wave * kWave < rows) {   // uniform per wave: some lane has a column
-                const int cc = c < rows ? c : rows - 1;
-                int tot = 0, off = 0, pre = 0;   // the low field's sum, the high field's, the low field's before the tile
-                for (int b0 = 0; b0 < nt; b0 += 16) {   // 16 reads in flight (clamped, masked after)
-                    uint32_t w[16];
+        for (int j = 0; j < NPJ; ++j) {
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) w[u] = xcopy[(b0 + u < nt ? b0 + u : nt - 1) * rows + cc];
-                    uint32_t sum = 0, sp = 0;
-#pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        sum += b0 + u < nt ? w[u] : 0u;
-                        sp += b0 + u < tile ? w[u] : 0u;
-                    }
-                    tot += (int)(sum & 0xFFFFu);
-                    off += (int)(sum >> 16);
-                    pre += (int)(sp & 0xFFFFu);
-                }
+            for (int h = 0; h < 2; ++h) {
+                const int c = 2 * (tid + j * kLayoutTile) + h;
+                const int tot = ctot[2 * j + h], off = coff[2 * j + h], pre = cpre[2 * j + h];
                 if (c < E) {
                     base_e[c] = off + pre;
                     if (tile == 0) {
@@ -1466,7 +1480,7 @@ ExchangeFn pick_exchange(int K, int E)
 // kXchSlots streams per GPU. In host code `xch_tables` only names the symbol;
 // its address on each GPU comes from hipGetSymbolAddress (xch_slot).
 constexpr int kXchSlots = 8;
-constexpr size_t kXchEntries = (size_t)1 << 14;   // also the LDS copy's size: 64 KiB
+constexpr size_t kXchEntries = (size_t)1 << 16;   // 512 KiB per table
 __device__ __align__(256) uint64_t xch_tables[kXchSlots * kXchEntries];
 
 constexpr int kXchMaxDevices = 64;
@@ -1578,7 +1592,7 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
     // vector stores of the slot rows when the arrays allow them
     const auto a16 = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     const int vec = (a16(L.slot_e) && a16(L.slot_g) ? 1 : 0) | (G % 4 == 0 && a16(L.slot_tg) ? 2 : 0);
-    const int rows = E + G + 2;   // exchange table columns
+    const int rows = (E + G + 3) & ~1;   // exchange table columns (even)
     if (K <= 8 && ntiles <= tuning().layout_exchange_max_tiles && (size_t)ntiles * rows <= kXchEntries) {
         uint64_t *xt = nullptr;
         uint32_t tag = 0;
@@ -1589,8 +1603,7 @@ hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const L
         if (ntiles == 1 || xt) {
             const long long wt = tuning().base_wait_ticks;
             const size_t lds = (size_t)E * kWaves * sizeof(unsigned long long) +
-                               ((size_t)E * (kWaves + 2) + 2 * (size_t)rows) * sizeof(int) +
-                               ((size_t)(xt ? ntiles : 1) * rows + 2) * sizeof(uint32_t);
+                               ((size_t)E * (kWaves + 2) + 2 * (size_t)(E + G + 1)) * sizeof(int);
             const int xvec = vec | (a16(idx) ? 4 : 0);   // bit 2: index rows as 16-byte vectors (K % 4 == 0)
             hipLaunchKernelGGL(pick_exchange(K, E), dim3(ntiles), dim3(kLayoutTile), lds, stream, idx, T, K, E, G,
                                gmagic, ntiles, xt, tag, (uint64_t)(wt < 0 ? 0 : wt), wt < 0 ? 1 : 0, L, xvec);

@@ -168,9 +168,10 @@ int64_t moe_recv_rows_bound(int T, int K, int G, int mode);
  * required in every case (the one-launch forms below do not touch it).
  * stream: a hipStream_t (NULL = the null stream).
  * Forms. For K <= 8 the layout is one launch with a workgroup per tile of 256
- * tokens. When the tiles' table of (tiles * (E + G + 2)) entries fits 16384
- * (T <= 15616 at E = 256, G = 8) the workgroups learn one another's per-tile
- * counts through a table in library memory, one per stream on each GPU (8
+ * tokens. For up to 64 tiles (T <= 16384; always within the table's 65536
+ * entries of E + G + 2 columns, rounded up to even) the workgroups learn one
+ * another's per-tile counts through a table in library memory, one per
+ * stream on each GPU (8
  * streams per GPU get one; later streams, streams under graph capture and
  * hipStreamPerThread take the forms below): each entry carries the call's
  * number on its stream, so an entry of an earlier call or of a concurrent
