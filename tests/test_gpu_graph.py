@@ -33,11 +33,14 @@ def _u16_to_bf16_tensor(a):
 
 # (T, H, E, G, K, fused): fused = capture moe_layout_dispatch instead of the two calls
 # (one launch for the smallest batches; else the count kernel and a placing dispatch
-# whose workgroup 0 computes the offsets); moe_layout takes one launch up to
-# T * K = 16384 and count + place above (2500 x 8)
+# whose workgroup 0 computes the offsets). Under capture moe_layout does not use its
+# per-stream exchange tables (a replay would repeat the call's tag): one tile (T <= 256)
+# takes the one-launch kernel with nothing to exchange, larger batches one launch
+# counting every token per tile up to T * K = 16384 and count + place above (2500 x 8)
 CASES = [(700, 1024, 64, 8, 6, False), (300, 512, 32, 4, 8, True), (2000, 2048, 256, 8, 8, False),
          (2000, 2048, 256, 8, 8, True), (1500, 512, 64, 8, 6, True), (2500, 1024, 256, 8, 8, False),
-         (700, 1024, 64, 8, 8, True), (64, 2048, 8, 8, 2, True)]   # the last in one launch
+         (700, 1024, 64, 8, 8, True), (64, 2048, 8, 8, 2, True),   # the last in one launch
+         (200, 1024, 64, 8, 4, False)]
 
 
 @pytest.mark.parametrize("T,H,E,G,K,fused", CASES)
