@@ -7,18 +7,24 @@
 // fused into the conversion, packed e4m3 conversions, 128-bit loads, all
 // experts in one launch, edge tiles predicated per row with rows padded to 16.
 //
-// Design. A workgroup (256 threads) owns a segment of up to 256 rows of one
-// expert and 128 columns (see cast_transpose_cols_kernel), stores C as it
-// goes and writes its part of T_e from LDS at the end, in consecutive 16-byte
-// runs. C goes out with non-temporal stores and T with plain ones, the pair
-// measured fastest on MI355X. The workgroup finds its expert and segment from
-// a scan of per-expert segment counts over all experts (E <= 1024). Bound by
-// HBM: 2 bytes read and 2 written per element.
-// Measured at 4096 tokens x 7168, 256 experts (t4096) and at 4096 x 4096, 128
-// experts with Zipf routing (skew), against the earlier form with row tiles of
-// 128 rows x 512 columns: 180.6 against 185.0 us and 100.7 against 112.2 us;
-// HBM writes 484.3 MB for 483.9 MB of C and T (x1.001; the row tiles wrote
-// 514.4 MB, x1.063, their split T_e lines written back in parts).
+// Design. Two forms, picked by the rows per expert on average (the host knows
+// the row bound and E, not the counts): for at most 32, row tiles of 128 rows
+// x 512 columns (cast_transpose_kernel), whose pass shape follows a tile's few
+// rows; for more, column blocks (cast_transpose_cols_kernel), where a
+// workgroup owns up to 256 rows of one expert and 128 columns, stores C as it
+// goes and writes its part of T_e from LDS at the end in consecutive 16-byte
+// runs, so no T_e line is split between workgroups. C goes out with
+// non-temporal stores and T with plain ones, the pair measured fastest on
+// MI355X. A workgroup finds its expert and tile (segment) from a scan of
+// per-expert tile counts over all experts (E <= 1024). Bound by HBM: 2 bytes
+// read and 2 written per element.
+// Measured (µs; 4096 tokens x 7168, 256 experts / 4096 x 4096, 128 experts,
+// Zipf routing / 256 tokens x 7168, 256 experts): row tiles 185.0 / 112.2 /
+// 28.8, column blocks 180.6 / 100.7 / 86.9. At 4096 x 7168 the row tiles wrote
+// 514.4 MB to HBM for 483.9 MB of C and T (x1.063: an expert of more than 128
+// rows has its T_e rows split at the tile boundary, inside cache lines that
+// two workgroups, in general on two XCDs, write back in parts), the column
+// blocks 484.3 MB (x1.001).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -70,7 +76,187 @@ __device__ __forceinline__ bool ct_scan2(int va, int vb, bool flag, int *s, int 
     return any != 0;
 }
 
-// A workgroup owns a segment of up to 256 rows of one expert (all of its rows
+// Row-tile form, for experts of a few dozen rows: a workgroup owns a tile of
+// up to 128 rows of one expert (tiles never straddle experts) and the 512
+// columns of one column group, the 1-D grid running column groups fastest.
+// Threads work on items of 4 consecutive rows x 8 columns (four 16-byte
+// loads); the tile's padded row count picks the shape of a pass: Q row quads
+// (4..32, the power of two that covers the rows) by 256/Q column chunks, so a
+// tile of 16 rows covers its 512 columns in one pass and a full tile takes
+// eight passes of 64 columns. Each thread converts its item, stores four
+// 8-byte runs of C, and packs each column's 4 bytes into one 32-bit word of an
+// LDS tile [columns][Q + 1 words] (column c also shifted by c/8 words). After
+// a barrier each thread reads 16 rows of a column (4 words) and stores them as
+// one 16-byte run of T_e; padding rows come from zero inputs. The loads of
+// pass k+1 are issued before pass k is converted, and the LDS tile is
+// double-buffered, so one barrier per pass suffices. A T_e row is written by
+// one workgroup while its expert fits one tile; for more rows it is split
+// between two, which write the line at the split back in parts (the form
+// below is used then).
+constexpr int kCtRows = 128;        // rows per tile
+constexpr int kCtGroupCols = 512;   // columns per workgroup
+// LDS words of one tile buffer: max over Q in {4, 8, 16, 32} of
+// (2048 / Q) columns x (Q + 1) words, plus the c/8 shift
+constexpr int kCtLdsWords = 512 * 5 + 64;
+
+__global__ __launch_bounds__(kCtBS) void cast_transpose_kernel(
+    const u32x4 *__restrict__ x, int H, int E, int rows_bound, const int32_t *__restrict__ expert_offset,
+    const float *__restrict__ scale, uint8_t *__restrict__ c_out, uint8_t *__restrict__ t_out,
+    float *__restrict__ amax, int32_t *__restrict__ pad_offset)
+{
+    __shared__ int s_red[3 * kCtWaves];
+    __shared__ int s_info[5];   // expert, its first tile, its padded-row prefix, row offset, rows
+    __shared__ uint32_t s_t[2][kCtLdsWords];
+    __shared__ float s_amax[kCtWaves];
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    // 1-D grid, column group fastest: the workgroups in flight read whole rows
+    // of a compact window of tiles rather than one column slice of every row
+    const int ncg = (H + kCtGroupCols - 1) / kCtGroupCols;
+    const int tile = blockIdx.x / ncg, cg = blockIdx.x % ncg;
+
+    // Per-expert tile counts and padded row counts; thread owns experts
+    // tid*ept .. tid*ept+ept-1 (contiguous, so one scan gives the prefixes).
+    const int ept = (E + kCtBS - 1) / kCtBS;
+    int lo[kCtEpt], nn[kCtEpt], lt = 0, lp = 0;
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kCtEpt; ++j) {
+        const int e = tid * ept + j;
+        lo[j] = 0;
+        nn[j] = 0;
+        if (j < ept && e < E) {
+            // a layout's offsets rise from 0 to at most rows_bound, the rows x
+            // and C hold; any others (a layout not written for these sizes)
+            // stop the whole grid below, before any write
+            const int a = expert_offset[e], b = expert_offset[e + 1];
+            bad = bad || a < 0 || b < a || b > rows_bound;
+            lo[j] = a;
+            nn[j] = bad ? 0 : b - a;
+        }
+        lt += (nn[j] + kCtRows - 1) / kCtRows;
+        lp += (nn[j] + 15) / 16 * 16;
+    }
+    int rt, rp, tot_t, tot_p;
+    if (ct_scan2(lt, lp, bad, s_red, rt, rp, tot_t, tot_p)) return;   // uniform
+    const bool first = blockIdx.x == 0;
+#pragma unroll
+    for (int j = 0; j < kCtEpt; ++j) {
+        const int e = tid * ept + j;
+        const int nt = (nn[j] + kCtRows - 1) / kCtRows;
+        if (j < ept && e < E) {
+            if (first) pad_offset[e] = rp;
+            if (rt <= tile && tile < rt + nt) {   // exactly one thread owns the tile
+                s_info[0] = e;
+                s_info[1] = rt;
+                s_info[2] = rp;
+                s_info[3] = lo[j];
+                s_info[4] = nn[j];
+            }
+        }
+        rt += nt;
+        rp += (nn[j] + 15) / 16 * 16;
+    }
+    if (first && tid == 0) pad_offset[E] = tot_p;
+    if (tile >= tot_t) return;   // uniform: the grid covers the tile bound
+    __syncthreads();
+
+    const int e = s_info[0], o = s_info[3], n = s_info[4];
+    const int npad = (n + 15) / 16 * 16;
+    const int r0 = (tile - s_info[1]) * kCtRows;                   // first row of the tile
+    const int nrows = n - r0 < kCtRows ? n - r0 : kCtRows;         // valid rows
+    const int prows = npad - r0 < kCtRows ? npad - r0 : kCtRows;   // rows of T to write (x16)
+    const float s = scale[e];
+    const int hv = H / 8;   // 16-byte chunks per row
+    uint8_t *te = t_out + (size_t)H * s_info[2];
+    const u32x4 *xt = x + (size_t)(o + r0) * hv;
+    uint8_t *ct_rows = c_out + (size_t)(o + r0) * H;
+
+    // pass shape: Q = 2^lq row quads, C = 2^lc column chunks, W = 8C columns
+    const int nq = prows / 4;
+    const int lq = nq <= 4 ? 2 : nq <= 8 ? 3 : nq <= 16 ? 4 : 5;
+    const int lc = 8 - lq, lr = lq - 2;   // run blocks of 16 rows per column: 2^lr
+    const int Q = 1 << lq, W = 8 << lc;
+    const int q = tid >> lc, cc = tid & ((1 << lc) - 1);
+    const int gcol = cg * kCtGroupCols;
+    const int ncols = H - gcol < kCtGroupCols ? H - gcol : kCtGroupCols;
+    const int passes = (ncols + W - 1) / W;
+
+    auto load = [&](u32x4(&v)[4], int k) {
+        const int ch = ((gcol + k * W) >> 3) + cc;   // chunk index within the row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 4 * q + i;
+            v[i] = u32x4{0, 0, 0, 0};
+            if (ch < hv && row < nrows) v[i] = __builtin_nontemporal_load(xt + (size_t)row * hv + ch);
+        }
+    };
+
+    float a = 0.f;
+    u32x4 cur[4], nxt[4];
+    load(cur, 0);
+    for (int k = 0; k < passes; ++k) {
+        if (k + 1 < passes) load(nxt, k + 1);
+        uint32_t *buf = s_t[k & 1];
+        const int c0 = gcol + k * W;
+        const int ch = (c0 >> 3) + cc;
+        uint32_t b[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float f[8];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                f[2 * m] = bf16_lo(cur[i][m]);
+                f[2 * m + 1] = bf16_hi(cur[i][m]);
+            }
+#pragma unroll
+            for (int m = 0; m < 8; ++m) a = amax_step(a, f[m]);
+            const int p0 = (int)e4m3x4(f[0], f[1], f[2], f[3], s);
+            const int p1 = (int)e4m3x4(f[4], f[5], f[6], f[7], s);
+            b[i][0] = (uint32_t)p0;
+            b[i][1] = (uint32_t)p1;
+            const int row = 4 * q + i;
+            if (ch < hv && row < nrows)
+                __builtin_nontemporal_store(u32x2{(uint32_t)p0, (uint32_t)p1},
+                                            reinterpret_cast<u32x2 *>(ct_rows + (size_t)row * H + 8 * ch));
+        }
+        // column 8cc + m holds byte m of each row's 8; 4 rows -> one word
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int w = m >> 2, sh = (m & 3) * 8;
+            const uint32_t word = ((b[0][w] >> sh) & 0xFFu) | (((b[1][w] >> sh) & 0xFFu) << 8) |
+                                  (((b[2][w] >> sh) & 0xFFu) << 16) | (((b[3][w] >> sh) & 0xFFu) << 24);
+            buf[(8 * cc + m) * (Q + 1) + cc + q] = word;
+        }
+        __syncthreads();
+        // T: W columns x 2^lr runs of 16 rows = 512 runs, two per thread
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int p = u * kCtBS + tid;
+            const int col = p >> lr, rb = p & ((1 << lr) - 1);
+            if (c0 + col < H && rb * 16 < prows) {
+                const uint32_t *src = buf + col * (Q + 1) + (col >> 3) + rb * 4;
+                const u32x4 run = u32x4{src[0], src[1], src[2], src[3]};
+                store16<false>(reinterpret_cast<u32x4 *>(te + (size_t)(c0 + col) * npad + r0 + rb * 16), run);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+    }
+    // amax: workgroup max, one atomic per workgroup (max of non-negative
+    // floats = max of their bit patterns as unsigned integers)
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+    if (lane == 0) s_amax[wave] = a;
+    __syncthreads();
+    if (tid == 0) {
+        float m = s_amax[0];
+#pragma unroll
+        for (int w = 1; w < kCtWaves; ++w) m = fmaxf(m, s_amax[w]);
+        atomicMax(reinterpret_cast<unsigned int *>(amax + e), __float_as_uint(m));
+    }
+}
+
+// Column-block form, for experts of more rows. A workgroup owns a segment of up to 256 rows of one expert (all of its rows
 // for nearly every expert at uniform routing) and 128 columns. It walks the
 // segment 64 rows at a time, storing C as it goes (whole 128-byte segments of
 // a row), and builds the segment's part of T_e (128 columns x up to 256 rows)
@@ -254,6 +440,15 @@ hipError_t launch_cast_transpose(const void *x, int64_t rows_bound, int H, int E
                                  const int32_t *expert_offset, const float *scale, void *c_out,
                                  void *t_out, float *amax, int32_t *pad_offset, hipStream_t stream)
 {
+    if (rows_bound <= (int64_t)32 * E) {   // a few dozen rows per expert: row tiles
+        const int64_t tiles = (rows_bound + kCtRows - 1) / kCtRows + E;   // >= sum of ceil(n_e / 128)
+        const int64_t blocks = tiles * ((H + kCtGroupCols - 1) / kCtGroupCols);
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;   // the 1-D grid's limit
+        hipLaunchKernelGGL(cast_transpose_kernel, dim3((unsigned)blocks), dim3(kCtBS), 0, stream,
+                           (const u32x4 *)x, H, E, (int)rows_bound, expert_offset, scale, (uint8_t *)c_out,
+                           (uint8_t *)t_out, amax, pad_offset);
+        return hipGetLastError();
+    }
     const int64_t segs = (rows_bound + kCbSeg - 1) / kCbSeg + E;   // >= sum of ceil(n_e / 256)
     const int64_t blocks = segs * ((H + kCbCols - 1) / kCbCols);
     if (blocks > INT32_MAX) return hipErrorInvalidValue;   // the 1-D grid's limit
