@@ -45,15 +45,7 @@ __device__ __forceinline__ bool ct_scan2(int va, int vb, bool flag, int *s, int 
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const bool wflag = __any(flag);
-    int xa = va, xb = vb;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int ya = __shfl_up(xa, o), yb = __shfl_up(xb, o);
-        if (lane >= o) {
-            xa += ya;
-            xb += yb;
-        }
-    }
+    const int xa = wave_incl_scan(va), xb = wave_incl_scan(vb);
     if (lane == kWave - 1) {
         s[wave] = xa;
         s[kCtWaves + wave] = xb;

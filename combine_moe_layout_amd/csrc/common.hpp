@@ -84,6 +84,24 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane)
     return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in registers by DPP moves:
+// shifts by 1, 2, 4 and 8 lanes inside each row of 16 (a Hillis-Steele scan of
+// the row; lanes shifted in from outside the row read 0), then the last lane of
+// row 0 added into rows 1 and 3 (row_bcast:15) and the last lane of row 1, by
+// then the total of rows 0-1, into rows 2 and 3 (row_bcast:31). Each step is a
+// VALU operation, not an LDS round trip as a lane shuffle is. Every lane of the
+// wave must be active.
+__device__ __forceinline__ int wave_incl_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);    // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);    // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);    // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);    // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
+    return x;
+}
+
 // Group of expert x, floor(x / epg), without a division: a multiply-high by
 // magic = floor(2^32 / epg) + 1 (for x < 2^16 the product's error is below
 // 2^-16 and cannot cross an integer), or x itself when epg = 1 (magic = 0;

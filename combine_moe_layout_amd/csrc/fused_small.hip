@@ -113,12 +113,7 @@ __global__ __launch_bounds__(kFusedBS) void fused_layout_dispatch_kernel(
             c[j] = (j < ept && e < E) ? s_cnt[e] : 0;
             local += c[j];
         }
-        int incl = local;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(local);
         if (lane == kWave - 1) s_red[wave] = incl;
         __syncthreads();
         int base = 0;
@@ -134,12 +129,7 @@ __global__ __launch_bounds__(kFusedBS) void fused_layout_dispatch_kernel(
     }
     if (wave == 0) {
         const int gt = lane < G ? s_gcnt[lane] : 0;
-        int incl = gt;
-#pragma unroll
-        for (int o = 1; o < kMaxG; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(gt);
         if (lane < G) s_goff[lane] = incl - gt;
         if (lane == G - 1) s_goff[G] = incl;
     }

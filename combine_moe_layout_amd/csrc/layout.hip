@@ -315,12 +315,7 @@ __device__ __forceinline__ void tile_write_recv_src_e(int npairs, const int32_t 
 __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave_tot, int *total)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     __syncthreads();   // s_wave_tot free (a previous scan may still be reading it)
     if (lane == kWave - 1) s_wave_tot[wave] = x;
     __syncthreads();
@@ -502,12 +497,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_place_kernel(
     // Group offsets: an exclusive scan over the G <= 32 groups in wave 0.
     if (wave == 0) {
         const int gt = lane < G ? tot_g[lane] : 0;
-        int incl = gt;
-#pragma unroll
-        for (int o = 1; o < kMaxG; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(gt);
         if (lane < G) {
             const int goff = incl - gt;
             if (tile == 0) {
@@ -607,12 +597,7 @@ constexpr int kFinWaves = kFinBS / kWave;
 __device__ __forceinline__ int fin_scan(int v, int *s_wave_tot, int &total)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == kWave - 1) s_wave_tot[wave] = x;
     __syncthreads();
     int base = 0, all = 0;
@@ -716,12 +701,7 @@ __global__ __launch_bounds__(kFinBS) void layout_finalize_kernel(
     if (tid == 0) L.expert_offset[E] = etot;
     if (wave == 0) {   // groups: an exclusive scan over the G <= 32 totals in wave 0
         const int gt = lane < G ? tg : 0;
-        int incl = gt;
-#pragma unroll
-        for (int o = 1; o < kMaxG; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(gt);
         if (lane < G) {
             const int goff = incl - gt;
             L.group_count[lane] = gt;
@@ -922,12 +902,7 @@ __global__ __launch_bounds__(kOpBS) void layout_onepass_kernel(
     if (wave == 0) {   // groups: an exclusive scan over the G <= 32 totals
         const int gbv = lane < G ? gb[lane] : 0;
         const int gt = lane < G ? gbv + ga[lane] : 0;
-        int incl = gt;
-#pragma unroll
-        for (int o = 1; o < kMaxG; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(gt);
         if (lane < G) {
             const int goff = incl - gt;
             if (tile == 0) {
@@ -1080,12 +1055,7 @@ __device__ void xch_fallback_offsets(int E, int G, int tile, const int *s_tot, c
     if (tile == 0 && tid == 0) L.expert_offset[E] = carry;
     if (wave == 0) {
         const int gt = lane < G ? s_tot[E + lane] : 0;
-        int incl = gt;
-#pragma unroll
-        for (int o = 1; o < kMaxG; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(gt);
         if (lane < G) {
             const int goff = incl - gt;
             if (tile == 0) {
@@ -1199,12 +1169,7 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
             if (lane < G) loff_g[gl][w] = r;
             r += lane < G ? gcnt[gl][w] : 0;
         }
-        int incl = r;
-#pragma unroll
-        for (int o = 1; o < kMaxG; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(r);
         if (lane < G) lgstart[lane] = incl - r;
         if (lane == kMaxG - 1) s_gpairs = incl;
     }

@@ -100,12 +100,7 @@ __device__ __forceinline__ void fin_column_bases(int col, const int (&v)[kFinBat
 __device__ __forceinline__ int fin_block_scan(int v, int *s_tot, int &total)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == kWave - 1) s_tot[wave] = x;
     __syncthreads();
     int base = 0, all = 0;
@@ -154,12 +149,7 @@ __device__ void finalize_role(const PlaceArgs &P)
         const bool live = lane < G;
         int v[kFinBatch];
         int tot = fin_column_sum(tab, rows, live ? E + lane : E + G, v);
-        int incl = live ? tot : 0;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int y = __shfl_up(incl, o);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(live ? tot : 0);
         if (live) {
             const int goff = incl - tot;
             P.L.group_count[lane] = tot;
@@ -195,12 +185,7 @@ __device__ __forceinline__ void self_bases(const PlaceArgs &P, int tile, bool va
     int tot = 0;
     for (int c = c0; c < c1; ++c)
         for (int b = 0; b < nt; ++b) tot += tab[(size_t)b * rows + c];
-    int incl = tot;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(tot);
     const int owner = valid ? e / cpl : 0;
     int x = __shfl(incl - tot, owner);
     if (valid) {
@@ -212,12 +197,7 @@ __device__ __forceinline__ void self_bases(const PlaceArgs &P, int tile, bool va
     int gt = 0;
     if (lane < G)
         for (int b = 0; b < nt; ++b) gt += tab[(size_t)b * rows + E + lane];
-    int gincl = gt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(gincl, o);
-        if (lane >= o) gincl += y;
-    }
+    const int gincl = wave_incl_scan(gt);
     if (hg) {
         int y = gincl - gt;
         for (int b = 0; b < tile; ++b) y += tab[(size_t)b * rows + E + lane];

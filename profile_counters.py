@@ -21,8 +21,8 @@ Each kernel instance gets the median over its launches of the bytes per launch
 the algorithmic bytes where bench.py defines them, the L2 hit rate, the average
 duration from the trace, and the hash of its kernel's code (bench.py's
 source_hash: comments and spacing aside). bench.py reports `traffic` only while
-that hash matches the current sources. Raw rocprofv3 output stays in OUTDIR; a
-markdown table of the result is printed.
+that hash matches the current sources. Raw rocprofv3 output stays in OUTDIR, with a
+copy of the resulting counters.json; a markdown table of the result is printed.
 """
 from __future__ import annotations
 
@@ -244,8 +244,9 @@ def main():
         K["t4096.cast_transpose"] = record("cast_transpose", pick(r, "cast_transpose_cols_kernel"), scale,
                                            (R * wl.H * 2, R * wl.H + npad * wl.H), top=51)
     doc["taken"] = time.strftime("%Y-%m-%d")
-    with open(path, "w") as f:
-        json.dump(doc, f, indent=1)
+    for p in (path, os.path.join(args.out, "counters.json")):   # the second beside the raw output
+        with open(p, "w") as f:
+            json.dump(doc, f, indent=1)
     print("| kernel instance | avg us | read MB | written MB | read ratio | write ratio | total ratio | L2 hit |")
     print("|---|---|---|---|---|---|---|---|")
     for k, v in K.items():
