@@ -64,7 +64,7 @@ def combine_bytes(T, H, K, R):
 KERNEL_SOURCES = {
     "dispatch": ("dispatch.hip", "place.hpp", "common.hpp", "kernels.hpp"),
     "combine": ("combine.hip", "common.hpp", "kernels.hpp"),
-    "layout": ("layout.hip", "common.hpp", "kernels.hpp"),
+    "layout": ("layout.hip", "layout_exchange.hip", "layout_tile.hpp", "common.hpp", "kernels.hpp"),
     "regroup": ("regroup.hip", "common.hpp", "kernels.hpp"),
     "cast_transpose": ("cast_transpose.hip", "common.hpp", "kernels.hpp"),
 }

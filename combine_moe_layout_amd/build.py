@@ -37,6 +37,14 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
+# Flags for one source file only. The exchange layout is a single short,
+# latency-bound launch: there kernel-argument preloading (the first arguments
+# arrive in SGPRs when a wave starts instead of by a scalar load at its entry)
+# measured 0.6 µs faster per call; the placing dispatch measured slower with it.
+FILE_FLAGS = {
+    "layout_exchange.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+}
+
 
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -51,8 +59,8 @@ def sources() -> list[str]:
 
 def _compile(src: str, save_temps: bool, build_dir: str = BUILD, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *(f"-D{d}" for d in defines), "-I", INCLUDE, "-I", CSRC, "-c",
-           src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *(f"-D{d}" for d in defines),
+           "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     if save_temps:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=build_dir)

@@ -60,6 +60,13 @@ struct LayoutPtrs {
 hipError_t launch_layout(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L,
                          int32_t *ws, hipStream_t stream);
 
+// The one-launch exchange layout (layout_exchange.hip) when it applies (top-k
+// <= 8, T >= 1, at most the tuned number of tiles, an exchange table free for
+// the stream); `launched` tells whether it ran. vec: bit 0 slot_e and slot_g,
+// bit 1 slot_tg (with G % 4 == 0), bit 2 the index rows, 16-byte aligned.
+hipError_t launch_layout_exchange(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L, int vec,
+                                  hipStream_t stream, bool &launched);
+
 // First half of the fused layout + dispatch for T > the small-batch limit
 // and top-k <= 8: the count kernel, which also sets every tile's bases in
 // the workspace to -1 and the status to 0; then, unless `finalize_in_dispatch`,

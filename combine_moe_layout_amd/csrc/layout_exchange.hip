@@ -1,0 +1,591 @@
+// One-launch layout with an exchange between tiles (moe_layout, top-k <= 8, up
+// to 64 tiles): the count and place kernels of layout.hip as one workgroup
+// per tile, which learns what it needs of the other tiles from a
+// table in library memory instead of from a second launch. The workgroup
+// counts its tile as the count kernel does (the per-(expert, wave) words stay
+// in LDS) and takes the tile's own exclusive prefix of its counts over the
+// experts, and over the groups. It writes, per column (E experts, G groups,
+// two summary columns: the tile's numbers of expert and group pairs, and its
+// error bits; one padding column to an even count), one 64-bit entry
+// tag << 32 | value with one atomic store, the value packing the tile's count
+// and its prefix. Each thread then reads two adjacent columns of every tile
+// (one 16-byte read per tile). Summed over
+// the tiles, the prefixes give each expert's offset, and the counts of the
+// tiles before this one its first receive row in this tile, so no scan is
+// left after the exchange. The tag is this call's number on its stream, which
+// the host never repeats while the table can hold entries of earlier calls;
+// an entry of an earlier call, or one that a concurrent call overwrote, never
+// carries it, so every value taken is this call's and nothing needs to be set
+// before the call. The reads are bounded (wait_ticks of the constant 100 MHz
+// clock); a workgroup whose wait runs out, or every workgroup when `recount`
+// is set, counts all T tokens itself instead (exact, O(T * K) per workgroup),
+// scans the totals, and reports MOE_STATUS_SYNC_FALLBACK if it is tile 0.
+// With one tile there is nothing to exchange and xt is NULL.
+//
+// This file is compiled with kernel-argument preloading (the first arguments
+// arrive in SGPRs when a wave starts, instead of by a scalar load at its
+// entry), which took about 0.6 µs off this kernel at 4096 tokens x top-8
+// (10.8 -> 10.2 µs per call); the other kernels stay without it, as the
+// placing dispatch measured slower with it.
+#include "moe_ep.h"
+
+#include "layout_tile.hpp"
+
+#include <mutex>
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ void xch_put(uint64_t *p, uint32_t tag, uint32_t v)
+{
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Packed values of a table entry, two 16-bit fields, so that a column is
+// summed over up to 16 tiles with one 32-bit add per entry and no carry
+// between the fields (a field is at most 256 * 8 per tile): count | prefix
+// << 16 for an expert or group column; expert pairs | group pairs << 16 for
+// the first summary column; for the second, the tile's error bits as counts,
+// bit 0 in the low byte and bit 1 in the next, so the sum tells whether any
+// tile had each bit.
+__device__ __forceinline__ uint32_t xch_pack(int lo, int hi) { return (uint32_t)lo | (uint32_t)hi << 16; }
+__device__ __forceinline__ uint32_t xch_err_pack(int err) { return (uint32_t)(err & 1) | (uint32_t)(err & 2) << 7; }
+__device__ __forceinline__ int xch_err_unpack(uint32_t s) { return ((s & 0xFFu) ? 1 : 0) | ((s & 0xFF00u) ? 2 : 0); }
+
+// Every token's valid entries counted into s_tot (all tiles) and s_pre (tiles
+// before `tile`), groups likewise in columns E.., error bits ORed into column
+// E + G: the counts the exchange would have given, from the indices alone.
+template <int KMAX, bool EXACT>
+__device__ void xch_recount(const int32_t *__restrict__ idx, int T, int Krt, int E, int G, uint32_t gmagic,
+                            int tile, int *s_tot, int *s_pre)
+{
+    const int K = EXACT ? KMAX : Krt;
+    const int tid = threadIdx.x, rows = E + G + 1;
+    for (int c = tid; c < rows; c += kLayoutTile) s_tot[c] = s_pre[c] = 0;
+    __syncthreads();
+#pragma unroll 1
+    for (int u0 = 0; u0 < T; u0 += kLayoutTile) {
+        const int u = u0 + tid;
+        const bool before = u0 < tile * kLayoutTile;   // uniform: tiles are whole multiples of 256
+        int e[KMAX];
+        load_row<KMAX>(idx, u, T, K, e);
+        mask_row<KMAX>(u, T, K, e);
+        const Inserted ins = classify_token<KMAX>(e, u < T, K, E, gmagic);
+        const uint32_t bad = ins.bad();
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k < K && u < T && !((bad >> k) & 1u)) {
+                atomicAdd(&s_tot[e[k]], 1);
+                if (before) atomicAdd(&s_pre[e[k]], 1);
+            }
+        }
+        for (int g = 0; g < G; ++g) {
+            if ((ins.gm >> g) & 1u) {
+                atomicAdd(&s_tot[E + g], 1);
+                if (before) atomicAdd(&s_pre[E + g], 1);
+            }
+        }
+        if (ins.err()) atomicOr(&s_tot[E + G], ins.err());
+    }
+    __syncthreads();
+}
+
+// The fallback's offsets: from the recounted totals and prefixes, scans over
+// the experts and groups give each column's offset; base = offset + the count
+// of earlier tiles; tile 0 writes the counts, offsets and status.
+template <int NCH>
+__device__ void xch_fallback_offsets(int E, int G, int tile, const int *s_tot, const int *s_pre, int *base_e,
+                                     int *base_g, int *s_wave_tot, const LayoutPtrs &L)
+{
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    int carry = 0;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        if (j * kLayoutTile < E) {   // uniform
+            const int x = j * kLayoutTile + tid;
+            const int tx = x < E ? s_tot[x] : 0;
+            int all;
+            const int excl = block_exclusive_scan(tx, s_wave_tot, &all);
+            if (x < E) {
+                base_e[x] = carry + excl + s_pre[x];
+                if (tile == 0) {
+                    L.expert_count[x] = tx;
+                    L.expert_offset[x] = carry + excl;
+                }
+            }
+            carry += all;
+        }
+    }
+    if (tile == 0 && tid == 0) L.expert_offset[E] = carry;
+    if (wave == 0) {
+        const int gt = lane < G ? s_tot[E + lane] : 0;
+        const int incl = wave_incl_scan(gt);
+        if (lane < G) {
+            const int goff = incl - gt;
+            if (tile == 0) {
+                L.group_count[lane] = gt;
+                L.group_offset[lane] = goff;
+            }
+            base_g[lane] = goff + s_pre[E + lane];
+        }
+        if (tile == 0 && lane == G - 1) L.group_offset[G] = incl;
+        if (tile == 0 && lane == 0) *L.status = s_tot[E + G] | MOE_STATUS_SYNC_FALLBACK;
+    }
+}
+
+template <int KMAX, bool EXACT, int NCH>
+__global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
+    const int32_t *__restrict__ idx, int T, int vec, int Krt, int E, int G, uint32_t gmagic, int ntiles,
+    uint64_t *__restrict__ xt, uint32_t tag, uint64_t wait_ticks, int recount, LayoutPtrs L)
+{
+    static_assert(KMAX <= 8, "the tile's entries are staged for at most 8 per token");
+    constexpr int NCOL = NCH + 1;                  // columns a thread publishes (E + G + 3 <= NCOL * 256)
+    constexpr int NPJ = NCH == 1 ? 1 : 3;          // column pairs a thread reads ((E + G + 3) / 2 <= NPJ * 256)
+    constexpr int kXB = 16;                        // tiles per round of reads
+    // dynamic LDS: emask [E][kWaves] u64; int loff_e [E][kWaves], lstart [E], base_e [E],
+    // s_tot [E+G+1], s_pre [E+G+1] (the fallback's)
+    extern __shared__ unsigned long long emask[];
+    int *loff_e = reinterpret_cast<int *>(emask + E * kWaves);   // rank base of (expert, wave) in the tile
+    int *lstart = loff_e + E * kWaves;                           // expert's first place in the tile's pair list
+    int *base_e = lstart + E;                                    // expert's first receive row of the tile
+    int *s_tot = base_e + E;
+    int *s_pre = s_tot + E + G + 1;
+    __shared__ int32_t s_src[kLayoutTile * KMAX];   // the tile's pair ids in slot order
+    __shared__ int32_t s_dst[kLayoutTile * KMAX];   // and their receive slots
+    __shared__ int s_wave_tot[kWaves];
+    __shared__ int gcnt[kMaxG][kWaves];
+    __shared__ int lgstart[kMaxG];
+    __shared__ int base_g[kMaxG];
+    __shared__ int loff_g[kMaxG][kWaves];
+    __shared__ uint64_t gball[kMaxG][kWaves];
+    __shared__ int s_err, s_late, s_gpairs;
+    const int K = EXACT ? KMAX : Krt;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int tile = blockIdx.x;
+    const int t = tile * kLayoutTile + tid;
+    const int rows = (E + G + 3) & ~1;   // table columns: experts, groups, pairs, error bits (+1: even)
+    const uint64_t below = lanemask_lt(lane);
+
+    // Count the tile (as the count kernel).
+    int e[KMAX];
+    if (EXACT && KMAX >= 4 && (vec & 4)) {   // 16-byte aligned index rows: K / 4 vector loads
+        const u32x4 *row = reinterpret_cast<const u32x4 *>(idx + (size_t)(t < T ? t : T - 1) * KMAX);
+#pragma unroll
+        for (int k = 0; k < KMAX; k += 4) {
+            const u32x4 q = row[k / 4];
+            e[k] = (int)q.x;
+            e[k + 1] = (int)q.y;
+            e[k + 2] = (int)q.z;
+            e[k + 3] = (int)q.w;
+        }
+    } else {
+        load_row<KMAX>(idx, t, T, K, e);
+    }
+    for (int i = tid; i < E * kWaves; i += kLayoutTile) emask[i] = 0ull;
+    if (tid == 0) {
+        s_err = 0;
+        s_late = recount;
+    }
+    __syncthreads();
+    mask_row<KMAX>(t, T, K, e);
+    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, gmagic, emask, wave, lane);
+    const uint32_t gm = ins.gm, bad = ins.bad();
+    if (t < T) L.tok_group_mask[t] = gm;
+    for (int g = 0; g < G; ++g) {
+        const uint64_t b = __ballot((gm >> g) & 1u);
+        if (lane == 0) {
+            gcnt[g][wave] = __popcll(b);
+            gball[g][wave] = b;
+        }
+    }
+    if (ins.err()) atomicOr(&s_err, ins.err());
+    __syncthreads();
+
+    // The tile's own layout: per (expert, wave) the rank base inside the tile
+    // and the expert's count; an exclusive scan of the counts over the experts
+    // (each expert's first place in the tile's slot-ordered pair list); per
+    // (group, wave) the rank base and over the groups the same scan.
+    int cnt_x[NCH], npairs = 0;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+        cnt_x[j] = 0;
+        if (j * kLayoutTile < E) {   // uniform
+            const int x = j * kLayoutTile + tid;
+            if (x < E) {
+                const unsigned long long *m = emask + x * kWaves;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    loff_e[x * kWaves + w] = cnt_x[j];
+                    cnt_x[j] += __popcll(m[w]);
+                }
+            }
+            int all;
+            const int lex = block_exclusive_scan(cnt_x[j], s_wave_tot, &all);
+            if (x < E) lstart[x] = npairs + lex;
+            npairs += all;
+        }
+    }
+    if (wave == 0) {   // groups: lane g < G
+        const int gl = lane < G ? lane : 0;
+        int r = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            if (lane < G) loff_g[gl][w] = r;
+            r += lane < G ? gcnt[gl][w] : 0;
+        }
+        const int incl = wave_incl_scan(r);
+        if (lane < G) lgstart[lane] = incl - r;
+        if (lane == kMaxG - 1) s_gpairs = incl;
+    }
+    __syncthreads();
+
+    // The tile's value of column c (see xch_pack).
+    auto own_value = [&](int c) -> uint32_t {
+        if (c < E) {
+            const unsigned long long *m = emask + c * kWaves;
+            return xch_pack(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]), lstart[c]);
+        }
+        if (c < E + G) {
+            const int g = c - E;
+            return xch_pack(gcnt[g][0] + gcnt[g][1] + gcnt[g][2] + gcnt[g][3], lgstart[g]);
+        }
+        if (c == E + G) return xch_pack(npairs, s_gpairs);
+        if (c == E + G + 1) return xch_err_pack(s_err);
+        return 0u;   // the padding column
+    };
+    // Publish it, for the columns c = tid + j * 256.
+    const bool xch = xt != nullptr && !recount;   // uniform
+    if (xch) {
+#pragma unroll
+        for (int j = 0; j < NCOL; ++j) {
+            const int c = tid + j * kLayoutTile;
+            if (c < rows) xch_put(xt + (size_t)tile * rows + c, tag, own_value(c));
+        }
+    }
+
+    // Each entry's rank inside the tile (lr among the tile's pairs of its
+    // expert, lg of its group) and its place li in the tile's pair list, where
+    // its pair id is staged. (LDS reads from clamped indices, masked
+    // afterwards: a read under a lane-dependent branch gets a branch and a
+    // wait of its own.)
+    const size_t p0 = (size_t)t * K;
+    uint32_t ok_k = 0;   // bit k: entry k counts
+    int lr[KMAX], lg[KMAX], li[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const bool v = t < T && k < K && !((bad >> k) & 1u);
+        ok_k |= v ? 1u << k : 0u;
+        const int x = v ? e[k] : 0, g = group_of(x, gmagic);
+        lr[k] = loff_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
+        lg[k] = loff_g[g][wave] + __popcll(gball[g][wave] & below);
+        li[k] = lstart[x] + lr[k];
+    }
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        if ((ok_k >> k) & 1u) s_src[li[k]] = (int32_t)(p0 + k);
+
+    // Every tile's values of the column pairs this thread owns (columns 2p and
+    // 2p + 1, p = tid + j * 256), summed: a column's total, its offset (the
+    // tiles' prefixes summed) and its count in the tiles before this one. A
+    // pair is one 16-byte read per tile, and a wave reads consecutive pairs of
+    // one tile row; kXB tiles per round, their reads in flight together; a
+    // round is read again until each of its entries carries the tag or the
+    // wait runs out (both uniform per wave). Within a round the packed values
+    // are summed whole (no carry crosses a 16-bit field in 16 tiles). (A
+    // 16-byte read racing with the 8-byte atomic stores of its two entries can
+    // see one old and one new, never half of an entry, both being single
+    // requests within one cache line.) With one tile the values are this
+    // tile's own.
+    const int npair = rows / 2;
+    int ctot[2 * NPJ], coff[2 * NPJ], cpre[2 * NPJ];
+#pragma unroll
+    for (int q = 0; q < 2 * NPJ; ++q) ctot[q] = coff[q] = cpre[q] = 0;
+    if (xch) {
+        const __amdgpu_buffer_rsrc_t tab =
+            __builtin_amdgcn_make_buffer_rsrc(xt, (short)0, ntiles * rows * 8, 0x00020000);
+        const uint64_t t0 = wall_clock64();
+        bool late = false;
+#pragma unroll
+        for (int j = 0; j < NPJ; ++j) {
+            if (j * kLayoutTile + wave * kWave < npair) {   // uniform per wave: some lane has a pair
+                const int pc = tid + j * kLayoutTile < npair ? tid + j * kLayoutTile : npair - 1;
+                for (int b0 = 0; b0 < ntiles && !late; b0 += kXB) {
+                    u32x4 v[kXB];
+                    while (true) {
+                        // The offset passes through an empty asm on each pass, so
+                        // the compiler cannot take the reads as loop-invariant and
+                        // hoist them out of the wait (the buffer-load builtin counts
+                        // as a plain read of its buffer).
+                        int off = pc * 16;
+                        __asm__ volatile("" : "+v"(off));
+#pragma unroll
+                        for (int u = 0; u < kXB; ++u) {
+                            const int b = b0 + u < ntiles ? b0 + u : ntiles - 1;
+                            v[u] = __builtin_amdgcn_raw_buffer_load_b128(tab, off, b * rows * 8, kCpolSc1);
+                        }
+                        uint32_t miss = 0;
+#pragma unroll
+                        for (int u = 0; u < kXB; ++u)
+                            miss |= b0 + u < ntiles ? (v[u].y ^ tag) | (v[u].w ^ tag) : 0u;
+                        if (__all(miss == 0)) break;
+                        if (wall_clock64() - t0 > wait_ticks) {
+                            late = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                    uint32_t s0 = 0, s1 = 0, p0s = 0, p1s = 0;
+#pragma unroll
+                    for (int u = 0; u < kXB; ++u) {
+                        s0 += b0 + u < ntiles ? v[u].x : 0u;
+                        s1 += b0 + u < ntiles ? v[u].z : 0u;
+                        p0s += b0 + u < tile ? v[u].x : 0u;
+                        p1s += b0 + u < tile ? v[u].z : 0u;
+                    }
+                    ctot[2 * j] += (int)(s0 & 0xFFFFu);
+                    coff[2 * j] += (int)(s0 >> 16);
+                    cpre[2 * j] += (int)(p0s & 0xFFFFu);
+                    ctot[2 * j + 1] += (int)(s1 & 0xFFFFu);
+                    coff[2 * j + 1] += (int)(s1 >> 16);
+                    cpre[2 * j + 1] += (int)(p1s & 0xFFFFu);
+                }
+            }
+        }
+        if (late) s_late = 1;
+    } else if (!recount) {
+#pragma unroll
+        for (int j = 0; j < NPJ; ++j) {
+            const int pc = tid + j * kLayoutTile;
+            if (pc < npair) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t w = own_value(2 * pc + h);
+                    ctot[2 * j + h] = (int)(w & 0xFFFFu);
+                    coff[2 * j + h] = (int)(w >> 16);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const bool fell_back = s_late != 0;   // uniform
+    if (!fell_back) {
+        // Each owned column's results: an expert's (group's) first receive row
+        // in this tile is its offset + its count in earlier tiles; tile 0
+        // writes the counts, offsets and status.
+#pragma unroll
+        for (int j = 0; j < NPJ; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = 2 * (tid + j * kLayoutTile) + h;
+                const int tot = ctot[2 * j + h], off = coff[2 * j + h], pre = cpre[2 * j + h];
+                if (c < E) {
+                    base_e[c] = off + pre;
+                    if (tile == 0) {
+                        L.expert_count[c] = tot;
+                        L.expert_offset[c] = off;
+                    }
+                } else if (c < E + G) {
+                    base_g[c - E] = off + pre;
+                    if (tile == 0) {
+                        L.group_count[c - E] = tot;
+                        L.group_offset[c - E] = off;
+                    }
+                } else if (c == E + G && tile == 0) {
+                    L.expert_offset[E] = tot;
+                    L.group_offset[G] = off;
+                } else if (c == E + G + 1 && tile == 0) {
+                    *L.status = xch_err_unpack((uint32_t)tot);
+                }
+            }
+        }
+    } else {
+        xch_recount<KMAX, EXACT>(idx, T, K, E, G, gmagic, tile, s_tot, s_pre);
+        xch_fallback_offsets<NCH>(E, G, tile, s_tot, s_pre, base_e, base_g, s_wave_tot, L);
+    }
+    __syncthreads();   // base_e, base_g
+
+    // Slots: base + rank inside the tile.
+    if (t < T) {
+        int se[KMAX], sg[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            const bool v = (ok_k >> k) & 1u;
+            const int x = v ? e[k] : 0;
+            const int be = base_e[x], bg = base_g[group_of(x, gmagic)];
+            se[k] = v ? be + lr[k] : -1;
+            sg[k] = v ? bg + lg[k] : -1;
+        }
+        if (EXACT && (vec & 1)) {   // 16-byte aligned slot arrays, K in {2, 4, 8}
+            if constexpr (KMAX == 2) {
+                *reinterpret_cast<u32x2 *>(L.slot_e + p0) = u32x2{(uint32_t)se[0], (uint32_t)se[1]};
+                *reinterpret_cast<u32x2 *>(L.slot_g + p0) = u32x2{(uint32_t)sg[0], (uint32_t)sg[1]};
+            } else {
+#pragma unroll
+                for (int k = 0; k < KMAX; k += 4) {
+                    *reinterpret_cast<u32x4 *>(L.slot_e + p0 + k) =
+                        u32x4{(uint32_t)se[k], (uint32_t)se[k + 1], (uint32_t)se[k + 2], (uint32_t)se[k + 3]};
+                    *reinterpret_cast<u32x4 *>(L.slot_g + p0 + k) =
+                        u32x4{(uint32_t)sg[k], (uint32_t)sg[k + 1], (uint32_t)sg[k + 2], (uint32_t)sg[k + 3]};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (k < K) {
+                    L.slot_e[p0 + k] = se[k];
+                    L.slot_g[p0 + k] = sg[k];
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if ((ok_k >> k) & 1u) s_dst[li[k]] = se[k];
+        int32_t *tg = L.slot_tg + (size_t)t * G;
+        for (int g0 = 0; g0 < G; g0 += 4) {
+            int r4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int g = g0 + u < kMaxG ? g0 + u : kMaxG - 1;
+                const int r = base_g[g] + loff_g[g][wave] + __popcll(gball[g][wave] & below);
+                r4[u] = g0 + u < G && ((gm >> (g0 + u)) & 1u) ? r : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (r4[u] >= 0) L.recv_src_g[r4[u]] = t;
+            if (vec & 2) {   // G % 4 == 0 and slot_tg 16-byte aligned
+                *reinterpret_cast<u32x4 *>(tg + g0) = u32x4{(uint32_t)r4[0], (uint32_t)r4[1], (uint32_t)r4[2], (uint32_t)r4[3]};
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (g0 + u < G) tg[g0 + u] = r4[u];
+            }
+        }
+    }
+    __syncthreads();
+    tile_write_recv_src_e(npairs, s_src, s_dst, L.recv_src_e, tid, kLayoutTile);
+}
+
+using ExchangeFn = void (*)(const int32_t *, int, int, int, int, int, uint32_t, int, uint64_t *, uint32_t, uint64_t,
+                            int, LayoutPtrs);
+
+template <int NCH>
+ExchangeFn pick_exchange_n(int K)
+{
+    switch (K) {
+    case 2: return layout_exchange_kernel<2, true, NCH>;
+    case 4: return layout_exchange_kernel<4, true, NCH>;
+    case 8: return layout_exchange_kernel<8, true, NCH>;
+    default: return layout_exchange_kernel<8, false, NCH>;
+    }
+}
+
+ExchangeFn pick_exchange(int K, int E)
+{
+    return E <= kLayoutTile ? pick_exchange_n<1>(K) : pick_exchange_n<kMaxEChunks>(K);
+}
+
+// Exchange tables of the one-launch layout, in library memory (zero when the
+// library is loaded): one table of kXchEntries 64-bit entries for each of up to
+// kXchSlots streams per GPU. In host code `xch_tables` only names the symbol;
+// its address on each GPU comes from hipGetSymbolAddress (xch_slot).
+constexpr int kXchSlots = 8;
+constexpr size_t kXchEntries = (size_t)1 << 16;   // 512 KiB per table
+__device__ __align__(256) uint64_t xch_tables[kXchSlots * kXchEntries];
+
+constexpr int kXchMaxDevices = 64;
+struct XchDevice {
+    uint64_t *tables = nullptr;        // address of xch_tables on this GPU
+    hipStream_t stream[kXchSlots] = {};
+    uint32_t seq[kXchSlots] = {};      // the last tag given out on each stream's table
+    int used = 0;
+};
+std::mutex g_xch_mu;
+XchDevice g_xch[kXchMaxDevices];
+
+// The exchange table of `stream` and this call's tag on it: the stream's
+// previous tag + 1. Calls on one stream run in order, so a table is never
+// used by two calls at once unless the caller reuses a stream handle across
+// threads or devices in ways HIP does not order; even then an entry is only
+// taken when it carries the reader's own tag, so a clash costs a timed-out
+// wait, never a wrong count. *xt stays NULL (the caller takes the two-launch
+// layout) for a stream under graph capture (a replay would repeat the tag),
+// for the per-thread default stream (its calls from different threads are not
+// ordered) and for streams beyond kXchSlots on one GPU.
+hipError_t xch_slot(hipStream_t stream, uint64_t **xt, uint32_t *tag)
+{
+    *xt = nullptr;
+    if (stream == hipStreamPerThread) return hipSuccess;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();   // not ours to report; take the two-launch form
+        return hipSuccess;
+    }
+    if (cs != hipStreamCaptureStatusNone) return hipSuccess;
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t sd = -1;
+        if ((e = hipStreamGetDevice(stream, &sd)) != hipSuccess) return e;
+        dev = sd;
+    }
+    if (dev < 0 || dev >= kXchMaxDevices) return hipSuccess;
+    std::lock_guard<std::mutex> lock(g_xch_mu);
+    XchDevice &d = g_xch[dev];
+    if (!d.tables) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(xch_tables));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        d.tables = static_cast<uint64_t *>(p);
+    }
+    int s = 0;
+    while (s < d.used && d.stream[s] != stream) ++s;
+    if (s == d.used) {
+        if (d.used == kXchSlots) return hipSuccess;
+        d.stream[s] = stream;
+        d.seq[s] = 0;
+        ++d.used;
+    }
+    uint64_t *tab = d.tables + (size_t)s * kXchEntries;
+    if (d.seq[s] == 0xFFFFFFFFu) {   // every tag used: clear the table in stream order and start again
+        if ((e = hipMemsetAsync(tab, 0, sizeof(uint64_t) * kXchEntries, stream)) != hipSuccess) return e;
+        d.seq[s] = 0;
+    }
+    *tag = ++d.seq[s];
+    *xt = tab;
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_layout_exchange(const int32_t *idx, int T, int K, int E, int G, const LayoutPtrs &L, int vec,
+                                  hipStream_t stream, bool &launched)
+{
+    launched = false;
+    const int ntiles = layout_tiles(T);
+    const int rows = (E + G + 3) & ~1;   // exchange table columns (even)
+    if (T == 0 || K > 8 || ntiles > tuning().layout_exchange_max_tiles || (size_t)ntiles * rows > kXchEntries)
+        return hipSuccess;
+    uint64_t *xt = nullptr;
+    uint32_t tag = 0;
+    if (ntiles > 1) {
+        const hipError_t e = xch_slot(stream, &xt, &tag);
+        if (e != hipSuccess || !xt) return e;
+    }
+    const long long wt = tuning().base_wait_ticks;
+    const size_t lds = (size_t)E * kWaves * sizeof(unsigned long long) +
+                       ((size_t)E * (kWaves + 2) + 2 * (size_t)(E + G + 1)) * sizeof(int);
+    hipLaunchKernelGGL(pick_exchange(K, E), dim3(ntiles), dim3(kLayoutTile), lds, stream, idx, T, vec, K, E, G,
+                       group_magic(E, G), ntiles, xt, tag, (uint64_t)(wt < 0 ? 0 : wt), wt < 0 ? 1 : 0, L);
+    launched = true;
+    return hipGetLastError();
+}
+
+}  // namespace moe
