@@ -158,6 +158,23 @@ def time_calls(fns, iters, flush=None):
             for j in range(len(fns))]
 
 
+def time_stream(fn, n=100, lead=20):
+    """µs per call of fn issued n times back to back between two events, after `lead`
+    calls that fill the queue (the host issues a call faster than the GPU runs it,
+    so the GPU never waits for the host): what a call costs in a stream of work,
+    without the fixed cost that a pair of events around each call adds."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(lead):
+        fn()
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
 def host_bits(t):
     """A device tensor's bytes on the host, as unsigned integers of its element size."""
     import numpy as np
@@ -759,7 +776,9 @@ def _layout_host(L):
 
 def workload_table(moe, names=WORKLOAD_NAMES, it=50, oracle_threads=0):
     """Per-workload timings of every call in both receive layouts (median µs over `it`
-    event-timed calls; GB/s = algorithmic bytes / median), the per-expert step
+    event-timed calls; GB/s = algorithmic bytes / median; for the layout also the µs
+    per call in a stream of back-to-back calls, `layout_us_stream`, since a pair of
+    events around one short call adds a fixed cost of its own), the per-expert step
     replayed from a captured HIP graph (no host launch cost), and, with
     oracle_threads > 0, both oracle builds timed per call on the same inputs and the
     GPU's outputs of every call checked against the oracle's (`parity`). Each workload
@@ -781,7 +800,8 @@ def workload_table(moe, names=WORKLOAD_NAMES, it=50, oracle_threads=0):
         R, P = int(L.expert_offset[E].item()), int(L.group_offset[G].item())
         t_lay = time_calls([lay], it)[0]
         row = {"T": T, "H": H, "E": E, "G": G, "K": K, "routing": wl.routing, "dtype": dt,
-               "layout_us": round(stats(t_lay)["median"], 2)}
+               "layout_us": round(stats(t_lay)["median"], 2),
+               "layout_us_stream": round(min(time_stream(lay) for _ in range(3)), 2)}
         gpu = {"L": _layout_host(L)}
         cstats = {"layout": (stats(t_lay), layout_bytes(T, K, E, G, P))}
         for mode, nrows in (("expert", R), ("group", P)):
