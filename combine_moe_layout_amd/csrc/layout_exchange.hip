@@ -2,9 +2,9 @@
 // to 64 tiles): the count and place kernels of layout.hip as one workgroup
 // per tile, which learns what it needs of the other tiles from a
 // table in library memory instead of from a second launch. The workgroup
-// counts its tile as the count kernel does (the per-(expert, wave) words stay
-// in LDS) and takes the tile's own exclusive prefix of its counts over the
-// experts, and over the groups. It writes, per column (E experts, G groups,
+// counts its tile with per-(expert, wave) words in LDS as the count kernel
+// does (with two lanes per token, below) and takes the tile's own exclusive
+// prefix of its counts over the experts, and over the groups. It writes, per column (E experts, G groups,
 // two summary columns: the tile's numbers of expert and group pairs, and its
 // error bits; one padding column to an even count), one 64-bit entry
 // tag << 32 | value with one atomic store, the value packing the tile's count
@@ -26,7 +26,9 @@
 // arrive in SGPRs when a wave starts, instead of by a scalar load at its
 // entry), which took about 0.6 µs off this kernel at 4096 tokens x top-8
 // (10.8 -> 10.2 µs per call); the other kernels stay without it, as the
-// placing dispatch measured slower with it.
+// placing dispatch measured slower with it. Two lanes per token (each with
+// half the entries to insert, rank and place) then took it to 9.8 µs; one
+// lane per token with 4 waves had half as many threads for the same work.
 #include "moe_ep.h"
 
 #include "layout_tile.hpp"
@@ -53,6 +55,39 @@ __device__ __forceinline__ uint32_t xch_pack(int lo, int hi) { return (uint32_t)
 __device__ __forceinline__ uint32_t xch_err_pack(int err) { return (uint32_t)(err & 1) | (uint32_t)(err & 2) << 7; }
 __device__ __forceinline__ int xch_err_unpack(uint32_t s) { return ((s & 0xFFu) ? 1 : 0) | ((s & 0xFF00u) ? 2 : 0); }
 
+// The workgroup: two lanes per token of the 256-token tile, kXT = 512
+// threads in 8 waves of 32 tokens. Lane l of a wave takes token l % 32 of the
+// wave and half l / 32 of its entries (k in [h * KMAX / 2, (h + 1) * KMAX / 2)),
+// so each lane inserts, ranks and places half of a token's entries; both lanes
+// of a token hold its whole index row, so the repeats of an entry are still
+// found in registers. The LDS words are 32-bit, one per (expert, wave), bit j
+// for token j of the wave; the group words come from ballots over the lanes of
+// the first half. Rank of an entry inside the tile = popcounts of its expert's
+// words of earlier waves + popcount of its own wave's word below bit j: the
+// token-ascending order, as with one lane per token.
+constexpr int kXT = 2 * kLayoutTile;
+constexpr int kXW = kXT / kWave;   // 8
+
+// Exclusive prefix sum over the kXT threads; *total gets the sum. `first`:
+// no earlier scan may still be reading s_wave_tot.
+__device__ __forceinline__ int xch_block_scan(int v, int *s_wave_tot, int *total, bool first = false)
+{
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int x = wave_incl_scan(v);
+    if (!first) __syncthreads();   // s_wave_tot free (a previous scan may still be reading it)
+    if (lane == kWave - 1) s_wave_tot[wave] = x;
+    __syncthreads();
+    int base = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kXW; ++w) {
+        const int c = s_wave_tot[w];
+        base += w < wave ? c : 0;
+        all += c;
+    }
+    *total = all;
+    return base + x - v;
+}
+
 // Every token's valid entries counted into s_tot (all tiles) and s_pre (tiles
 // before `tile`), groups likewise in columns E.., error bits ORed into column
 // E + G: the counts the exchange would have given, from the indices alone.
@@ -62,12 +97,12 @@ __device__ void xch_recount(const int32_t *__restrict__ idx, int T, int Krt, int
 {
     const int K = EXACT ? KMAX : Krt;
     const int tid = threadIdx.x, rows = E + G + 1;
-    for (int c = tid; c < rows; c += kLayoutTile) s_tot[c] = s_pre[c] = 0;
+    for (int c = tid; c < rows; c += kXT) s_tot[c] = s_pre[c] = 0;
     __syncthreads();
 #pragma unroll 1
-    for (int u0 = 0; u0 < T; u0 += kLayoutTile) {
+    for (int u0 = 0; u0 < T; u0 += kXT) {
         const int u = u0 + tid;
-        const bool before = u0 < tile * kLayoutTile;   // uniform: tiles are whole multiples of 256
+        const bool before = u < tile * kLayoutTile;
         int e[KMAX];
         load_row<KMAX>(idx, u, T, K, e);
         mask_row<KMAX>(u, T, K, e);
@@ -94,19 +129,19 @@ __device__ void xch_recount(const int32_t *__restrict__ idx, int T, int Krt, int
 // The fallback's offsets: from the recounted totals and prefixes, scans over
 // the experts and groups give each column's offset; base = offset + the count
 // of earlier tiles; tile 0 writes the counts, offsets and status.
-template <int NCH>
+template <int NX>
 __device__ void xch_fallback_offsets(int E, int G, int tile, const int *s_tot, const int *s_pre, int *base_e,
                                      int *base_g, int *s_wave_tot, const LayoutPtrs &L)
 {
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     int carry = 0;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        if (j * kLayoutTile < E) {   // uniform
-            const int x = j * kLayoutTile + tid;
+    for (int j = 0; j < NX; ++j) {
+        if (j * kXT < E) {   // uniform
+            const int x = j * kXT + tid;
             const int tx = x < E ? s_tot[x] : 0;
             int all;
-            const int excl = block_exclusive_scan(tx, s_wave_tot, &all);
+            const int excl = xch_block_scan(tx, s_wave_tot, &all);
             if (x < E) {
                 base_e[x] = carry + excl + s_pre[x];
                 if (tile == 0) {
@@ -134,159 +169,209 @@ __device__ void xch_fallback_offsets(int E, int G, int tile, const int *s_tot, c
     }
 }
 
-template <int KMAX, bool EXACT, int NCH>
-__global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
+// NX: experts in chunks of kXT (E <= NX * 512).
+template <int KMAX, bool EXACT, int NX>
+__global__ __launch_bounds__(kXT) void layout_exchange_kernel(
     const int32_t *__restrict__ idx, int T, int vec, int Krt, int E, int G, uint32_t gmagic, int ntiles,
     uint64_t *__restrict__ xt, uint32_t tag, uint64_t wait_ticks, int recount, LayoutPtrs L)
 {
-    static_assert(KMAX <= 8, "the tile's entries are staged for at most 8 per token");
-    constexpr int NCOL = NCH + 1;                  // columns a thread publishes (E + G + 3 <= NCOL * 256)
-    constexpr int NPJ = NCH == 1 ? 1 : 3;          // column pairs a thread reads ((E + G + 3) / 2 <= NPJ * 256)
+    static_assert(KMAX == 2 || KMAX == 4 || KMAX == 8, "two lanes take KMAX / 2 entries of a token each");
+    constexpr int KH = KMAX / 2;                   // entries per lane
+    constexpr int NCOL = NX + 1;                   // columns a thread publishes (E + G + 3 <= NCOL * 512)
     constexpr int kXB = 16;                        // tiles per round of reads
-    // dynamic LDS: emask [E][kWaves] u64; int loff_e [E][kWaves], lstart [E], base_e [E],
+    // dynamic LDS: uint32 ew [E][kXW]; int loff_e [E][kXW], lstart [E], base_e [E],
     // s_tot [E+G+1], s_pre [E+G+1] (the fallback's)
-    extern __shared__ unsigned long long emask[];
-    int *loff_e = reinterpret_cast<int *>(emask + E * kWaves);   // rank base of (expert, wave) in the tile
-    int *lstart = loff_e + E * kWaves;                           // expert's first place in the tile's pair list
-    int *base_e = lstart + E;                                    // expert's first receive row of the tile
+    extern __shared__ uint32_t ew[];
+    int *loff_e = reinterpret_cast<int *>(ew + E * kXW);   // rank base of (expert, wave) in the tile
+    int *lstart = loff_e + E * kXW;                        // expert's first place in the tile's pair list
+    int *base_e = lstart + E;                              // expert's first receive row of the tile
     int *s_tot = base_e + E;
     int *s_pre = s_tot + E + G + 1;
     __shared__ int32_t s_src[kLayoutTile * KMAX];   // the tile's pair ids in slot order
     __shared__ int32_t s_dst[kLayoutTile * KMAX];   // and their receive slots
-    __shared__ int s_wave_tot[kWaves];
-    __shared__ int gcnt[kMaxG][kWaves];
+    __shared__ int s_wave_tot[kXW];
+    __shared__ int gcnt[kMaxG][kXW];
     __shared__ int lgstart[kMaxG];
+    __shared__ int gtot[kMaxG];   // the tile's count of each group
     __shared__ int base_g[kMaxG];
-    __shared__ int loff_g[kMaxG][kWaves];
-    __shared__ uint64_t gball[kMaxG][kWaves];
+    __shared__ int loff_g[kMaxG][kXW];
+    __shared__ uint32_t gball[kMaxG][kXW];
     __shared__ int s_err, s_late, s_gpairs;
     const int K = EXACT ? KMAX : Krt;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int j = lane & 31, h = lane >> 5;   // token j of the wave, half h of its entries
     const int tile = blockIdx.x;
-    const int t = tile * kLayoutTile + tid;
+    const int t = tile * kLayoutTile + wave * 32 + j;
     const int rows = (E + G + 3) & ~1;   // table columns: experts, groups, pairs, error bits (+1: even)
-    const uint64_t below = lanemask_lt(lane);
+    const uint32_t below = (1u << j) - 1u;
 
-    // Count the tile (as the count kernel).
-    int e[KMAX];
-    if (EXACT && KMAX >= 4 && (vec & 4)) {   // 16-byte aligned index rows: K / 4 vector loads
-        const u32x4 *row = reinterpret_cast<const u32x4 *>(idx + (size_t)(t < T ? t : T - 1) * KMAX);
+    // Count the tile. Lane h loads its own entries k = h * KH + q and the other
+    // lane's (k = (1 - h) * KH + q), choosing them by address: selecting
+    // between registers by h would make the compiler index a private array.
+    int own[KH], oth[KH];
+    {
+        const int tc = t < T ? t : T - 1;
+        if constexpr (EXACT && KMAX == 8) {
+            if (vec & 4) {   // 16-byte aligned index rows: two vector loads
+                const u32x4 *row = reinterpret_cast<const u32x4 *>(idx + (size_t)tc * KMAX);
+                const u32x4 a = row[h], b = row[h ^ 1];
+                own[0] = (int)a.x; own[1] = (int)a.y; own[2] = (int)a.z; own[3] = (int)a.w;
+                oth[0] = (int)b.x; oth[1] = (int)b.y; oth[2] = (int)b.z; oth[3] = (int)b.w;
+            } else {
+                const int32_t *row = idx + (size_t)tc * KMAX;
 #pragma unroll
-        for (int k = 0; k < KMAX; k += 4) {
-            const u32x4 q = row[k / 4];
-            e[k] = (int)q.x;
-            e[k + 1] = (int)q.y;
-            e[k + 2] = (int)q.z;
-            e[k + 3] = (int)q.w;
+                for (int q = 0; q < KH; ++q) {
+                    own[q] = row[h * KH + q];
+                    oth[q] = row[(h ^ 1) * KH + q];
+                }
+            }
+        } else {
+            // clamped in-range addresses; entries k >= K are masked below
+            const int32_t *row = idx + (size_t)tc * K;
+#pragma unroll
+            for (int q = 0; q < KH; ++q) {
+                const int ko = h * KH + q, kt = (h ^ 1) * KH + q;
+                own[q] = row[ko < K ? ko : K - 1];
+                oth[q] = row[kt < K ? kt : K - 1];
+            }
         }
-    } else {
-        load_row<KMAX>(idx, t, T, K, e);
     }
-    for (int i = tid; i < E * kWaves; i += kLayoutTile) emask[i] = 0ull;
+    for (int i = tid; i < E * kXW; i += kXT) ew[i] = 0u;
     if (tid == 0) {
         s_err = 0;
         s_late = recount;
     }
     __syncthreads();
-    mask_row<KMAX>(t, T, K, e);
-    const Inserted ins = insert_token<KMAX>(e, t < T, K, E, gmagic, emask, wave, lane);
-    const uint32_t gm = ins.gm, bad = ins.bad();
-    if (t < T) L.tok_group_mask[t] = gm;
+    // Classify (as the count kernel: an entry repeats iff its expert equals an
+    // earlier in-range entry of the token; the groups are those of its in-range
+    // entries) and insert this lane's valid entries. Each lane reports the
+    // errors of its own entries; both lanes find the token's groups.
+    const bool live = t < T;
+    uint32_t gm = 0, ok_q = 0;   // ok_q bit q: entry h * KH + q counts
+    int err = 0;
+#pragma unroll
+    for (int q = 0; q < KH; ++q) {
+        const int ko = h * KH + q, kt = (h ^ 1) * KH + q;
+        if (!(live && ko < K)) own[q] = -1;
+        if (!(live && kt < K)) oth[q] = -1;
+    }
+#pragma unroll
+    for (int q = 0; q < KH; ++q) {
+        const bool ino = (unsigned)own[q] < (unsigned)E, int_ = (unsigned)oth[q] < (unsigned)E;
+        gm |= ino ? 1u << group_of(own[q], gmagic) : 0u;
+        gm |= int_ ? 1u << group_of(oth[q], gmagic) : 0u;
+        err |= (live && h * KH + q < K && !ino) ? 1 : 0;   // an entry of the token, out of range
+        bool rep = false;
+#pragma unroll
+        for (int p = 0; p < q; ++p) rep = rep || own[p] == own[q];
+#pragma unroll
+        for (int p = 0; p < KH; ++p) rep = rep || (h != 0 && oth[p] == own[q]);   // the first half comes first
+        err |= (ino && rep) ? 2 : 0;
+        const bool v = ino && !rep;
+        ok_q |= v ? 1u << q : 0u;
+        if (v) atomicOr(&ew[own[q] * kXW + wave], 1u << j);
+    }
+    if (t < T && h == 0) L.tok_group_mask[t] = gm;
     for (int g = 0; g < G; ++g) {
-        const uint64_t b = __ballot((gm >> g) & 1u);
+        const uint64_t b = __ballot(h == 0 && ((gm >> g) & 1u));   // bits 0-31: the wave's tokens
         if (lane == 0) {
             gcnt[g][wave] = __popcll(b);
-            gball[g][wave] = b;
+            gball[g][wave] = (uint32_t)b;
         }
     }
-    if (ins.err()) atomicOr(&s_err, ins.err());
+    if (err) atomicOr(&s_err, err);
     __syncthreads();
 
     // The tile's own layout: per (expert, wave) the rank base inside the tile
     // and the expert's count; an exclusive scan of the counts over the experts
     // (each expert's first place in the tile's slot-ordered pair list); per
     // (group, wave) the rank base and over the groups the same scan.
-    int cnt_x[NCH], npairs = 0;
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-        cnt_x[j] = 0;
-        if (j * kLayoutTile < E) {   // uniform
-            const int x = j * kLayoutTile + tid;
-            if (x < E) {
-                const unsigned long long *m = emask + x * kWaves;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
-                    loff_e[x * kWaves + w] = cnt_x[j];
-                    cnt_x[j] += __popcll(m[w]);
-                }
-            }
-            int all;
-            const int lex = block_exclusive_scan(cnt_x[j], s_wave_tot, &all);
-            if (x < E) lstart[x] = npairs + lex;
-            npairs += all;
-        }
-    }
-    if (wave == 0) {   // groups: lane g < G
+    // The groups first, in the last wave (lane g < G), which has no experts of
+    // the first chunk for E <= 448: it runs beside the experts' popcounts.
+    if (wave == kXW - 1) {
         const int gl = lane < G ? lane : 0;
         int r = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kXW; ++w) {
             if (lane < G) loff_g[gl][w] = r;
             r += lane < G ? gcnt[gl][w] : 0;
         }
         const int incl = wave_incl_scan(r);
-        if (lane < G) lgstart[lane] = incl - r;
+        if (lane < G) {
+            lgstart[lane] = incl - r;
+            gtot[lane] = r;
+        }
         if (lane == kMaxG - 1) s_gpairs = incl;
+    }
+    int npairs = 0, cnt_x[NX] = {};   // cnt_x[c]: the count of expert c * 512 + tid in the tile
+#pragma unroll
+    for (int c = 0; c < NX; ++c) {
+        if (c * kXT < E) {   // uniform
+            const int x = c * kXT + tid;
+            int cnt = 0;
+            if (x < E) {
+#pragma unroll
+                for (int w = 0; w < kXW; ++w) {
+                    loff_e[x * kXW + w] = cnt;
+                    cnt += __popc(ew[x * kXW + w]);
+                }
+            }
+            cnt_x[c] = cnt;
+            int all;
+            const int lex = xch_block_scan(cnt, s_wave_tot, &all, c == 0);   // (s_wave_tot unused before)
+            if (x < E) lstart[x] = npairs + lex;
+            npairs += all;
+        }
     }
     __syncthreads();
 
-    // The tile's value of column c (see xch_pack).
-    auto own_value = [&](int c) -> uint32_t {
-        if (c < E) {
-            const unsigned long long *m = emask + c * kWaves;
-            return xch_pack(__popcll(m[0]) + __popcll(m[1]) + __popcll(m[2]) + __popcll(m[3]), lstart[c]);
-        }
-        if (c < E + G) {
-            const int g = c - E;
-            return xch_pack(gcnt[g][0] + gcnt[g][1] + gcnt[g][2] + gcnt[g][3], lgstart[g]);
-        }
+    // The tile's value of column c (see xch_pack); n: an expert's count, when
+    // the caller has it.
+    auto own_value = [&](int c, int n) -> uint32_t {
+        if (c < E) return xch_pack(n, lstart[c]);
+        if (c < E + G) return xch_pack(gtot[c - E], lgstart[c - E]);
         if (c == E + G) return xch_pack(npairs, s_gpairs);
         if (c == E + G + 1) return xch_err_pack(s_err);
         return 0u;   // the padding column
     };
-    // Publish it, for the columns c = tid + j * 256.
+    auto expert_count = [&](int c) -> int {
+        int n = 0;
+#pragma unroll
+        for (int w = 0; w < kXW; ++w) n += __popc(ew[c * kXW + w]);
+        return n;
+    };
+    // Publish it, for the columns c = tid + jj * 512 (an expert's count is this
+    // thread's cnt_x[jj]).
     const bool xch = xt != nullptr && !recount;   // uniform
     if (xch) {
 #pragma unroll
-        for (int j = 0; j < NCOL; ++j) {
-            const int c = tid + j * kLayoutTile;
-            if (c < rows) xch_put(xt + (size_t)tile * rows + c, tag, own_value(c));
+        for (int jj = 0; jj < NCOL; ++jj) {
+            const int c = tid + jj * kXT;
+            if (c < rows) xch_put(xt + (size_t)tile * rows + c, tag, own_value(c, jj < NX ? cnt_x[jj] : 0));
         }
     }
 
-    // Each entry's rank inside the tile (lr among the tile's pairs of its
-    // expert, lg of its group) and its place li in the tile's pair list, where
-    // its pair id is staged. (LDS reads from clamped indices, masked
-    // afterwards: a read under a lane-dependent branch gets a branch and a
-    // wait of its own.)
+    // Each of this lane's entries' rank inside the tile (lr among the tile's
+    // pairs of its expert, lg of its group) and its place li in the tile's pair
+    // list, where its pair id is staged. (LDS reads from clamped indices,
+    // masked afterwards: a read under a lane-dependent branch gets a branch and
+    // a wait of its own.)
     const size_t p0 = (size_t)t * K;
-    uint32_t ok_k = 0;   // bit k: entry k counts
-    int lr[KMAX], lg[KMAX], li[KMAX];
+    int lr[KH], lg[KH], li[KH];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        const bool v = t < T && k < K && !((bad >> k) & 1u);
-        ok_k |= v ? 1u << k : 0u;
-        const int x = v ? e[k] : 0, g = group_of(x, gmagic);
-        lr[k] = loff_e[x * kWaves + wave] + __popcll(emask[x * kWaves + wave] & below);
-        lg[k] = loff_g[g][wave] + __popcll(gball[g][wave] & below);
-        li[k] = lstart[x] + lr[k];
+    for (int q = 0; q < KH; ++q) {
+        const bool v = (ok_q >> q) & 1u;
+        const int x = v ? own[q] : 0, g = group_of(x, gmagic);
+        lr[q] = loff_e[x * kXW + wave] + __popc(ew[x * kXW + wave] & below);
+        lg[q] = loff_g[g][wave] + __popc(gball[g][wave] & below);
+        li[q] = lstart[x] + lr[q];
     }
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        if ((ok_k >> k) & 1u) s_src[li[k]] = (int32_t)(p0 + k);
+    for (int q = 0; q < KH; ++q)
+        if ((ok_q >> q) & 1u) s_src[li[q]] = (int32_t)(p0 + h * KH + q);
 
     // Every tile's values of the column pairs this thread owns (columns 2p and
-    // 2p + 1, p = tid + j * 256), summed: a column's total, its offset (the
+    // 2p + 1, p = tid + jj * 512), summed: a column's total, its offset (the
     // tiles' prefixes summed) and its count in the tiles before this one. A
     // pair is one 16-byte read per tile, and a wave reads consecutive pairs of
     // one tile row; kXB tiles per round, their reads in flight together; a
@@ -298,18 +383,18 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
     // requests within one cache line.) With one tile the values are this
     // tile's own.
     const int npair = rows / 2;
-    int ctot[2 * NPJ], coff[2 * NPJ], cpre[2 * NPJ];
+    int ctot[2 * NX], coff[2 * NX], cpre[2 * NX];
 #pragma unroll
-    for (int q = 0; q < 2 * NPJ; ++q) ctot[q] = coff[q] = cpre[q] = 0;
+    for (int q = 0; q < 2 * NX; ++q) ctot[q] = coff[q] = cpre[q] = 0;
     if (xch) {
         const __amdgpu_buffer_rsrc_t tab =
             __builtin_amdgcn_make_buffer_rsrc(xt, (short)0, ntiles * rows * 8, 0x00020000);
         const uint64_t t0 = wall_clock64();
         bool late = false;
 #pragma unroll
-        for (int j = 0; j < NPJ; ++j) {
-            if (j * kLayoutTile + wave * kWave < npair) {   // uniform per wave: some lane has a pair
-                const int pc = tid + j * kLayoutTile < npair ? tid + j * kLayoutTile : npair - 1;
+        for (int jj = 0; jj < NX; ++jj) {
+            if (jj * kXT + wave * kWave < npair) {   // uniform per wave: some lane has a pair
+                const int pc = tid + jj * kXT < npair ? tid + jj * kXT : npair - 1;
                 for (int b0 = 0; b0 < ntiles && !late; b0 += kXB) {
                     u32x4 v[kXB];
                     while (true) {
@@ -343,26 +428,27 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
                         p0s += b0 + u < tile ? v[u].x : 0u;
                         p1s += b0 + u < tile ? v[u].z : 0u;
                     }
-                    ctot[2 * j] += (int)(s0 & 0xFFFFu);
-                    coff[2 * j] += (int)(s0 >> 16);
-                    cpre[2 * j] += (int)(p0s & 0xFFFFu);
-                    ctot[2 * j + 1] += (int)(s1 & 0xFFFFu);
-                    coff[2 * j + 1] += (int)(s1 >> 16);
-                    cpre[2 * j + 1] += (int)(p1s & 0xFFFFu);
+                    ctot[2 * jj] += (int)(s0 & 0xFFFFu);
+                    coff[2 * jj] += (int)(s0 >> 16);
+                    cpre[2 * jj] += (int)(p0s & 0xFFFFu);
+                    ctot[2 * jj + 1] += (int)(s1 & 0xFFFFu);
+                    coff[2 * jj + 1] += (int)(s1 >> 16);
+                    cpre[2 * jj + 1] += (int)(p1s & 0xFFFFu);
                 }
             }
         }
         if (late) s_late = 1;
     } else if (!recount) {
 #pragma unroll
-        for (int j = 0; j < NPJ; ++j) {
-            const int pc = tid + j * kLayoutTile;
+        for (int jj = 0; jj < NX; ++jj) {
+            const int pc = tid + jj * kXT;
             if (pc < npair) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t w = own_value(2 * pc + h);
-                    ctot[2 * j + h] = (int)(w & 0xFFFFu);
-                    coff[2 * j + h] = (int)(w >> 16);
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int c = 2 * pc + hh;
+                    const uint32_t w = own_value(c, c < E ? expert_count(c) : 0);
+                    ctot[2 * jj + hh] = (int)(w & 0xFFFFu);
+                    coff[2 * jj + hh] = (int)(w >> 16);
                 }
             }
         }
@@ -374,11 +460,11 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
         // in this tile is its offset + its count in earlier tiles; tile 0
         // writes the counts, offsets and status.
 #pragma unroll
-        for (int j = 0; j < NPJ; ++j) {
+        for (int jj = 0; jj < NX; ++jj) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int c = 2 * (tid + j * kLayoutTile) + h;
-                const int tot = ctot[2 * j + h], off = coff[2 * j + h], pre = cpre[2 * j + h];
+            for (int hh = 0; hh < 2; ++hh) {
+                const int c = 2 * (tid + jj * kXT) + hh;
+                const int tot = ctot[2 * jj + hh], off = coff[2 * jj + hh], pre = cpre[2 * jj + hh];
                 if (c < E) {
                     base_e[c] = off + pre;
                     if (tile == 0) {
@@ -401,53 +487,55 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
         }
     } else {
         xch_recount<KMAX, EXACT>(idx, T, K, E, G, gmagic, tile, s_tot, s_pre);
-        xch_fallback_offsets<NCH>(E, G, tile, s_tot, s_pre, base_e, base_g, s_wave_tot, L);
+        xch_fallback_offsets<NX>(E, G, tile, s_tot, s_pre, base_e, base_g, s_wave_tot, L);
     }
     __syncthreads();   // base_e, base_g
 
-    // Slots: base + rank inside the tile.
+    // Slots: base + rank inside the tile, this lane's KH entries.
     if (t < T) {
-        int se[KMAX], sg[KMAX];
+        int se[KH], sg[KH];
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            const bool v = (ok_k >> k) & 1u;
-            const int x = v ? e[k] : 0;
+        for (int q = 0; q < KH; ++q) {
+            const bool v = (ok_q >> q) & 1u;
+            const int x = v ? own[q] : 0;
             const int be = base_e[x], bg = base_g[group_of(x, gmagic)];
-            se[k] = v ? be + lr[k] : -1;
-            sg[k] = v ? bg + lg[k] : -1;
+            se[q] = v ? be + lr[q] : -1;
+            sg[q] = v ? bg + lg[q] : -1;
         }
-        if (EXACT && (vec & 1)) {   // 16-byte aligned slot arrays, K in {2, 4, 8}
-            if constexpr (KMAX == 2) {
-                *reinterpret_cast<u32x2 *>(L.slot_e + p0) = u32x2{(uint32_t)se[0], (uint32_t)se[1]};
-                *reinterpret_cast<u32x2 *>(L.slot_g + p0) = u32x2{(uint32_t)sg[0], (uint32_t)sg[1]};
+        const size_t pk = p0 + h * KH;   // this lane's first entry
+        if (EXACT && (vec & 1)) {        // 16-byte aligned slot arrays, K in {2, 4, 8}
+            if constexpr (KH == 4) {
+                *reinterpret_cast<u32x4 *>(L.slot_e + pk) =
+                    u32x4{(uint32_t)se[0], (uint32_t)se[1], (uint32_t)se[2], (uint32_t)se[3]};
+                *reinterpret_cast<u32x4 *>(L.slot_g + pk) =
+                    u32x4{(uint32_t)sg[0], (uint32_t)sg[1], (uint32_t)sg[2], (uint32_t)sg[3]};
+            } else if constexpr (KH == 2) {
+                *reinterpret_cast<u32x2 *>(L.slot_e + pk) = u32x2{(uint32_t)se[0], (uint32_t)se[1]};
+                *reinterpret_cast<u32x2 *>(L.slot_g + pk) = u32x2{(uint32_t)sg[0], (uint32_t)sg[1]};
             } else {
-#pragma unroll
-                for (int k = 0; k < KMAX; k += 4) {
-                    *reinterpret_cast<u32x4 *>(L.slot_e + p0 + k) =
-                        u32x4{(uint32_t)se[k], (uint32_t)se[k + 1], (uint32_t)se[k + 2], (uint32_t)se[k + 3]};
-                    *reinterpret_cast<u32x4 *>(L.slot_g + p0 + k) =
-                        u32x4{(uint32_t)sg[k], (uint32_t)sg[k + 1], (uint32_t)sg[k + 2], (uint32_t)sg[k + 3]};
-                }
+                L.slot_e[pk] = se[0];
+                L.slot_g[pk] = sg[0];
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (k < K) {
-                    L.slot_e[p0 + k] = se[k];
-                    L.slot_g[p0 + k] = sg[k];
+            for (int q = 0; q < KH; ++q) {
+                if (h * KH + q < K) {
+                    L.slot_e[pk + q] = se[q];
+                    L.slot_g[pk + q] = sg[q];
                 }
             }
         }
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            if ((ok_k >> k) & 1u) s_dst[li[k]] = se[k];
+        for (int q = 0; q < KH; ++q)
+            if ((ok_q >> q) & 1u) s_dst[li[q]] = se[q];
+        // the token's groups, in blocks of 4: lane h takes the blocks 4 * (2 i + h)
         int32_t *tg = L.slot_tg + (size_t)t * G;
-        for (int g0 = 0; g0 < G; g0 += 4) {
+        for (int g0 = 4 * h; g0 < G; g0 += 8) {
             int r4[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int g = g0 + u < kMaxG ? g0 + u : kMaxG - 1;
-                const int r = base_g[g] + loff_g[g][wave] + __popcll(gball[g][wave] & below);
+                const int r = base_g[g] + loff_g[g][wave] + __popc(gball[g][wave] & below);
                 r4[u] = g0 + u < G && ((gm >> (g0 + u)) & 1u) ? r : -1;
             }
 #pragma unroll
@@ -463,26 +551,27 @@ __global__ __launch_bounds__(kLayoutTile) void layout_exchange_kernel(
         }
     }
     __syncthreads();
-    tile_write_recv_src_e(npairs, s_src, s_dst, L.recv_src_e, tid, kLayoutTile);
+    tile_write_recv_src_e(npairs, s_src, s_dst, L.recv_src_e, tid, kXT);
 }
 
 using ExchangeFn = void (*)(const int32_t *, int, int, int, int, int, uint32_t, int, uint64_t *, uint32_t, uint64_t,
                             int, LayoutPtrs);
 
-template <int NCH>
+template <int NX>
 ExchangeFn pick_exchange_n(int K)
 {
     switch (K) {
-    case 2: return layout_exchange_kernel<2, true, NCH>;
-    case 4: return layout_exchange_kernel<4, true, NCH>;
-    case 8: return layout_exchange_kernel<8, true, NCH>;
-    default: return layout_exchange_kernel<8, false, NCH>;
+    case 2: return layout_exchange_kernel<2, true, NX>;
+    case 4: return layout_exchange_kernel<4, true, NX>;
+    case 8: return layout_exchange_kernel<8, true, NX>;
+    default: return layout_exchange_kernel<8, false, NX>;
     }
 }
 
 ExchangeFn pick_exchange(int K, int E)
 {
-    return E <= kLayoutTile ? pick_exchange_n<1>(K) : pick_exchange_n<kMaxEChunks>(K);
+    static_assert(2 * kXT >= 1024, "E <= 1024 in two chunks");
+    return E <= kXT ? pick_exchange_n<1>(K) : pick_exchange_n<2>(K);
 }
 
 // Exchange tables of the one-launch layout, in library memory (zero when the
@@ -580,9 +669,9 @@ hipError_t launch_layout_exchange(const int32_t *idx, int T, int K, int E, int G
         if (e != hipSuccess || !xt) return e;
     }
     const long long wt = tuning().base_wait_ticks;
-    const size_t lds = (size_t)E * kWaves * sizeof(unsigned long long) +
-                       ((size_t)E * (kWaves + 2) + 2 * (size_t)(E + G + 1)) * sizeof(int);
-    hipLaunchKernelGGL(pick_exchange(K, E), dim3(ntiles), dim3(kLayoutTile), lds, stream, idx, T, vec, K, E, G,
+    const size_t lds = (size_t)E * kXW * sizeof(uint32_t) +
+                       ((size_t)E * (kXW + 2) + 2 * (size_t)(E + G + 1)) * sizeof(int);
+    hipLaunchKernelGGL(pick_exchange(K, E), dim3(ntiles), dim3(kXT), lds, stream, idx, T, vec, K, E, G,
                        group_magic(E, G), ntiles, xt, tag, (uint64_t)(wt < 0 ? 0 : wt), wt < 0 ? 1 : 0, L);
     launched = true;
     return hipGetLastError();
