@@ -15,8 +15,8 @@ Prints ONE JSON line. `value` = algorithmic HBM bytes of a step (reads + writes,
 each byte counted once) / wall time per step, the median over --processes
 separate processes (this one and fresh children, one after another). Per-call
 times come from HIP events recorded around every call of every 4th timed step,
-on the stream the kernels run on; every timed step's status word is ORed into a
-device accumulator and checked after the timed region. The same line carries
+on the stream the kernels run on; every timed step writes a status word of its
+own, all checked after the timed region. The same line carries
 the roofline of the dominant kernel (the combine), the CPU oracle timed on the
 host cores (its single-thread canonical build and its OpenMP build on every
 core, per call and per workload, asserted bit-identical), and secondary
@@ -27,6 +27,7 @@ every call on every workload with its parity against the oracle.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import re
 import json
@@ -410,24 +411,26 @@ def main():
     T, H, E, G, K = wl.T, wl.H, wl.E, wl.G, wl.K
     dv = Dev(moe, d, modes=("expert",))
     L, D, out = dv.L, dv.D["expert"], dv.out
-    status_or = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # One status word per timed step: step s runs on a Layout that shares every array
+    # of L but its status word, status_words[s] (each step's count kernel clears its
+    # own word and the combine adds its bits), so every step's status is kept and
+    # checked after the timed region without a kernel of its own inside it.
+    status_words = torch.full((args.steps,), -1, dtype=torch.int32, device="cuda")
+    Ls = [dataclasses.replace(L, status=status_words[s:s + 1]) for s in range(args.steps)]
+    for Lx in Ls:
+        Lx.ref()   # the C structs, built before the timed region
 
     # one step: routing layout + dispatch as one call (the library's form for this
     # batch: the count kernel, then a dispatch whose workgroup 0 computes the offsets
-    # and whose workgroups place their own tokens), then the combine; the status word
-    # of every step is ORed into status_or; the three separate calls are timed in extras
-    fns = [
-        lambda: moe.moe_layout_dispatch(dv.idx, E, G, dv.x, dv.w, "expert", "bf16", out_layout=L, out=D),
-        lambda: moe.moe_combine(L, D.recv_x, dv.w, "expert", out=out),
-    ]
+    # and whose workgroups place their own tokens), then the combine; the three
+    # separate calls are timed in extras
+    def step(Lx):
+        moe.moe_layout_dispatch(dv.idx, E, G, dv.x, dv.w, "expert", "bf16", out_layout=Lx, out=D)
+        moe.moe_combine(Lx, D.recv_x, dv.w, "expert", out=out)
+
     for _ in range(args.warmup):
-        for f in fns:
-            f()
-        # (also warms torch's kernel for it: the first launch of a torch kernel in a
-        # process loads its code object, tens of ms, which must not land in the timing)
-        status_or.bitwise_or_(L.status)
+        step(L)
     torch.cuda.synchronize()
-    status_or.zero_()
 
     # Per-call HIP events on every EVENT_EVERY-th timed step: a sample of the timed
     # region for the per-call times, while most steps carry no event records (each
@@ -439,22 +442,25 @@ def main():
     t0 = time.perf_counter()
     for s in range(args.steps):
         e = ev.get(s)
+        Lx = Ls[s]
         if e:
             e[0].record()
-        fns[0]()
+        moe.moe_layout_dispatch(dv.idx, E, G, dv.x, dv.w, "expert", "bf16", out_layout=Lx, out=D)
         if e:
             e[1].record()
-        fns[1]()
+        moe.moe_combine(Lx, D.recv_x, dv.w, "expert", out=out)
         if e:
             e[2].record()
-        status_or.bitwise_or_(L.status)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) / args.steps * 1e3
     us = {name: [ev[s][i].elapsed_time(ev[s][i + 1]) * 1e3 for s in sampled]
           for i, name in enumerate(("layout_dispatch", "combine"))}
 
-    step_status = int(status_or.item())
+    words = status_words.cpu().numpy()
+    if (words == -1).any():
+        raise RuntimeError("a timed step left its status word unwritten")
+    step_status = int(np.bitwise_or.reduce(words))
     if step_status & moe.STATUS_ERRORS:
         raise RuntimeError(f"a timed step's status word reported bad data: {step_status:#x}")
     R = int(L.expert_offset[E].item())

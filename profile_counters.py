@@ -296,8 +296,8 @@ def summaries(out: str, res: dict, K: dict, cal: dict, dirs: list[str]) -> None:
         lines = ["# Kernel trace: t4096 per-expert step", "", HEAD, "",
                  f"Workload: {wdesc}, per-expert receive buffers. A step is `moe_layout_dispatch` (the layout's "
                  "count kernel, then the bf16 dispatch whose workgroup 0 computes the offsets and per-tile bases "
-                 "while every workgroup places its own token), `moe_combine`, and the OR of the step's status "
-                 "word into an accumulator (a one-element torch kernel).", "",
+                 "while every workgroup places its own token) and `moe_combine`; each timed step keeps a status "
+                 "word of its own.", "",
                  "    " + command("step", "trace"), "",
                  "Per-kernel statistics over the run (3 warm-up + 20 timed steps, and torch's own set-up copies "
                  "and fills):", ""] + trace_table(res["step"])
