@@ -100,16 +100,20 @@ def test_layout_full_workloads(moe, orc, name):
     check_layout(L, orc.layout(d["topk_idx"], wl.E, wl.G))
 
 
+# moe_layout on a plain stream takes the one-launch exchange layout for K <= 8 and
+# up to 64 tiles of 256 tokens (two lanes per token; E > 512 in two expert chunks),
+# and count + place for K > 8 or more tiles
 EDGE_SHAPES = [
     (0, 8, 256, 8), (1, 8, 256, 8), (1, 1, 1, 1), (255, 8, 256, 8), (256, 8, 256, 8),
     (257, 8, 256, 8), (1000, 1, 7, 7), (777, 32, 64, 32), (513, 6, 1024, 32), (4097, 8, 256, 1),
     (300, 2, 8, 8), (2000, 3, 12, 4), (1025, 8, 1000, 8), (600, 16, 16, 16),
-    # either side of the one-launch layout's limit (T * K <= 16384), and rounds of its count
     (2048, 8, 256, 8), (2049, 8, 256, 8), (4096, 4, 64, 8), (8192, 2, 8, 8), (5000, 3, 1024, 32),
-    # every token takes every expert (K = E), with G = E, G = 1 and between; above the limit too
+    # every token takes every expert (K = E), with G = E, G = 1 and between
     (300, 32, 32, 32), (200, 8, 8, 1), (700, 16, 16, 4), (2500, 8, 8, 8),
-    # count + place: ragged tile, K not 2/4/8, G = 32, exactly 16 tiles
-    (3000, 7, 200, 8), (2300, 8, 256, 32), (4096, 8, 256, 8),
+    # ragged tile, K not 2/4/8, G = 32, exactly 16 tiles; E just above one expert chunk
+    (3000, 7, 200, 8), (2300, 8, 256, 32), (4096, 8, 256, 8), (1500, 8, 520, 8),
+    # 64 tiles (the exchange's limit) and 65 (count + place with K <= 8)
+    (16384, 8, 256, 8), (16385, 6, 64, 8),
 ]
 
 
@@ -120,7 +124,8 @@ def test_layout_edge_shapes(moe, orc, T, K, E, G):
     check_layout(L, orc.layout(idx, E, G))
 
 
-# seeds 0-5: T * K <= 16384 (the one-launch layout); 6-8: larger (count + place)
+# seeds 0-5: 200-900 tokens, K 2-8 (odd K: the half-row split with K < 8); 6-8:
+# 2100-4000 tokens, K = 8 (the exchange over 9-16 tiles)
 @pytest.mark.parametrize("seed", range(9))
 def test_layout_invalid_entries(moe, orc, seed):
     rng = np.random.default_rng(seed)
