@@ -464,22 +464,12 @@ constexpr int kFinBS = 1024;                  // finalize: one workgroup, a thre
 constexpr int kFinSerialTiles = 8;            // tiles past the first batch loaded one by one
 constexpr int kFinWaves = kFinBS / kWave;
 
-// Exclusive prefix sum over the 1024 threads of the finalize workgroup.
+// Exclusive prefix sum over the 1024 threads of the finalize (or one-pass)
+// workgroup, with no barrier before it: the caller orders it after any earlier
+// reader of s_wave_tot.
 __device__ __forceinline__ int fin_scan(int v, int *s_wave_tot, int &total)
 {
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int x = wave_incl_scan(v);
-    if (lane == kWave - 1) s_wave_tot[wave] = x;
-    __syncthreads();
-    int base = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kFinWaves; ++w) {
-        const int c = s_wave_tot[w];
-        base += w < wave ? c : 0;
-        all += c;
-    }
-    total = all;
-    return base + x - v;
+    return block_exclusive_scan<kFinWaves>(v, s_wave_tot, &total, true);
 }
 
 // Finalize (fused layout + dispatch): one workgroup. A column's total over the

@@ -68,26 +68,6 @@ __device__ __forceinline__ int xch_err_unpack(uint32_t s) { return ((s & 0xFFu) 
 constexpr int kXT = 2 * kLayoutTile;
 constexpr int kXW = kXT / kWave;   // 8
 
-// Exclusive prefix sum over the kXT threads; *total gets the sum. `first`:
-// no earlier scan may still be reading s_wave_tot.
-__device__ __forceinline__ int xch_block_scan(int v, int *s_wave_tot, int *total, bool first = false)
-{
-    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-    const int x = wave_incl_scan(v);
-    if (!first) __syncthreads();   // s_wave_tot free (a previous scan may still be reading it)
-    if (lane == kWave - 1) s_wave_tot[wave] = x;
-    __syncthreads();
-    int base = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < kXW; ++w) {
-        const int c = s_wave_tot[w];
-        base += w < wave ? c : 0;
-        all += c;
-    }
-    *total = all;
-    return base + x - v;
-}
-
 // Every token's valid entries counted into s_tot (all tiles) and s_pre (tiles
 // before `tile`), groups likewise in columns E.., error bits ORed into column
 // E + G: the counts the exchange would have given, from the indices alone.
@@ -141,7 +121,7 @@ __device__ void xch_fallback_offsets(int E, int G, int tile, const int *s_tot, c
             const int x = j * kXT + tid;
             const int tx = x < E ? s_tot[x] : 0;
             int all;
-            const int excl = xch_block_scan(tx, s_wave_tot, &all);
+            const int excl = block_exclusive_scan<kXW>(tx, s_wave_tot, &all);
             if (x < E) {
                 base_e[x] = carry + excl + s_pre[x];
                 if (tile == 0) {
@@ -318,7 +298,7 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
             }
             cnt_x[c] = cnt;
             int all;
-            const int lex = xch_block_scan(cnt, s_wave_tot, &all, c == 0);   // (s_wave_tot unused before)
+            const int lex = block_exclusive_scan<kXW>(cnt, s_wave_tot, &all, c == 0);   // (s_wave_tot unused before)
             if (x < E) lstart[x] = npairs + lex;
             npairs += all;
         }

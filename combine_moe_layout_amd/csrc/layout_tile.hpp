@@ -125,17 +125,20 @@ __device__ __forceinline__ void tile_write_recv_src_e(int npairs, const int32_t 
     for (int i = tid; i < npairs; i += nthreads) recv_src_e[s_dst[i]] = s_src[i];
 }
 
-// Exclusive prefix sum over the 256 threads of the workgroup; *total gets the sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave_tot, int *total)
+// Exclusive prefix sum over the NW waves of the workgroup; *total gets the sum.
+// `first`: no earlier scan may still be reading s_wave_tot (its first barrier
+// is then left out).
+template <int NW = kWaves>
+__device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave_tot, int *total, bool first = false)
 {
     const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
     const int x = wave_incl_scan(v);
-    __syncthreads();   // s_wave_tot free (a previous scan may still be reading it)
+    if (!first) __syncthreads();   // s_wave_tot free (a previous scan may still be reading it)
     if (lane == kWave - 1) s_wave_tot[wave] = x;
     __syncthreads();
     int base = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const int c = s_wave_tot[w];
         base += w < wave ? c : 0;
         all += c;
