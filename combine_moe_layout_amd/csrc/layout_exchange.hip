@@ -559,7 +559,7 @@ ExchangeFn pick_exchange(int K, int E)
 // kXchSlots streams per GPU. In host code `xch_tables` only names the symbol;
 // its address on each GPU comes from hipGetSymbolAddress (xch_slot).
 constexpr int kXchSlots = 8;
-constexpr size_t kXchEntries = (size_t)1 << 16;   // 512 KiB per table
+constexpr size_t kXchEntries = (size_t)64 * (1024 + 32 + 4);   // 64 tiles of the widest row (E = 1024, G = 32): 530 KiB per table
 __device__ __align__(256) uint64_t xch_tables[kXchSlots * kXchEntries];
 
 constexpr int kXchMaxDevices = 64;

@@ -112,8 +112,9 @@ EDGE_SHAPES = [
     (300, 32, 32, 32), (200, 8, 8, 1), (700, 16, 16, 4), (2500, 8, 8, 8),
     # ragged tile, K not 2/4/8, G = 32, exactly 16 tiles; E just above one expert chunk
     (3000, 7, 200, 8), (2300, 8, 256, 32), (4096, 8, 256, 8), (1500, 8, 520, 8),
-    # 64 tiles (the exchange's limit) and 65 (count + place with K <= 8)
-    (16384, 8, 256, 8), (16385, 6, 64, 8),
+    # 64 tiles (the exchange's limit; at the widest table row too) and 65 (count + place
+    # with K <= 8)
+    (16384, 8, 256, 8), (16384, 8, 1024, 32), (16385, 6, 64, 8),
 ]
 
 
