@@ -118,8 +118,9 @@ struct Tuning {
     bool fp8_group_w4 = true;        // plain per-group FP8 dispatch at 4 waves per SIMD
     int fused_fp8_place_max_t = 3072;  // moe_layout_dispatch with FP8: a placing dispatch up
                                        // to this T, moe_layout + the plain dispatch above
-    int layout_exchange_max_tiles = 64;     // moe_layout in one launch exchanging per-tile counts, up to
-                                            // this many tiles of 256 tokens (top-k <= 8; 0: never)
+    int layout_exchange_max_tiles = 128;    // moe_layout in one launch exchanging per-tile counts, up to
+                                            // this many tiles of 256 tokens (top-k <= 8; at most 128;
+                                            // 0: never)
     int layout_onepass_max_pairs = 16384;   // else in one launch counting every token per tile, up to
                                             // T * K pairs (top-k <= 8)
     int fused_onepass_max_pairs = 0;        // moe_layout_dispatch as that layout + a plain dispatch

@@ -33,7 +33,7 @@
 // Kernel 2' (finalize, the fused layout + dispatch): one workgroup computes the
 // counts, offsets and status once and a base per (tile, column), from which
 // each dispatch workgroup places its own token (place.hpp).
-// One launch instead: up to 64 tiles exchange their counts through a table in
+// One launch instead: up to 128 tiles exchange their counts through a table in
 // library memory (layout_exchange.hip, top-k <= 8); where no table can be used
 // (graph capture, more streams than tables), with top-k <= 8 and T * K <=
 // 16384, each tile's workgroup counts all tokens itself (see

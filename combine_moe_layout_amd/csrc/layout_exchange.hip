@@ -1,5 +1,5 @@
 // One-launch layout with an exchange between tiles (moe_layout, top-k <= 8, up
-// to 64 tiles): the count and place kernels of layout.hip as one workgroup
+// to 128 tiles): the count and place kernels of layout.hip as one workgroup
 // per tile, which learns what it needs of the other tiles from a
 // table in library memory instead of from a second launch. The workgroup
 // counts its tile with per-(expert, wave) words in LDS as the count kernel
@@ -560,6 +560,11 @@ ExchangeFn pick_exchange(int K, int E)
 // its address on each GPU comes from hipGetSymbolAddress (xch_slot).
 constexpr int kXchSlots = 8;
 constexpr size_t kXchEntries = (size_t)64 * (1024 + 32 + 4);   // 64 tiles of the widest row (E = 1024, G = 32): 530 KiB per table
+// Most tiles of one exchange. Every tile's workgroup waits for all the others,
+// so all of them must be able to run at once: 128 workgroups take at most half
+// of the chip's 256 CUs, leaving room for other work on the GPU. (A workgroup
+// whose wait runs out still finishes exactly, by recounting.)
+constexpr int kXchMaxTiles = 128;
 __device__ __align__(256) uint64_t xch_tables[kXchSlots * kXchEntries];
 
 constexpr int kXchMaxDevices = 64;
@@ -640,7 +645,8 @@ hipError_t launch_layout_exchange(const int32_t *idx, int T, int K, int E, int G
     launched = false;
     const int ntiles = layout_tiles(T);
     const int rows = (E + G + 3) & ~1;   // exchange table columns (even)
-    if (T == 0 || K > 8 || ntiles > tuning().layout_exchange_max_tiles || (size_t)ntiles * rows > kXchEntries)
+    if (T == 0 || K > 8 || ntiles > tuning().layout_exchange_max_tiles || ntiles > kXchMaxTiles ||
+        (size_t)ntiles * rows > kXchEntries)
         return hipSuccess;
     uint64_t *xt = nullptr;
     uint32_t tag = 0;

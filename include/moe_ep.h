@@ -168,8 +168,9 @@ int64_t moe_recv_rows_bound(int T, int K, int G, int mode);
  * required in every case (the one-launch forms below do not touch it).
  * stream: a hipStream_t (NULL = the null stream).
  * Forms. For K <= 8 the layout is one launch with a workgroup per tile of 256
- * tokens. For up to 64 tiles (T <= 16384; always within the table's 65536
- * entries of E + G + 2 columns, rounded up to even) the workgroups learn one
+ * tokens. For up to 128 tiles (T <= 32768) whose rows of E + G + 2 columns,
+ * rounded up to even, fit the table's 67840 entries (so 64 tiles at E = 1024,
+ * G = 32; the workgroups must be able to run at once) the workgroups learn one
  * another's per-tile counts through a table in library memory, one per
  * stream on each GPU (8
  * streams per GPU get one; later streams, streams under graph capture and

@@ -101,8 +101,9 @@ def test_layout_full_workloads(moe, orc, name):
 
 
 # moe_layout on a plain stream takes the one-launch exchange layout for K <= 8 and
-# up to 64 tiles of 256 tokens (two lanes per token; E > 512 in two expert chunks),
-# and count + place for K > 8 or more tiles
+# up to 128 tiles of 256 tokens as its table allows (64 at E = 1024, G = 32; two
+# lanes per token; E > 512 in two expert chunks), and count + place for K > 8 or
+# more tiles
 EDGE_SHAPES = [
     (0, 8, 256, 8), (1, 8, 256, 8), (1, 1, 1, 1), (255, 8, 256, 8), (256, 8, 256, 8),
     (257, 8, 256, 8), (1000, 1, 7, 7), (777, 32, 64, 32), (513, 6, 1024, 32), (4097, 8, 256, 1),
@@ -112,9 +113,9 @@ EDGE_SHAPES = [
     (300, 32, 32, 32), (200, 8, 8, 1), (700, 16, 16, 4), (2500, 8, 8, 8),
     # ragged tile, K not 2/4/8, G = 32, exactly 16 tiles; E just above one expert chunk
     (3000, 7, 200, 8), (2300, 8, 256, 32), (4096, 8, 256, 8), (1500, 8, 520, 8),
-    # 64 tiles (the exchange's limit; at the widest table row too) and 65 (count + place
-    # with K <= 8)
-    (16384, 8, 256, 8), (16384, 8, 1024, 32), (16385, 6, 64, 8),
+    # at and past the exchange's limits: 64 tiles at the widest table row, 65 there
+    # (count + place), 128 tiles, 129 (count + place with K <= 8)
+    (16384, 8, 1024, 32), (16385, 8, 1024, 32), (32768, 8, 256, 8), (32769, 6, 64, 8),
 ]
 
 
