@@ -108,6 +108,44 @@ __global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_kernel(
     }
 }
 
+// Small batches: one workgroup per (token, slice of kDispatchBS vectors of its
+// row), grid T x slices. A lane loads its one vector and stores it to each
+// destination row, so a workgroup's chain is one load and nslot stores instead
+// of ITER loads and ITER * nslot stores: with few tokens the grid is then large
+// enough to fill the chip and each workgroup short. Slice 0 also writes the
+// metadata. Same rows, same bytes as dispatch_bf16_kernel.
+template <bool NT, bool NTL>
+__global__ __launch_bounds__(kDispatchBS) void dispatch_bf16_split_kernel(
+    const u32x4 *__restrict__ x, int nvec, int K, int nslot, const int32_t *__restrict__ slots,
+    const float *__restrict__ topk_w, const int32_t *__restrict__ topk_idx,
+    u32x4 *__restrict__ recv_x, float *__restrict__ recv_w, int32_t *__restrict__ recv_idx)
+{
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int j = blockIdx.y * kDispatchBS + tid;
+    const int32_t *ts = slots + (size_t)t * nslot;
+    const int64_t rows = (int64_t)gridDim.x * (K < nslot ? K : nslot);
+    u32x4 v = {};
+    if (j < nvec) v = load16<NTL>(x + (size_t)t * nvec + j);
+    for (int d = 0; d < nslot; ++d) {
+        const int s = ts[d];
+        if (s < 0 || s >= rows) continue;
+        if (j < nvec) store16<NT>(recv_x + (size_t)s * nvec + j, v);
+    }
+    if (blockIdx.y != 0) return;
+    const bool wl = tid < K, il = tid >= K && tid < 2 * K;
+    float wv = 0.f;
+    int iv = 0;
+    if (wl) wv = topk_w[(size_t)t * K + tid];
+    if (il) iv = topk_idx[(size_t)t * K + tid - K];
+    for (int d = 0; d < nslot; ++d) {
+        const int s = ts[d];
+        if (s < 0 || s >= rows) continue;
+        if (wl) recv_w[(size_t)s * K + tid] = wv;
+        if (il) recv_idx[(size_t)s * K + tid - K] = iv;
+    }
+}
+
 // One 16-element chunk per lane per pass; the workgroup has as many lanes as
 // the row has chunks (rounded up to whole waves, at most kFp8MaxBS), so a
 // lane holds one chunk's state and occupancy stays high.
@@ -312,6 +350,7 @@ const Tuning &tuning()
         env("MOE_EP_FP8_GROUP_W4", r.fp8_group_w4);
         if (const char *f = getenv("MOE_EP_FUSED_FP8_PLACE_MAX_T")) r.fused_fp8_place_max_t = atoi(f);
         env("MOE_EP_REGROUP_XCD_ORDER", r.regroup_xcd_order);
+        if (const char *f = getenv("MOE_EP_DISPATCH_SPLIT_MAX_WGS")) r.dispatch_split_max_wgs = atoi(f);
         return r;
     }();
     return t;
@@ -326,6 +365,14 @@ hipError_t launch_dispatch_bf16(const void *x, int T, int H, int K, int nslot, c
     const int iter = iters_for(nvec, kDispatchBS);
     const bool full = nvec % (kDispatchBS * iter) == 0;
     const bool nt = tuning().dispatch_nt_store, ntl = tuning().dispatch_nt_load;
+    const int slices = (nvec + kDispatchBS - 1) / kDispatchBS;
+    if (!place && slices > 1 && slices <= 65535 && (int64_t)T * slices <= tuning().dispatch_split_max_wgs) {
+        auto sfn = nt ? (ntl ? dispatch_bf16_split_kernel<true, true> : dispatch_bf16_split_kernel<true, false>)
+                      : (ntl ? dispatch_bf16_split_kernel<false, true> : dispatch_bf16_split_kernel<false, false>);
+        hipLaunchKernelGGL(sfn, dim3(T, slices), dim3(kDispatchBS), 0, stream, (const u32x4 *)x, nvec, K, nslot,
+                           slots, topk_w, topk_idx, (u32x4 *)recv_x, recv_w, recv_idx);
+        return hipGetLastError();
+    }
     auto fn = place ? pick<Bf16PlaceInst>(iter, nt, ntl, full) : pick<Bf16Inst>(iter, nt, ntl, full);
     hipLaunchKernelGGL(fn, dim3(T), dim3(kDispatchBS), 0, stream, (const u32x4 *)x, nvec, K, nslot,
                        slots, topk_w, topk_idx, (u32x4 *)recv_x, recv_w, recv_idx,

@@ -107,7 +107,7 @@ inline uint32_t group_magic(int E, int G)
 // best on MI355X; MOE_EP_DISPATCH_NT_{LOAD,STORE}=0/1, MOE_EP_FP8_FORM=0/1/2,
 // MOE_EP_FP8_GROUP_W4=0/1, MOE_EP_FUSED_FP8_PLACE_MAX_T=<T>, MOE_EP_{LAYOUT,FUSED}_ONEPASS_MAX_PAIRS=<T*K>,
 // MOE_EP_FUSED_SMALL_MAX_WORK=<T*K*E>, MOE_EP_LAYOUT_EXCHANGE_MAX_TILES=<tiles>,
-// MOE_EP_FUSED_FINALIZE=0/1/2, MOE_EP_FUSED_FINALIZE_ROUNDS=<n> and
+// MOE_EP_FUSED_FINALIZE=0/1/2, MOE_EP_FUSED_FINALIZE_ROUNDS=<n>, MOE_EP_DISPATCH_SPLIT_MAX_WGS=<n> and
 // MOE_EP_BASE_WAIT_TICKS=<ticks> in the environment override them (read once per
 // process) for A/B runs and tests.
 struct Tuning {
@@ -133,6 +133,8 @@ struct Tuning {
                                             // workgroup 0 (bf16), 2 workgroup 0 (bf16 and FP8)
     int fused_finalize_rounds = 4;          // ... for E up to this many columns per thread
     bool regroup_xcd_order = true;          // regroup: each XCD takes a contiguous run of group rows
+    int dispatch_split_max_wgs = 4096;      // plain bf16 dispatch: a workgroup per (token, row slice)
+                                            // while T * slices stays within this (0: never)
 };
 const Tuning &tuning();
 // Whether the FP8 dispatch of rows of H elements runs in a small-workgroup form.

@@ -381,10 +381,13 @@ def test_dispatch_fp8_adversarial_blocks(moe, orc, mode, T, H, E, G, K):
 
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("H", [2056, 3072, 5120, 6144, 6152, 8192])   # 3..8 vectors per lane, two ragged
-def test_dispatch_bf16_every_vector_count(moe, orc, mode, H):
+@pytest.mark.parametrize("T", [300, 1500])
+def test_dispatch_bf16_every_vector_count(moe, orc, mode, H, T):
     """The bf16 dispatch at every vector count per lane it compiles, plain and through
-    the fused call (the placing instances), with ragged last passes."""
-    T, E, G, K = 300, 64, 8, 8
+    the fused call (the placing instances), with ragged last passes. At T = 300 the
+    plain dispatch takes its split form (a workgroup per token and row slice, while
+    T x slices <= 4096), at T = 1500 the whole-row form."""
+    E, G, K = 64, 8, 8
     d = si.make_inputs(T, H, E, K, seed=H + 3)
     idx_d, w_d, x_d = to_dev(d["topk_idx"]), to_dev(d["topk_w"]), dev_bf16(d["x"])
     Lo = orc.layout(d["topk_idx"], E, G)
