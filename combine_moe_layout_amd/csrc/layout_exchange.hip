@@ -170,7 +170,6 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
     __shared__ int32_t s_src[kLayoutTile * KMAX];   // the tile's pair ids in slot order
     __shared__ int32_t s_dst[kLayoutTile * KMAX];   // and their receive slots
     __shared__ int s_wave_tot[kXW];
-    __shared__ int gcnt[kMaxG][kXW];
     __shared__ int lgstart[kMaxG];
     __shared__ int gtot[kMaxG];   // the tile's count of each group
     __shared__ int base_g[kMaxG];
@@ -254,10 +253,7 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
     if (t < T && h == 0) L.tok_group_mask[t] = gm;
     for (int g = 0; g < G; ++g) {
         const uint64_t b = __ballot(h == 0 && ((gm >> g) & 1u));   // bits 0-31: the wave's tokens
-        if (lane == 0) {
-            gcnt[g][wave] = __popcll(b);
-            gball[g][wave] = (uint32_t)b;
-        }
+        if (lane == 0) gball[g][wave] = (uint32_t)b;
     }
     if (err) atomicOr(&s_err, err);
     __syncthreads();
@@ -274,7 +270,7 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
 #pragma unroll
         for (int w = 0; w < kXW; ++w) {
             if (lane < G) loff_g[gl][w] = r;
-            r += lane < G ? gcnt[gl][w] : 0;
+            r += lane < G ? __popc(gball[gl][w]) : 0;
         }
         const int incl = wave_incl_scan(r);
         if (lane < G) {
