@@ -38,8 +38,10 @@ def orc():
 def check(L, Lo, what):
     assert int(L.status.item()) == Lo["status"], what
     for n in NAMES:
-        np.testing.assert_array_equal(getattr(L, n).cpu().numpy().astype(np.int64), Lo[n].astype(np.int64),
-                                      err_msg=f"{what} {n}")
+        got = getattr(L, n).cpu().numpy()
+        if n == "tok_group_mask":   # uint32 bits held as int32 (group 31 is the sign bit)
+            got = got.view(np.uint32)
+        np.testing.assert_array_equal(got.astype(np.int64), Lo[n].astype(np.int64), err_msg=f"{what} {n}")
     np.testing.assert_array_equal(L.recv_src_e.cpu().numpy()[:Lo["R_expert"]], Lo["recv_src_e"][:Lo["R_expert"]])
     np.testing.assert_array_equal(L.recv_src_g.cpu().numpy()[:Lo["R_group"]], Lo["recv_src_g"][:Lo["R_group"]])
 
@@ -108,3 +110,35 @@ def test_more_streams_than_tables(moe, orc):
     torch.cuda.synchronize()
     for n, (L, idx, E, G) in enumerate(runs):
         check(L, orc.layout(idx, E, G), f"stream {n}")
+
+
+def test_random_layouts_up_to_128_tiles(moe, orc):
+    """60 random routing problems of 1-128 tiles (the exchange's range; past 16 tiles
+    its reads take several rounds), top-k 1-8 (the two lanes of a token split its
+    entries; odd K leaves the second lane short), E up to 1024 in G groups, with
+    repeated experts at random positions of a token (within one lane's half and
+    across the two halves) and out-of-range entries; every layout array against the
+    oracle, bit for bit. Layouts that do not fit the exchange table take count +
+    place, which is checked the same way."""
+    rng = np.random.default_rng(20261203)
+    for rnd in range(60):
+        G = int(rng.choice([1, 4, 8, 32]))
+        E = G * int(rng.choice([1, 2, 8, 32])) if G < 32 else 32 * int(rng.choice([1, 8, 32]))
+        K = int(rng.integers(1, 9))
+        K = min(K, E)
+        T = int(rng.integers(1, 128 * 256 + 1))
+        d = si.make_inputs(T, 8, E, K, seed=3000 + rnd, routing="zipf" if rnd % 3 == 0 else "uniform")
+        idx = d["topk_idx"].copy()
+        if K > 1 and rnd % 2 == 0:                       # repeats: random token, random positions
+            n = int(rng.integers(1, 20))
+            ts, k1 = rng.integers(0, T, n), rng.integers(1, K, n)
+            k0 = (rng.random(n) * k1).astype(np.int64)   # an earlier position
+            idx[ts, k1] = idx[ts, k0]
+        if rnd % 5 == 0:                                  # out of range
+            n = int(rng.integers(1, 10))
+            idx[rng.integers(0, T, n), rng.integers(0, K, n)] = rng.choice([-1, E, E + 3, -100], n)
+        what = f"round {rnd}: T={T} E={E} G={G} K={K}"
+        print(what, flush=True)
+        L = moe.moe_layout(torch.from_numpy(idx).cuda(), E, G)
+        torch.cuda.synchronize()
+        check(L, orc.layout(idx, E, G), what)
