@@ -306,7 +306,9 @@ def summaries(out: str, res: dict, K: dict, cal: dict, dirs: list[str]) -> None:
                       f"dispatch call {ku['layout_dispatch']['mean']:.2f} µs (mean; the count kernel, the dispatch "
                       f"and the gap between them), the combine {ku['combine']['mean']:.2f} µs (mean); "
                       f"{b['value']:.1f} GB/s for the step ({b['ms_per_step'] * 1e3:.2f} µs per step by the wall "
-                      "clock, the profiler attached)."]
+                      "clock, the profiler attached). Events bracket the host call, so they also hold the launch gap "
+                      "before the kernel and the event commands themselves (a few µs, more with the profiler "
+                      "attached); the trace's durations are the kernels' alone."]
         write_md(dirs, "t4096_expert_step_kernel_trace.md", lines)
         items = [("step", K[k]) for k in ("dispatch_expert_bf16", "combine_expert_bf16", "layout_count_t4096")]
         lines = ["# HBM traffic counters: t4096 per-expert step", "", HEAD, "",
