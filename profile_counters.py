@@ -383,6 +383,8 @@ def main():
     ap.add_argument("--only", default=None)
     ap.add_argument("--from-raw", action="store_true",
                     help="rebuild counters.json and the summaries from OUTDIR's raw output")
+    ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"),
+                    help="where counters.json and the summaries go (default: the repository's profiles/)")
     args = ap.parse_args()
     args.out = os.path.abspath(args.out)   # the passes run from /tmp
     os.makedirs(args.out, exist_ok=True)
@@ -398,7 +400,8 @@ def main():
         for n in names:
             for kind in passes_of(n):
                 run_pass(args.out, n, kind)
-    path = os.path.join(ROOT, "profiles", "counters.json")
+    os.makedirs(args.profiles_dir, exist_ok=True)
+    path = os.path.join(args.profiles_dir, "counters.json")
     doc = json.load(open(path)) if os.path.exists(path) else {"kernels": {}}
     if not args.only:
         doc["kernels"] = {}   # every target again: no record of a kernel that no longer runs stays
@@ -467,7 +470,7 @@ def main():
         rec("t4096.cast_transpose", "cast_transpose", r, "cast_transpose_cols_kernel",
             (R * wl.H * 2, R * wl.H + npad * wl.H), top=51)
     doc["taken"] = time.strftime("%Y-%m-%d", time.localtime(os.path.getmtime(hpath)))
-    dirs = [os.path.join(ROOT, "profiles"), args.out]
+    dirs = [args.profiles_dir, args.out]
     for d in dirs:
         with open(os.path.join(d, "counters.json"), "w") as f:
             json.dump(doc, f, indent=1)
