@@ -33,6 +33,7 @@
 
 #include "layout_tile.hpp"
 
+#include <algorithm>
 #include <mutex>
 
 namespace moe {
@@ -67,6 +68,9 @@ __device__ __forceinline__ int xch_err_unpack(uint32_t s) { return ((s & 0xFFu) 
 // token-ascending order, as with one lane per token.
 constexpr int kXT = 2 * kLayoutTile;
 constexpr int kXW = kXT / kWave;   // 8
+// Pair sums left by the reader groups after the first: (groups - 1) x pairs,
+// at most (8 - waves per pair set) x 64 with groups = 8 / waves per pair set.
+constexpr int kXPartMax = (kXW - 1) * kWave;
 
 // Every token's valid entries counted into s_tot (all tiles) and s_pre (tiles
 // before `tile`), groups likewise in columns E.., error bits ORed into column
@@ -149,8 +153,9 @@ __device__ void xch_fallback_offsets(int E, int G, int tile, const int *s_tot, c
     }
 }
 
-// NX: experts in chunks of kXT (E <= NX * 512).
-template <int KMAX, bool EXACT, int NX>
+// NX: experts in chunks of kXT (E <= NX * 512). MR: more than one round of
+// tiles, read by several groups of waves (E <= 512 only).
+template <int KMAX, bool EXACT, int NX, bool MR>
 __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
     const int32_t *__restrict__ idx, int T, int vec, int Krt, int E, int G, uint32_t gmagic, int ntiles,
     uint64_t *__restrict__ xt, uint32_t tag, uint64_t wait_ticks, int recount, LayoutPtrs L)
@@ -176,6 +181,8 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
     __shared__ int loff_g[kMaxG][kXW];
     __shared__ uint32_t gball[kMaxG][kXW];
     __shared__ int s_err, s_late, s_gpairs;
+    constexpr bool kMR = MR && NX == 1;
+    __shared__ int s_part[kMR ? kXPartMax : 1][6];   // the other reader groups' column sums (below)
     const int K = EXACT ? KMAX : Krt;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int j = lane & 31, h = lane >> 5;   // token j of the wave, half h of its entries
@@ -358,7 +365,14 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
     // see one old and one new, never half of an entry, both being single
     // requests within one cache line.) With one tile the values are this
     // tile's own.
+    // With more than one round of tiles (and E <= 512) the waves without pairs
+    // read too: reader group r (waves r * wpp .. r * wpp + wpp - 1) takes the
+    // rounds r, r + nrg, ...; the groups after the first leave their sums in
+    // LDS for the first, whose threads own the columns.
     const int npair = rows / 2;
+    const int wpp = (npair + kWave - 1) / kWave;   // waves per set of pairs
+    const int nrg = kMR ? max(1, min(kXW / wpp, (ntiles + kXB - 1) / kXB)) : 1;
+    const int rg = kMR ? wave / wpp : 0;           // this wave's reader group (idle if >= nrg)
     int ctot[2 * NX], coff[2 * NX], cpre[2 * NX];
 #pragma unroll
     for (int q = 0; q < 2 * NX; ++q) ctot[q] = coff[q] = cpre[q] = 0;
@@ -369,9 +383,11 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
         bool late = false;
 #pragma unroll
         for (int jj = 0; jj < NX; ++jj) {
-            if (jj * kXT + wave * kWave < npair) {   // uniform per wave: some lane has a pair
-                const int pc = tid + jj * kXT < npair ? tid + jj * kXT : npair - 1;
-                for (int b0 = 0; b0 < ntiles && !late; b0 += kXB) {
+            // uniform per wave: in a reader group (one pair set: some lane has a pair)
+            if (kMR ? rg < nrg : jj * kXT + wave * kWave < npair) {
+                const int p = kMR ? (wave - rg * wpp) * kWave + lane : tid + jj * kXT;
+                const int pc = p < npair ? p : npair - 1;
+                for (int b0 = rg * kXB; b0 < ntiles && !late; b0 += nrg * kXB) {
                     u32x4 v[kXB];
                     while (true) {
                         // The offset passes through an empty asm on each pass, so
@@ -413,6 +429,18 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
                 }
             }
         }
+        if (kMR && rg > 0 && rg < nrg) {
+            const int p = (wave - rg * wpp) * kWave + lane;
+            if (p < npair) {
+                int *sp = s_part[(rg - 1) * npair + p];
+                sp[0] = ctot[0];
+                sp[1] = coff[0];
+                sp[2] = cpre[0];
+                sp[3] = ctot[1];
+                sp[4] = coff[1];
+                sp[5] = cpre[1];
+            }
+        }
         if (late) s_late = 1;
     } else if (!recount) {
 #pragma unroll
@@ -431,6 +459,17 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
     }
     __syncthreads();
     const bool fell_back = s_late != 0;   // uniform
+    if (kMR && xch && !fell_back && tid < npair) {
+        for (int r = 1; r < nrg; ++r) {
+            const int *sp = s_part[(r - 1) * npair + tid];
+            ctot[0] += sp[0];
+            coff[0] += sp[1];
+            cpre[0] += sp[2];
+            ctot[1] += sp[3];
+            coff[1] += sp[4];
+            cpre[1] += sp[5];
+        }
+    }
     if (!fell_back) {
         // Each owned column's results: an expert's (group's) first receive row
         // in this tile is its offset + its count in earlier tiles; tile 0
@@ -533,21 +572,29 @@ __global__ __launch_bounds__(kXT) void layout_exchange_kernel(
 using ExchangeFn = void (*)(const int32_t *, int, int, int, int, int, uint32_t, int, uint64_t *, uint32_t, uint64_t,
                             int, LayoutPtrs);
 
-template <int NX>
+template <int NX, bool MR>
 ExchangeFn pick_exchange_n(int K)
 {
     switch (K) {
-    case 2: return layout_exchange_kernel<2, true, NX>;
-    case 4: return layout_exchange_kernel<4, true, NX>;
-    case 8: return layout_exchange_kernel<8, true, NX>;
-    default: return layout_exchange_kernel<8, false, NX>;
+    case 2: return layout_exchange_kernel<2, true, NX, MR>;
+    case 4: return layout_exchange_kernel<4, true, NX, MR>;
+    case 8: return layout_exchange_kernel<8, true, NX, MR>;
+    default: return layout_exchange_kernel<8, false, NX, MR>;
     }
 }
 
-ExchangeFn pick_exchange(int K, int E)
+// The reader groups only where there are at least two (more than one round
+// of tiles, and idle waves for a second set of pairs): the other instance stays
+// as compact as it was (the groups' code cost it registers and 0.5 µs at 16
+// tiles, 0.8 µs at 32 tiles of E = 512 with one group).
+ExchangeFn pick_exchange(int K, int E, int G, int ntiles)
 {
     static_assert(2 * kXT >= 1024, "E <= 1024 in two chunks");
-    return E <= kXT ? pick_exchange_n<1>(K) : pick_exchange_n<2>(K);
+    constexpr int kRound = 16;   // tiles per round of reads
+    if (E > kXT) return pick_exchange_n<2, false>(K);
+    const int npair = ((E + G + 3) & ~1) / 2, wpp = (npair + kWave - 1) / kWave;
+    const int groups = std::min(kXW / wpp, (ntiles + kRound - 1) / kRound);
+    return groups >= 2 ? pick_exchange_n<1, true>(K) : pick_exchange_n<1, false>(K);
 }
 
 // Exchange tables of the one-launch layout, in library memory (zero when the
@@ -653,7 +700,7 @@ hipError_t launch_layout_exchange(const int32_t *idx, int T, int K, int E, int G
     const long long wt = tuning().base_wait_ticks;
     const size_t lds = (size_t)E * kXW * sizeof(uint32_t) +
                        ((size_t)E * (kXW + 2) + 2 * (size_t)(E + G + 1)) * sizeof(int);
-    hipLaunchKernelGGL(pick_exchange(K, E), dim3(ntiles), dim3(kXT), lds, stream, idx, T, vec, K, E, G,
+    hipLaunchKernelGGL(pick_exchange(K, E, G, ntiles), dim3(ntiles), dim3(kXT), lds, stream, idx, T, vec, K, E, G,
                        group_magic(E, G), ntiles, xt, tag, (uint64_t)(wt < 0 ? 0 : wt), wt < 0 ? 1 : 0, L);
     launched = true;
     return hipGetLastError();
