@@ -782,9 +782,10 @@ def _layout_host(L):
 
 def workload_table(moe, names=WORKLOAD_NAMES, it=50, oracle_threads=0):
     """Per-workload timings of every call in both receive layouts (median µs over `it`
-    event-timed calls; GB/s = algorithmic bytes / median; for the layout also the µs
-    per call in a stream of back-to-back calls, `layout_us_stream`, since a pair of
-    events around one short call adds a fixed cost of its own), the per-expert step
+    event-timed calls; GB/s = algorithmic bytes / median; for the layout, and for the
+    dispatch and combine of batches of at most 256 tokens, also the µs per call in a
+    stream of back-to-back calls, `*_us_stream`, since a pair of events around one
+    short call adds a fixed cost of its own), the per-expert step
     replayed from a captured HIP graph (no host launch cost), and, with
     oracle_threads > 0, both oracle builds timed per call on the same inputs and the
     GPU's outputs of every call checked against the oracle's (`parity`). Each workload
@@ -829,6 +830,9 @@ def workload_table(moe, names=WORKLOAD_NAMES, it=50, oracle_threads=0):
                          "combine_frac": round(bc / mc / 1e3 / PEAK_HBM_GBS, 4),
                          "dispatch_payload_gbs": round(nrows * H * (1 if wl.fp8 else 2) / md / 1e3, 1),
                          "combine_payload_gbs": round(nrows * H * 2 / mc / 1e3, 1)}
+            if T <= 256:   # launch-bound calls: also what each costs in a stream of calls
+                row[mode]["dispatch_us_stream"] = round(min(time_stream(disp) for _ in range(3)), 2)
+                row[mode]["combine_us_stream"] = round(min(time_stream(comb) for _ in range(3)), 2)
             if oracle_threads:
                 torch.cuda.synchronize()
                 g = {"out": host_bits(dv.out)}
